@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+* hand-worked fixtures under tests/golden/ (2:4 choices, codes, a packed layer);
+* exhaustive brute force with exact rational arithmetic on tiny layers
+  (all six 2:4 patterns of every group, a triple-loop product);
+* invariants fixed by the method: density, metadata validity, round trips;
+* planted mistakes: a wrong variant of an oracle step must fail a pin.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+DTYPES = ("f16", "bf16")
+
+
+def _num(v):
+    return -0.0 if v == "-0" else float(v)
+
+
+def _bits(values, dtype):
+    return wl.to_bits(np.array([[_num(v) for v in row] for row in values], dtype=np.float32), dtype) \
+        if isinstance(values[0], list) else wl.to_bits(np.array([_num(v) for v in values], dtype=np.float32), dtype)
+
+
+# ---------------------------------------------------------------------------
+# brute force (independent of the oracle): exact rationals, all six patterns
+# ---------------------------------------------------------------------------
+
+PAIRS = list(itertools.combinations(range(4), 2))   # the six 2:4 patterns, lexicographic
+
+
+def exact_value(bits16, dtype):
+    """Exact rational value of one 16-bit pattern, decoded field by field."""
+    b = int(bits16)
+    sign = -1 if b >> 15 else 1
+    if dtype == "f16":
+        e, m, bias, mb = (b >> 10) & 0x1F, b & 0x3FF, 15, 10
+        emax = 0x1F
+    else:
+        e, m, bias, mb = (b >> 7) & 0xFF, b & 0x7F, 127, 7
+        emax = 0xFF
+    assert e != emax, "finite inputs only"
+    if e == 0:
+        return sign * Fraction(m, 1 << mb) * Fraction(2) ** (1 - bias)
+    return sign * (1 + Fraction(m, 1 << mb)) * Fraction(2) ** (e - bias)
+
+
+def brute_score(bits16, dtype, c=None):
+    """|w|, or |w|*c rounded once to binary32 (the double product of two binary32 values is exact)."""
+    a = abs(exact_value(bits16, dtype))
+    if c is None:
+        return a
+    return Fraction(float(np.float32(float(a) * float(np.float32(c)))))
+
+
+def brute_pair(scores):
+    """Largest kept-score sum over the six patterns; ties go to the lexicographically smallest pair."""
+    best, best_sum = None, None
+    for p in PAIRS:
+        s = scores[p[0]] + scores[p[1]]
+        if best is None or s > best_sum:
+            best, best_sum = p, s
+    return best
+
+
+def brute_mask_and_pack(Wb, dtype, tmap, bn, bk, c=None):
+    """Pure-Python masking and packing, element by element."""
+    N, K = Wb.shape
+    Tk = K // bk
+    Wm = [[int(Wb[n, k]) for k in range(K)] for n in range(N)]
+    values, meta, index = [], [], []
+    voff = moff = 0
+    for tn in range(N // bn):
+        for tk in range(Tk):
+            t = tn * Tk + tk
+            index.append((voff, moff, int(tmap[t]), 0))
+            if tmap[t] == 0:
+                for r in range(bn):
+                    for cc in range(bk):
+                        values.append(int(Wb[tn * bn + r, tk * bk + cc]))
+                voff += bn * bk
+                continue
+            for r in range(bn):
+                n = tn * bn + r
+                word, nword = 0, 0
+                for g in range(bk // 4):
+                    ks = [tk * bk + 4 * g + i for i in range(4)]
+                    sc = [brute_score(Wb[n, k], dtype, None if c is None else c[k]) for k in ks]
+                    i0, i1 = brute_pair(sc)
+                    values += [int(Wb[n, ks[i0]]), int(Wb[n, ks[i1]])]
+                    for i in range(4):
+                        if i not in (i0, i1):
+                            Wm[n][ks[i]] = 0
+                    word |= (i0 | (i1 << 2)) << (4 * (g % 8))
+                    if g % 8 == 7:
+                        meta.append(word)
+                        word, nword = 0, nword + 1
+            voff += bn * bk // 2
+            moff += bn * bk // 32
+    return (np.array(Wm, dtype=np.uint16), np.array(values, dtype=np.uint16),
+            np.array(meta, dtype=np.uint32), np.array(index, dtype=np.uint32).reshape(-1, 4))
+
+
+def tie_heavy_bits(shape, dtype, g):
+    """Small integers and halves with many equal magnitudes, signed zeros, and a few subnormals."""
+    choices = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 3.0, 0.25], dtype=np.float32)
+    x = choices[g.integers(0, len(choices), size=shape)]
+    b = wl.to_bits(x, dtype)
+    sub = np.uint16(0x0001 if dtype == "f16" else 0x0001)   # smallest positive subnormal of each format
+    flip = g.random(shape) < 0.03
+    b[flip] = sub
+    return b
+
+
+# ---------------------------------------------------------------------------
+# golden fixtures
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_golden_two_of_four_groups(dtype):
+    gold = json.load(open(os.path.join(GOLD, "two_of_four_groups.json")))
+    for case in gold["groups"]:
+        s = oracle.selection_scores(_bits([case["w"]], dtype), dtype)
+        keep = oracle.keep_two_of_four(s)[0]
+        assert sorted(np.nonzero(keep)[0].tolist()) == case["keep"], case
+        i0, i1 = oracle.kept_positions(keep)
+        assert int(i0 | (i1 << 2)) == case["nibble"], case
+    for case in gold["scaled_groups"]:
+        c = np.array(case["c"], dtype=np.float32)
+        s = oracle.selection_scores(_bits([case["w"]], dtype), dtype, c)
+        keep = oracle.keep_two_of_four(s)[0]
+        assert sorted(np.nonzero(keep)[0].tolist()) == case["keep"], case
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_golden_pack_layer(dtype):
+    gold = json.load(open(os.path.join(GOLD, "pack_2x64.json")))
+    W = _bits(gold["W"], dtype)
+    tmap = np.array(gold["tile_map"], dtype=np.uint8)
+    vals, meta, index = oracle.pack(W, dtype, tmap, gold["bn"], gold["bk"])
+    assert np.array_equal(vals, _bits(gold["values"], dtype))
+    assert [f"{int(w):08X}" for w in meta] == gold["meta_hex"]
+    assert index.tolist() == gold["index"]
+    Wm = oracle.masked_weights(W, dtype, tmap, gold["bn"], gold["bk"])
+    assert np.array_equal(Wm[:, :32], _bits(gold["masked_W_tile0"], dtype))
+    assert np.array_equal(Wm[:, 32:], W[:, 32:])
+    Y = oracle.gemm_ref(_bits([[1.0] * 64], dtype), Wm, dtype)
+    assert Y.tolist() == [gold["masked_row_sums"]]
+    assert np.array_equal(oracle.unpack(vals, meta, index, 2, 64, 2, 32), Wm)
+
+
+# ---------------------------------------------------------------------------
+# brute force on tiny layers
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("scaled", [False, True])
+def test_brute_force_mask_and_pack(dtype, seed, scaled):
+    g = np.random.default_rng(1000 + seed)
+    N, K, bn, bk = 8, 64, 4, 32
+    W = tie_heavy_bits((N, K), dtype, g) if seed % 2 == 0 else wl.gaussian_bits((N, K), 0.02, dtype, g)
+    tmap = (g.random((N // bn) * (K // bk)) < 0.6).astype(np.uint8)
+    c = None
+    if scaled:
+        c = np.array(g.choice([0.0, 0.5, 1.0, 2.0, 3.0, 1.5], size=K), dtype=np.float32)
+    Wm_b, vals_b, meta_b, idx_b = brute_mask_and_pack(W, dtype, tmap, bn, bk, c)
+    vals, meta, idx = oracle.pack(W, dtype, tmap, bn, bk, c)
+    assert np.array_equal(oracle.masked_weights(W, dtype, tmap, bn, bk, c), Wm_b)
+    assert np.array_equal(vals, vals_b)
+    assert np.array_equal(meta, meta_b)
+    assert np.array_equal(idx, idx_b)
+
+
+def test_brute_force_selection_many_ties():
+    g = np.random.default_rng(7)
+    s = g.integers(0, 3, size=(4000, 4)).astype(np.float32)   # scores in {0,1,2}: ties everywhere
+    keep = oracle.keep_two_of_four(s)
+    for row, k in zip(s, keep):
+        p = brute_pair([Fraction(float(v)) for v in row])
+        assert sorted(np.nonzero(k)[0].tolist()) == list(p)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_brute_force_product(dtype):
+    g = np.random.default_rng(3)
+    M, N, K, bn, bk = 3, 8, 64, 4, 32
+    X = wl.gaussian_bits((M, K), 1.0, dtype, g)
+    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    tmap = np.array([1, 0, 0, 1], dtype=np.uint8)
+    Wm_b, *_ = brute_mask_and_pack(W, dtype, tmap, bn, bk)
+    Y = oracle.hybrid_ref(X, W, dtype, tmap, bn, bk)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(exact_value(X[m, k], dtype) * exact_value(Wm_b[n, k], dtype) for k in range(K))
+            mag = sum(abs(exact_value(X[m, k], dtype) * exact_value(Wm_b[n, k], dtype)) for k in range(K))
+            assert abs(Fraction(Y[m, n]) - exact) <= K * Fraction(2) ** -52 * mag
+
+
+def test_exact_value_decoder_matches_numpy():
+    # the brute force's own field decoder against numpy's binary16 (and the bf16 embedding in binary32)
+    allb = np.arange(0, 1 << 16, 97, dtype=np.uint16)
+    f16 = allb[(allb & 0x7C00) != 0x7C00]
+    assert all(float(exact_value(b, "f16")) == float(v) for b, v in zip(f16, f16.view(np.float16)))
+    bf = allb[(allb & 0x7F80) != 0x7F80]
+    assert all(float(exact_value(b, "bf16")) == float(np.uint32(int(b) << 16).view(np.float32)) for b in bf)
+
+
+# ---------------------------------------------------------------------------
+# invariants fixed by the method
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_all_dense_map_is_plain_product(dtype):
+    g = np.random.default_rng(11)
+    W = wl.gaussian_bits((128, 256), 0.02, dtype, g)
+    X = wl.gaussian_bits((5, 256), 1.0, dtype, g)
+    tmap = np.zeros(2 * 4, dtype=np.uint8)
+    assert np.array_equal(oracle.masked_weights(W, dtype, tmap, 64, 64), W)
+    vals, meta, idx = oracle.pack(W, dtype, tmap, 64, 64)
+    assert meta.size == 0 and vals.size == W.size
+    assert oracle.density(tmap) == 1.0
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("bn,bk", [(64, 64), (128, 128), (32, 96)])
+def test_sparse_invariants(dtype, bn, bk):
+    g = np.random.default_rng(bn + bk)
+    N, K = 2 * bn, 3 * bk
+    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    W[0, :8] = 0                                           # all-zero groups
+    W[1, 4:8] = wl.to_bits(np.array([-0.0, -0.0, 1.0, -0.0], np.float32), dtype)
+    tmap = np.array([1, 0, 1, 1, 1, 0], dtype=np.uint8)
+    Wm = oracle.masked_weights(W, dtype, tmap, bn, bk)
+    vals, meta, idx = oracle.pack(W, dtype, tmap, bn, bk)
+    T = tmap.size
+    n_s = int(tmap.sum())
+    # closed-form sizes and monotone offsets
+    assert vals.size == N * K - n_s * bn * bk // 2
+    assert meta.size * 4 == n_s * bn * bk // 8
+    assert idx.shape == (T, 4) and np.all(np.diff(idx[:, 0].astype(np.int64)) > 0)
+    assert np.all(idx[:, 3] == 0) and np.array_equal(idx[:, 2], tmap)
+    # density = 1 - 0.5 * sparse fraction, counted on the kept positions
+    tiles = oracle.as_tiles(Wm, bn, bk)
+    kept = 0
+    for t in range(T):
+        if tmap[t]:
+            groups = tiles[t].reshape(bn, bk // 4, 4)
+            nz = (groups & 0x7FFF) != 0
+            assert np.all(nz.sum(-1) <= 2)                 # at most two non-zeros per group
+            kept += bn * bk // 2
+        else:
+            kept += bn * bk
+    assert Fraction(kept, N * K) == 1 - Fraction(n_s, 2 * T)
+    assert math.isclose(oracle.density(tmap), kept / (N * K), rel_tol=1e-15)
+    # every code is one of the six patterns; every group has exactly two kept slots
+    nibs = (meta[:, None] >> (4 * np.arange(8)).astype(np.uint32)) & 0xF
+    assert set(np.unique(nibs).tolist()) <= oracle.VALID_NIBBLES
+    # unpack(pack(W)) == mask(W), bit for bit (signed zeros included)
+    assert np.array_equal(oracle.unpack(vals, meta, idx, N, K, bn, bk), Wm)
+    # -0.0 kept at position 0 of the second group of row 1 survives as 0x8000 when kept
+    assert Wm[1, 6] == W[1, 6]
+
+
+def test_all_sparse_map_equals_uniform_two_of_four():
+    g = np.random.default_rng(5)
+    W = wl.gaussian_bits((64, 128), 0.02, "bf16", g)
+    tmap = np.ones(2, dtype=np.uint8)
+    Wm = oracle.masked_weights(W, "bf16", tmap, 64, 64)
+    # a whole-matrix 2:4 by magnitude (no tiles at all) gives the same mask
+    s = np.abs(oracle.widen_f32(W, "bf16")).reshape(64, 32, 4)
+    keep = np.zeros_like(s, dtype=bool)
+    order = np.argsort(-s, axis=-1, kind="stable")          # descending, lower index first on ties
+    np.put_along_axis(keep, order[..., :2], True, axis=-1)
+    ref = np.where(keep.reshape(64, 128), W, np.uint16(0))
+    assert np.array_equal(Wm, ref)
+    assert oracle.density(tmap) == 0.5
+
+
+def test_linearity_in_x():
+    g = np.random.default_rng(9)
+    W = wl.gaussian_bits((64, 64), 0.02, "f16", g)
+    tmap = np.array([1], np.uint8)
+    X1 = wl.gaussian_bits((2, 64), 1.0, "f16", g)
+    X2 = wl.gaussian_bits((2, 64), 1.0, "f16", g)
+    Y1 = oracle.hybrid_ref(X1, W, "f16", tmap, 64, 64)
+    Y2 = oracle.hybrid_ref(X2, W, "f16", tmap, 64, 64)
+    Xs = np.concatenate([X1, X2])
+    assert np.allclose(oracle.hybrid_ref(Xs, W, "f16", tmap, 64, 64), np.concatenate([Y1, Y2]), rtol=0, atol=0)
+
+
+def test_tolerance_rule():
+    Yr = np.array([[1.0, -2.0], [0.5, 4.0]])
+    assert oracle.within_tolerance(Yr + 0.019, Yr)[0]
+    assert not oracle.within_tolerance(Yr + 0.021, Yr)[0]
+
+
+# ---------------------------------------------------------------------------
+# Wanda-derived maps
+# ---------------------------------------------------------------------------
+
+def test_column_norms_exact():
+    g = np.random.default_rng(21)
+    X = wl.gaussian_bits((16, 40), 1.0, "bf16", g)
+    c = oracle.column_norms(X, "bf16")
+    for k in range(40):
+        ss = sum(exact_value(X[r, k], "bf16") ** 2 for r in range(16))
+        exact = math.sqrt(ss)                       # float sqrt of a float-rounded rational: within 1 ulp64
+        assert abs(float(c[k]) - exact) <= float(np.spacing(np.float32(exact)))
+
+
+def test_wanda_cost_and_map_brute_force():
+    g = np.random.default_rng(31)
+    N, K, bn, bk = 8, 64, 4, 32
+    W = wl.gaussian_bits((N, K), 0.02, "bf16", g)
+    c = np.abs(g.standard_normal(K)).astype(np.float32) * np.float32(3)
+    cost = oracle.wanda_tile_cost(W, "bf16", c, bn, bk)
+    Tk = K // bk
+    for t in range(cost.size):
+        tn, tk = divmod(t, Tk)
+        exact = Fraction(0)
+        for r in range(bn):
+            for gi in range(bk // 4):
+                ks = [tk * bk + 4 * gi + i for i in range(4)]
+                sc = [brute_score(W[tn * bn + r, k], "bf16", c[k]) for k in ks]
+                p = brute_pair(sc)
+                exact += sum(sc[i] for i in range(4) if i not in p)
+        assert abs(Fraction(cost[t]) - exact) <= Fraction(2) ** -40 * exact
+    for n_s in (0, 1, 3, cost.size):
+        m = oracle.wanda_tile_map(cost, n_s)
+        assert int(m.sum()) == n_s
+        sel, rest = np.nonzero(m)[0], np.nonzero(m == 0)[0]
+        for a in sel:
+            for b in rest:
+                assert (cost[a], a) < (cost[b], b)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: a wrong variant of an oracle step must fail a pin
+# ---------------------------------------------------------------------------
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    gold = json.load(open(os.path.join(GOLD, "pack_2x64.json")))
+    W = _bits(gold["W"], "bf16")
+    tmap = np.array(gold["tile_map"], dtype=np.uint8)
+
+    def golden_ok():
+        vals, meta, index = oracle.pack(W, "bf16", tmap, 2, 32)
+        return (np.array_equal(vals, _bits(gold["values"], "bf16"))
+                and [f"{int(w):08X}" for w in meta] == gold["meta_hex"])
+
+    assert golden_ok()
+    # (1) tie-break toward the higher index
+    real_keep = oracle.hybrid.keep_two_of_four
+
+    def keep_high_ties(scores):
+        return real_keep(np.asarray(scores)[..., ::-1])[..., ::-1]
+    monkeypatch.setattr(oracle.hybrid, "keep_two_of_four", keep_high_ties)
+    assert not golden_ok()
+    monkeypatch.setattr(oracle.hybrid, "keep_two_of_four", real_keep)
+    # (2) kept pair stored higher index first (swapped code fields)
+    real_pos = oracle.hybrid.kept_positions
+    monkeypatch.setattr(oracle.hybrid, "kept_positions", lambda k: real_pos(k)[::-1])
+    assert not golden_ok()
+    monkeypatch.setattr(oracle.hybrid, "kept_positions", real_pos)
+    # (3) signed score (forgetting the magnitude)
+    real_scores = oracle.hybrid.selection_scores
+    monkeypatch.setattr(oracle.hybrid, "selection_scores",
+                        lambda Wb, dt, c=None: oracle.widen_f32(Wb, dt))
+    assert not golden_ok()
+    monkeypatch.setattr(oracle.hybrid, "selection_scores", real_scores)
+    assert golden_ok()

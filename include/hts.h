@@ -1,0 +1,177 @@
+/*
+ * hts.h -- hybrid tile-sparse (dense / 2:4) linear layers on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "PATCH: Learnable Tile-level Hybrid Sparsity for LLMs",
+ * section 2, core mechanism and inference/deployment): the weight W[N,K] of a
+ * linear layer is cut into bn x bk tiles; a per-tile map marks each tile dense
+ * (all weights kept) or 2:4 sparse (two of every four weights kept along K,
+ * six possible patterns).  Dense tiles run on the dense matrix cores and 2:4
+ * tiles on the sparse matrix cores, inside one product
+ *
+ *         Y[M,N] = X[M,K] . mask(W)^T        (fp32 accumulation)
+ *
+ * so that the overall sparsity can be anything from 0 % to 50 % (section 3).
+ * The same page stresses that speed needs compressed storage, not zeros; the
+ * packed format below is that storage.
+ *
+ * Conventions for every entry point
+ *   - All matrices are row-major.  W is [N,K] with leading dimension ldw,
+ *     X is [M,K] (ldx), Y is [M,N] (ldy); leading dimensions are in elements.
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary CPU memory, read or written only during the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
+ *     work is enqueued on it and the call returns without waiting; results are
+ *     ready when the stream reaches that point.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     frees nothing and keeps no pointer after a call returns.
+ *   - Every argument check is made on the host before anything is enqueued: a
+ *     failing call has no side effect and returns a status (details in
+ *     hts_last_error()).  Buffer sizes and the validity of device pointers
+ *     cannot be checked and are preconditions.
+ *   - Calls are thread-safe; calls that write the same buffers race.
+ */
+#ifndef HTS_H
+#define HTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HTS_ABI_VERSION 1u
+
+typedef enum {
+    HTS_OK = 0,
+    HTS_ERR_INVALID_ARG = 1,   /* null pointer where one is required, negative size, bad enum   */
+    HTS_ERR_DTYPE = 2,         /* element type not supported by this entry point                */
+    HTS_ERR_SHAPE = 3,         /* N, K not multiples of the tile, leading dimension too small   */
+    HTS_ERR_ALIGN = 4,         /* pointer not 16-byte aligned or leading dimension not a multiple of 8 */
+    HTS_ERR_MAP = 5,           /* a tile-map entry other than 0 or 1                            */
+    HTS_ERR_WORKSPACE = 6,     /* workspace smaller than hts_gemm_workspace() asks for          */
+    HTS_ERR_UNSUPPORTED = 7,   /* valid request this build does not implement (tile size ...)   */
+    HTS_ERR_HIP = 8            /* the HIP runtime reported an error (launch failure, no device) */
+} hts_status;
+
+typedef enum { HTS_F16 = 0, HTS_BF16 = 1, HTS_F32 = 2 } hts_dtype;
+
+enum { HTS_TILE_DENSE = 0, HTS_TILE_SPARSE24 = 1 };
+
+/* Shape of a tiled weight.  dtype is HTS_F16 or HTS_BF16 (W and X share it).
+ * bn, bk in {64, 128}; N % bn == 0 and K % bk == 0 (tiles cover W exactly);
+ * N*K < 2^32. */
+typedef struct {
+    int64_t N, K;
+    int32_t bn, bk;
+    int32_t dtype;
+    int32_t reserved;          /* must be 0 */
+} hts_desc;
+
+/* One record per tile, tiles in row-major tile order t = tn*(K/bk) + tk.
+ *   val_off  : first element of the tile in `values` (16-bit elements)
+ *   meta_off : first 32-bit word of the tile in `meta` (sparse tiles only; for a
+ *              dense tile it equals the next sparse tile's offset)
+ *   type     : HTS_TILE_DENSE or HTS_TILE_SPARSE24
+ *   reserved : 0 */
+typedef struct {
+    uint32_t val_off, meta_off, type, reserved;
+} hts_tile;
+
+typedef struct {
+    uint64_t values_bytes;     /* 2 * (N*K - n_sparse*bn*bk/2) */
+    uint64_t meta_bytes;       /* n_sparse * bn*bk/8            */
+    uint64_t index_bytes;      /* 16 * number of tiles          */
+    int64_t n_sparse;          /* number of 2:4 tiles           */
+} hts_sizes;
+
+/* Packed format (bit-exact contract of hts_pack / hts_unpack):
+ *   dense tile : bn*bk values, row-major inside the tile, raw bits of W.
+ *   2:4 tile   : per tile row r and group g of four weights (k = 4g..4g+3
+ *                from the tile start) the two kept weights, lower index first,
+ *                at values[val_off + r*(bk/2) + 2g + {0,1}] (raw bits); and the
+ *                4-bit code i0 | (i1 << 2) (i0 < i1 the kept positions in the
+ *                group) at bits 4*(g%8)..+3 of meta[meta_off + r*(bk/32) + g/8].
+ *   Kept pair: the two largest scores of the group, the lower index first among
+ *   equal scores.  Score = |w| as binary32, or the binary32 product |w| * c[k]
+ *   when a column scale c is given (the Wanda rule: weight magnitude times the
+ *   norm of the input activations of that column, page "SparseGPT vs Wanda:
+ *   one-shot LLM pruning without retraining", Wanda section).
+ *   Unpacked, a dropped weight reads +0.0. */
+
+uint32_t    hts_abi_version(void);
+/* Static text for a status code; never NULL. */
+const char* hts_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none).  Valid until the
+ * next call on the same thread. */
+const char* hts_last_error(void);
+
+/* Host only, synchronous.  Validates the descriptor and the map (uint8, one
+ * entry per tile, row-major tile order, 0 = dense, 1 = 2:4) and fills the tile
+ * index (index_host may be NULL to query sizes only) and the buffer sizes.
+ * Tile map: PATCH page, section 2 (per-tile dense / 2:4 decision). */
+hts_status hts_pack_plan(const hts_desc* d, const uint8_t* tile_map_host,
+                         hts_tile* index_host, hts_sizes* sizes);
+
+/* Device, asynchronous.  Writes the packed values and metadata of W under the
+ * index made by hts_pack_plan (copied to the device by the caller).
+ * col_scale: device float[K] column scale, or NULL for magnitude scores; must be
+ * finite and >= 0.  W must be finite.  meta may be NULL when n_sparse == 0.
+ * Buffers: values >= sizes.values_bytes, meta >= sizes.meta_bytes. */
+hts_status hts_pack(const hts_desc* d, const hts_tile* index, const void* W, int64_t ldw,
+                    const float* col_scale, void* values, uint32_t* meta, void* stream);
+
+/* Device, asynchronous.  Inverse of hts_pack: writes mask(W) into W_out[N,K]
+ * (ldw), +0.0 at the dropped positions of 2:4 tiles. */
+hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* values,
+                      const uint32_t* meta, void* W_out, int64_t ldw, void* stream);
+
+/* Host only.  Bytes of device workspace hts_gemm needs for this shape and M
+ * (currently always 0; pass NULL/0). */
+hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes);
+
+/* Device, asynchronous.  Y[M,N] = X[M,K] . mask(W)^T from the packed weight,
+ * fp32 accumulation, Y written as y_dtype (HTS_F32, HTS_F16 or HTS_BF16; 16-bit
+ * outputs rounded to nearest even).  Dense tiles use dense MFMA, 2:4 tiles
+ * sparse MFMA (or in-register expansion to dense MFMA when the environment
+ * variable HTS_SPARSE_PATH=decompress), both into one accumulator per output
+ * tile.  M == 0 is a no-op.  ldx, ldy: multiples of 8 and 4 with ldx >= K and
+ * ldy >= N. */
+hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values,
+                    const uint32_t* meta, int64_t M, const void* X, int64_t ldx,
+                    void* Y, int64_t ldy, int32_t y_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device, asynchronous.  The same-library dense product Y = X . W^T on a
+ * row-major W[N,K] (ldw) with the same kernels and no tile index: the
+ * reference point for speedups.  N and K multiples of 64. */
+hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K,
+                          const void* X, int64_t ldx, const void* W, int64_t ldw,
+                          void* Y, int64_t ldy, int32_t y_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device, asynchronous.  Wanda column scale c[k] = ||X[:,k]||_2 of calibration
+ * activations X[rows,K] (ldx): squares summed in fp64 over rows in order, one
+ * rounding of the square root to fp32 (Wanda section of the SparseGPT-vs-Wanda
+ * page: the input activation of each weight's column). */
+hts_status hts_col_norms(int32_t dtype, int64_t rows, int64_t K, const void* X, int64_t ldx,
+                         float* col_scale, void* stream);
+
+/* Device, asynchronous.  Per-tile Wanda cost: the fp64 sum of the scores a 2:4
+ * mask of the tile would drop (per row, pairs summed lower index first and
+ * accumulated over groups in order; rows accumulated in order).  cost: device
+ * double[T]. */
+hts_status hts_wanda_tile_cost(const hts_desc* d, const void* W, int64_t ldw,
+                               const float* col_scale, double* cost, void* stream);
+
+/* Device, asynchronous.  Tile map with the n_sparse lowest-cost tiles marked
+ * 2:4 (ties to the lower tile number), the rest dense: the layer-wise Wanda
+ * allocation of a target sparsity.  map: device uint8[T]. */
+hts_status hts_wanda_map(int64_t T, const double* cost, int64_t n_sparse, uint8_t* map,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HTS_H */

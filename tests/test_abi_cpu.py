@@ -1,0 +1,140 @@
+"""The C ABI on a host without a GPU: the library loads, exports every declared
+entry point, builds the tile index exactly as the oracle's plan, and rejects
+bad arguments before touching the GPU (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import tile_gemm_amd as hts
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "hts.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:hts_status|uint32_t|const char\*)\s+(hts_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = hts.lib()
+    names = declared_entry_points()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(hts.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    assert hts.hts_abi_version() == 1
+    for code in range(9):
+        assert hts.hts_status_string(code)
+    assert hts.hts_status_string(99) == "unknown status"
+
+
+def _maps():
+    out = []
+    for c in wl.CONFIGS:
+        for L in c.layers:
+            if L.map_kind == "wanda":
+                m = wl.exact_map(L.T, L.n_sparse_target, wl.rng(c.cfg_id, L.layer_id, wl.TAG_MAP))
+            else:
+                m = wl.tile_map(c, L)
+            out.append((L, m))
+    return out
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_plan_matches_oracle(case):
+    L, m = _maps()[case]
+    desc = hts.make_desc(L.N, L.K, L.bn, L.bk, L.dtype)
+    index, sizes = hts.hts_pack_plan(desc, m)
+    o_index, o_sizes = oracle.plan(m, L.N, L.K, L.bn, L.bk)
+    assert np.array_equal(index, o_index)
+    assert sizes["values_bytes"] == o_sizes["values_bytes"]
+    assert sizes["meta_bytes"] == o_sizes["meta_bytes"]
+    assert sizes["index_bytes"] == o_sizes["index_bytes"]
+    assert sizes["n_sparse"] == o_sizes["n_sparse"]
+
+
+def test_plan_edge_maps():
+    N, K, bn, bk = 512, 384, 128, 128
+    T = 12
+    for m in (np.zeros(T, np.uint8), np.ones(T, np.uint8), np.arange(T, dtype=np.uint8) % 2,
+              np.eye(1, T, 5, dtype=np.uint8).ravel()):
+        idx, sz = hts.hts_pack_plan(hts.make_desc(N, K, bn, bk, "bf16"), m)
+        assert np.array_equal(idx, oracle.plan(m, N, K, bn, bk)[0])
+        assert sz["values_bytes"] == 2 * (N * K - int(m.sum()) * bn * bk // 2)
+
+
+def _err(fn):
+    with pytest.raises(hts.HTSError) as e:
+        fn()
+    return e.value.status
+
+
+def test_plan_rejects_bad_arguments():
+    m = np.zeros(16, np.uint8)
+    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 64, 64, "f16"), np.full(16, 2, np.uint8))) == 5
+    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(250, 256, 64, 64, "f16"), m)) == 3
+    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 32, 64, "f16"), np.zeros(32, np.uint8))) == 7
+    d = hts.make_desc(256, 256, 64, 64, "f16")
+    d.dtype = 2
+    assert _err(lambda: hts.hts_pack_plan(d, m)) == 2
+    d = hts.make_desc(256, 256, 64, 64, "f16")
+    d.reserved = 1
+    assert _err(lambda: hts.hts_pack_plan(d, m)) == 1
+    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(1 << 17, 1 << 15, 128, 128, "bf16"),
+                                          np.zeros((1 << 10) * (1 << 8), np.uint8))) == 3
+
+
+# fake device addresses: never dereferenced, every call below fails its host checks
+A16, A8 = 0x10000, 0x10008
+
+
+def test_gemm_rejects_bad_arguments_before_any_launch():
+    L = hts.lib()
+    d = hts.make_desc(256, 256, 64, 64, "f16")
+    by = ctypes.byref
+
+    def gemm(desc=d, index=A16, values=A16, meta=A16, M=4, X=A16, ldx=256, Y=A16, ldy=256, yd=2):
+        return L.hts_gemm(by(desc), index, values, meta, M, X, ldx, Y, ldy, yd, None, 0, None)
+
+    assert gemm(M=-1) == 3
+    assert gemm(yd=7) == 2
+    assert gemm(index=None) == 1
+    assert gemm(values=A8) == 4
+    assert gemm(meta=A8) == 4
+    assert gemm(ldx=255) == 3
+    assert gemm(ldx=260) == 4
+    assert gemm(ldy=254) == 3
+    assert gemm(X=A8) == 4
+    assert gemm(Y=None) == 1
+    assert gemm(M=0) == 0                       # empty input: a no-op, nothing launched
+    bad = hts.make_desc(256, 256, 64, 96, "f16")
+    assert gemm(desc=bad) == 7
+    assert b"multiple" in L.hts_last_error() or b"64 or 128" in L.hts_last_error()
+
+
+def test_other_entry_points_reject_bad_arguments():
+    L = hts.lib()
+    by = ctypes.byref
+    d = hts.make_desc(256, 256, 64, 64, "bf16")
+    assert L.hts_pack(by(d), A16, A16, 255, None, A16, A16, None) == 3
+    assert L.hts_pack(by(d), A16, A8, 256, None, A16, A16, None) == 4
+    assert L.hts_pack(by(d), None, A16, 256, None, A16, A16, None) == 1
+    assert L.hts_unpack(by(d), A16, A16, A16, A16, 100, None) == 3
+    assert L.hts_dense_gemm(1, 4, 100, 256, A16, 256, A16, 256, A16, 256, 2, None, 0, None) == 3
+    assert L.hts_dense_gemm(2, 4, 128, 256, A16, 256, A16, 256, A16, 256, 2, None, 0, None) == 2
+    assert L.hts_dense_gemm(1, 0, 128, 256, A16, 256, A16, 256, A16, 256, 2, None, 0, None) == 0
+    assert L.hts_col_norms(1, 0, 16, A16, 16, A16, None) == 3
+    assert L.hts_col_norms(1, 4, 16, A16, 8, A16, None) == 3
+    assert L.hts_wanda_tile_cost(by(d), A16, 256, None, A16, None) == 1
+    assert L.hts_wanda_map(10, A16, 11, A16, None) == 3
+    assert L.hts_wanda_map(10, A8 + 4, 3, A16, None) == 4
+    n = ctypes.c_size_t(123)
+    assert L.hts_gemm_workspace(by(d), 16, by(n)) == 0 and n.value == 0

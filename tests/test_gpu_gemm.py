@@ -1,0 +1,166 @@
+"""GPU parity of the hybrid product (and of the same-library dense product) with the CPU oracle.
+
+Acceptance: max|Y - Y_ref| <= 5e-3 * max|Y_ref| with Y_ref = X . mask(W)^T in fp64.
+Full-size layers run in the launch configuration the benchmark times; at large M
+the comparison uses sampled rows of Y (every column), which the oracle computes
+row by row.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tile_gemm_amd as hts
+import workloads as wl
+from helpers import (DEV, activations, calib_scale, layer_id, named_layers, oracle_map, oracle_packed, sample_rows,
+                     say, weight)
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+
+
+@pytest.fixture(params=["smfmac", "decompress"])
+def sparse_path(request, monkeypatch):
+    monkeypatch.setenv("HTS_SPARSE_PATH", request.param)
+    return request.param
+
+
+def _packed_on_gpu(c, L):
+    vals, meta, idx, Wm = oracle_packed(c.cfg_id, L.name)
+    W = weight(c.cfg_id, L.name)
+    Wt = hts.tensor_from_bits(W, L.dtype, DEV)
+    m = oracle_map(c.cfg_id, L.name)
+    cs = None   # selection by magnitude, or by the Wanda score for Wanda-mapped layers
+    if L.map_kind == "wanda":
+        cs = torch.from_numpy(calib_scale(c.cfg_id, L.name)[1]).to(DEV)
+    return hts.pack(Wt, m, L.bn, L.bk, cs), Wm
+
+
+def _check(Y_gpu, Y_ref, what):
+    ok, rel = oracle.within_tolerance(Y_gpu, Y_ref, TOL)
+    say(f"    {what}: max err / max|ref| = {rel:.3e}")
+    assert ok, f"{what}: relative error {rel:.3e} > {TOL}"
+
+
+CASES = [(c, L, M) for c, L in named_layers() for M in c.Ms]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda x: f"{x[0].name}-{x[1].name}-M{x[2]}")
+def test_hybrid_gemm_named(case, sparse_path):
+    c, L, M = case
+    if sparse_path == "decompress" and c.name == "7b_block" and L.name not in ("q", "down"):
+        pytest.skip("expansion path covered on two block layers")
+    say(f"[gemm] {c.name}/{L.name} M={M} path={sparse_path}")
+    pw, Wm = _packed_on_gpu(c, L)
+    X = activations(c.cfg_id, L.name)[:M]
+    Xt = hts.tensor_from_bits(np.ascontiguousarray(X), L.dtype, DEV)
+    out_dtypes = [torch.float32] if c.name == "tiny" else [torch.float32, Xt.dtype]
+    rows = sample_rows(M)
+    Y_ref = oracle.gemm_ref(X[rows], Wm, L.dtype)
+    for od in out_dtypes:
+        Y = hts.gemm(Xt, pw, out_dtype=od)
+        torch.cuda.synchronize()
+        _check(Y[torch.from_numpy(rows).to(DEV)].float().cpu().numpy(), Y_ref, f"out={od}")
+
+
+RAGGED = [(M, dt, tile) for M in (1, 2, 3, 7, 15, 16, 17, 31, 64, 100, 127, 128, 129, 300)
+          for dt, tile in (("f16", (64, 64)), ("bf16", (128, 128)))]
+RAGGED += [(M, "bf16", tile) for M in (5, 16, 130) for tile in ((64, 128), (128, 64))]
+
+
+@pytest.mark.parametrize("M,dtype,tile", RAGGED)
+def test_hybrid_gemm_ragged_m(M, dtype, tile, sparse_path):
+    bn, bk = tile
+    N, K = 3 * 128, 4 * 128
+    g = np.random.default_rng(M * 7 + bn + bk)
+    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    X = wl.gaussian_bits((M, K), 1.0, dtype, g)
+    T = (N // bn) * (K // bk)
+    m = (g.random(T) < 0.5).astype(np.uint8)
+    say(f"[gemm-ragged] M={M} {dtype} tile={bn}x{bk} path={sparse_path}")
+    Y_ref = oracle.hybrid_ref(X, W, dtype, m, bn, bk)
+    pw = hts.pack(hts.tensor_from_bits(W, dtype, DEV), m, bn, bk)
+    Y = hts.gemm(hts.tensor_from_bits(X, dtype, DEV), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, f"M={M}")
+
+
+@pytest.mark.parametrize("kind", ["all_dense", "all_sparse", "checker", "one_sparse"])
+@pytest.mark.parametrize("M", [1, 16, 256])
+def test_hybrid_gemm_edge_maps(kind, M, sparse_path):
+    N, K, bn, bk = 512, 768, 128, 128
+    Tn, Tk = N // bn, K // bk
+    m = {"all_dense": np.zeros((Tn, Tk)), "all_sparse": np.ones((Tn, Tk)),
+         "checker": np.add.outer(np.arange(Tn), np.arange(Tk)) % 2,
+         "one_sparse": np.arange(Tn * Tk).reshape(Tn, Tk) == 7}[kind]
+    m = m.astype(np.uint8).ravel()
+    g = np.random.default_rng(17)
+    W = wl.gaussian_bits((N, K), 0.02, "bf16", g)
+    X = wl.gaussian_bits((M, K), 1.0, "bf16", g)
+    say(f"[gemm-edge] {kind} M={M} path={sparse_path}")
+    Y_ref = oracle.hybrid_ref(X, W, "bf16", m, bn, bk)
+    pw = hts.pack(hts.tensor_from_bits(W, "bf16", DEV), m, bn, bk)
+    Y = hts.gemm(hts.tensor_from_bits(X, "bf16", DEV), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, kind)
+    if kind == "all_dense":   # p = 0: the hybrid product equals the same-library dense product
+        Yd = hts.dense_gemm(hts.tensor_from_bits(X, "bf16", DEV), hts.tensor_from_bits(W, "bf16", DEV),
+                            out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Yd)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 200, 2048])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_dense_gemm(M, dtype):
+    N, K = 1024, 1536
+    g = np.random.default_rng(M)
+    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    X = wl.gaussian_bits((M, K), 1.0, dtype, g)
+    say(f"[dense] M={M} {dtype}")
+    rows = sample_rows(M)
+    Y_ref = oracle.gemm_ref(X[rows], W, dtype)
+    Y = hts.dense_gemm(hts.tensor_from_bits(X, dtype, DEV), hts.tensor_from_bits(W, dtype, DEV),
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy()[rows], Y_ref, "dense")
+
+
+def test_strided_x_and_y():
+    N, K, M = 256, 512, 40
+    g = np.random.default_rng(3)
+    W = wl.gaussian_bits((N, K), 0.02, "bf16", g)
+    Xbig = wl.gaussian_bits((M, K + 64), 1.0, "bf16", g)
+    m = np.array([1, 0, 1, 1, 0, 0, 1, 0], np.uint8)
+    Y_ref = oracle.hybrid_ref(np.ascontiguousarray(Xbig[:, :K]), W, "bf16", m, 128, 128)
+    pw = hts.pack(hts.tensor_from_bits(W, "bf16", DEV), m, 128, 128)
+    Xt = hts.tensor_from_bits(Xbig, "bf16", DEV)[:, :K]
+    Ybig = torch.full((M, N + 32), 7.0, dtype=torch.float32, device=DEV)
+    Y = Ybig[:, :N]
+    hts.gemm(Xt, pw, out=Y)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, "strided")
+    assert torch.all(Ybig[:, N:] == 7.0)           # nothing written past N
+
+
+def test_zero_rows_is_noop():
+    pw = hts.pack(hts.tensor_from_bits(np.zeros((128, 128), np.uint16), "bf16", DEV), np.ones(1, np.uint8),
+                  128, 128)
+    X = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    Y = hts.gemm(X, pw)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 128)
+
+
+@pytest.mark.parametrize("M", [1, 16, 2048])
+def test_deterministic(M):
+    c = wl.config("7b_up")
+    L = c.layers[0]
+    pw, _ = _packed_on_gpu(c, L)
+    Xt = hts.tensor_from_bits(np.ascontiguousarray(activations(c.cfg_id, L.name)[:M]), L.dtype, DEV)
+    Y1 = hts.gemm(Xt, pw, out_dtype=torch.float32)
+    Y2 = hts.gemm(Xt, pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)

@@ -1,0 +1,113 @@
+// Device-side helpers for gfx950 (CDNA4): 16-bit element handling and the
+// dense / sparse matrix-core instructions used by the product kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hts {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// Element-type tags.  BF16 = bfloat16, F16 = IEEE binary16.
+struct BF16T { static constexpr int id = 1; };
+struct F16T { static constexpr int id = 0; };
+
+// Exact widening of one 16-bit pattern to float.
+template <typename T> __device__ __forceinline__ float widen(uint32_t bits);
+template <> __device__ __forceinline__ float widen<BF16T>(uint32_t bits) {
+    return __uint_as_float(bits << 16);
+}
+template <> __device__ __forceinline__ float widen<F16T>(uint32_t bits) {
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)bits);
+    return (float)h;
+}
+
+// Round-to-nearest-even narrowing of a float (finite or not) to a 16-bit pattern.
+__device__ __forceinline__ uint32_t narrow_bf16(float f) {
+    __bf16 b = (__bf16)f;                      // RNE conversion on gfx950
+    return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t narrow_f16(float f) {
+    _Float16 h = (_Float16)f;                  // RNE conversion
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Dense 16x16x32 MFMA: A[16][32] x B[32][16] -> C[16][16], fp32 accumulate.
+// Operand lanes: A lane (i + 16h) holds A[i][8h .. 8h+7]; B lane (j + 16q) holds
+// B[8q .. 8q+7][j]; C lane (j + 16q) holds C[4q .. 4q+3][j].
+template <typename T> __device__ __forceinline__ f32x4 mfma_dense(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mfma_dense<BF16T>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mfma_dense<F16T>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Sparse 16x16x64 MFMA (SMFMAC): A is 16 x 64 with two of every four entries
+// stored.  A lane (i + 16h) holds the 8 stored values of row i for dense
+// k in [16h, 16h+16): value v belongs to group v/2 and sits at position
+// 4*(v/2) + idx_v, idx_v = bits [2v+1:2v] of the selected 16-bit index half
+// (ABID = 0: low half, 1: high half).  B lane (j + 16q) holds B[8q+e][j] for
+// e < 8 and B[32+8q+(e-8)][j] for e >= 8.  C as for the dense instruction.
+// (Lane layout measured on gfx950 with one-hot operands.)
+template <typename T, int ABID>
+__device__ __forceinline__ f32x4 mfma_sparse(u32x4 a, u32x4 b_lo, u32x4 b_hi, uint32_t idx, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma_sparse<BF16T, 0>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
+    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x16, b), c, (int)idx, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_sparse<BF16T, 1>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
+    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x16, b), c, (int)idx, 0, 1);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_sparse<F16T, 0>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
+    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x16, b), c, (int)idx, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_sparse<F16T, 1>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
+    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x16, b), c, (int)idx, 0, 1);
+}
+
+// Expand two 2:4 groups (4 stored 16-bit values in `v`, codes in the low byte
+// of `nib`: group 0 bits 0..3, group 1 bits 4..7) into 8 dense 16-bit values.
+__device__ __forceinline__ u32x4 expand_two_groups(uint2 v, uint32_t nib) {
+    uint32_t vals[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+    uint32_t out[8];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        uint32_t code = (nib >> (4 * g)) & 0xFu;
+        uint32_t i0 = code & 3u, i1 = code >> 2;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            uint32_t x = (i0 == (uint32_t)p) ? vals[2 * g] : 0u;
+            x = (i1 == (uint32_t)p) ? vals[2 * g + 1] : x;
+            out[4 * g + p] = x;
+        }
+    }
+    u32x4 r = {out[0] | (out[1] << 16), out[2] | (out[3] << 16), out[4] | (out[5] << 16),
+               out[6] | (out[7] << 16)};
+    return r;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace hts

@@ -1,0 +1,292 @@
+// C ABI of the hybrid tile-sparse library: argument checks, the tile index
+// (prefix sums over the tile map), variant choice and kernel launches.
+// Every check happens before anything is enqueued; a failing call has no effect.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "hts.h"
+#include "hts_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+hts_status fail(hts_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+hts_status ok() {
+    g_err[0] = '\0';
+    return HTS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is16bit(int32_t dt) { return dt == HTS_F16 || dt == HTS_BF16; }
+bool is_out(int32_t dt) { return dt == HTS_F16 || dt == HTS_BF16 || dt == HTS_F32; }
+
+hts_status check_desc(const hts_desc* d) {
+    if (!d) return fail(HTS_ERR_INVALID_ARG, "descriptor is NULL");
+    if (!is16bit(d->dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16 or HTS_BF16", d->dtype);
+    if (d->reserved != 0) return fail(HTS_ERR_INVALID_ARG, "descriptor reserved field must be 0");
+    if (d->N <= 0 || d->K <= 0) return fail(HTS_ERR_SHAPE, "N=%lld K=%lld must be positive", (long long)d->N,
+                                            (long long)d->K);
+    if (!((d->bn == 64 || d->bn == 128) && (d->bk == 64 || d->bk == 128)))
+        return fail(HTS_ERR_UNSUPPORTED, "tile %dx%d: bn and bk must each be 64 or 128", d->bn, d->bk);
+    if (d->N % d->bn || d->K % d->bk)
+        return fail(HTS_ERR_SHAPE, "N=%lld K=%lld are not multiples of the %dx%d tile", (long long)d->N,
+                    (long long)d->K, d->bn, d->bk);
+    if ((double)d->N * (double)d->K >= 4294967296.0)
+        return fail(HTS_ERR_SHAPE, "N*K must be below 2^32 (32-bit value offsets)");
+    return HTS_OK;
+}
+
+hts_status check_ld(int64_t ld, int64_t minv, int mult, const char* name) {
+    if (ld < minv) return fail(HTS_ERR_SHAPE, "%s=%lld is smaller than %lld", name, (long long)ld, (long long)minv);
+    if (ld % mult) return fail(HTS_ERR_ALIGN, "%s=%lld is not a multiple of %d", name, (long long)ld, mult);
+    return HTS_OK;
+}
+
+hts_status check_ptr(const void* p, const char* name) {
+    if (!p) return fail(HTS_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(HTS_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return HTS_OK;
+}
+
+hts_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(HTS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Sparse-tile path: SMFMAC unless HTS_SPARSE_PATH=decompress.
+int sparse_path() {
+    const char* v = getenv("HTS_SPARSE_PATH");
+    if (v && strcmp(v, "decompress") == 0) return hts::SPARSE_DECOMPRESS;
+    return hts::SPARSE_SMFMAC;
+}
+
+// Largest M served by the streaming kernel (HTS_DECODE_MAX_M, 0..16; default 16).
+int64_t decode_max_m() {
+    const char* v = getenv("HTS_DECODE_MAX_M");
+    if (v && *v) {
+        long x = strtol(v, nullptr, 10);
+        if (x >= 0 && x <= 16) return x;
+    }
+    return 16;
+}
+
+// Waves per panel of the streaming kernel: enough waves in total to keep HBM busy.
+int decode_ksplit(int64_t N) { return (N / 16 >= 512) ? 4 : 8; }
+
+hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
+    hipError_t e;
+    if (a.M <= decode_max_m())
+        e = hts::launch_gemm_decode(a, decode_ksplit(a.N), sparse_path(), s);
+    else
+        e = hts::launch_gemm_prefill(a, sparse_path(), s);
+    return hip_status(e, "product kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t hts_abi_version(void) { return HTS_ABI_VERSION; }
+
+const char* hts_status_string(int s) {
+    switch (s) {
+        case HTS_OK: return "ok";
+        case HTS_ERR_INVALID_ARG: return "invalid argument";
+        case HTS_ERR_DTYPE: return "unsupported element type";
+        case HTS_ERR_SHAPE: return "invalid shape";
+        case HTS_ERR_ALIGN: return "misaligned pointer or leading dimension";
+        case HTS_ERR_MAP: return "invalid tile map entry";
+        case HTS_ERR_WORKSPACE: return "workspace too small";
+        case HTS_ERR_UNSUPPORTED: return "unsupported configuration";
+        case HTS_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* hts_last_error(void) { return g_err; }
+
+hts_status hts_pack_plan(const hts_desc* d, const uint8_t* tile_map_host, hts_tile* index_host, hts_sizes* sizes) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if (!tile_map_host) return fail(HTS_ERR_INVALID_ARG, "tile map is NULL");
+    if (!sizes) return fail(HTS_ERR_INVALID_ARG, "sizes is NULL");
+    const int64_t T = (d->N / d->bn) * (d->K / d->bk);
+    for (int64_t t = 0; t < T; ++t)
+        if (tile_map_host[t] > 1)
+            return fail(HTS_ERR_MAP, "tile map entry %lld is %u (must be 0 or 1)", (long long)t, tile_map_host[t]);
+    const uint64_t dense = (uint64_t)d->bn * d->bk, sparse = dense / 2, mwords = dense / 32;
+    uint64_t voff = 0, moff = 0;
+    int64_t ns = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        if (index_host) {
+            index_host[t].val_off = (uint32_t)voff;
+            index_host[t].meta_off = (uint32_t)moff;
+            index_host[t].type = tile_map_host[t];
+            index_host[t].reserved = 0;
+        }
+        if (tile_map_host[t] == HTS_TILE_SPARSE24) {
+            voff += sparse;
+            moff += mwords;
+            ++ns;
+        } else {
+            voff += dense;
+        }
+    }
+    sizes->values_bytes = 2 * voff;
+    sizes->meta_bytes = 4 * moff;
+    sizes->index_bytes = 16 * (uint64_t)T;
+    sizes->n_sparse = ns;
+    return ok();
+}
+
+hts_status hts_pack(const hts_desc* d, const hts_tile* index, const void* W, int64_t ldw, const float* col_scale,
+                    void* values, uint32_t* meta, void* stream) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if ((st = check_ptr(index, "index")) || (st = check_ptr(W, "W")) || (st = check_ptr(values, "values")))
+        return st;
+    if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
+    if (col_scale && (reinterpret_cast<uintptr_t>(col_scale) & 3u))
+        return fail(HTS_ERR_ALIGN, "col_scale is not 4-byte aligned");
+    if ((st = check_ld(ldw, d->K, 8, "ldw"))) return st;
+    return hip_status(hts::launch_pack(*d, index, static_cast<const uint16_t*>(W), ldw, col_scale,
+                                       static_cast<uint16_t*>(values), meta, static_cast<hipStream_t>(stream)),
+                      "pack kernel launch");
+}
+
+hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta,
+                      void* W_out, int64_t ldw, void* stream) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if ((st = check_ptr(index, "index")) || (st = check_ptr(values, "values")) || (st = check_ptr(W_out, "W_out")))
+        return st;
+    if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
+    if ((st = check_ld(ldw, d->K, 8, "ldw"))) return st;
+    return hip_status(hts::launch_unpack(*d, index, static_cast<const uint16_t*>(values), meta,
+                                         static_cast<uint16_t*>(W_out), ldw, static_cast<hipStream_t>(stream)),
+                      "unpack kernel launch");
+}
+
+hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
+    if (!bytes) return fail(HTS_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    return ok();
+}
+
+hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta, int64_t M,
+                    const void* X, int64_t ldx, void* Y, int64_t ldy, int32_t y_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
+    if (!is_out(y_dtype)) return fail(HTS_ERR_DTYPE, "y_dtype %d is not F32, F16 or BF16", y_dtype);
+    if ((st = check_ptr(index, "index")) || (st = check_ptr(values, "values"))) return st;
+    if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
+    if ((st = check_ld(ldx, d->K, 8, "ldx")) || (st = check_ld(ldy, d->N, 4, "ldy"))) return st;
+    if (M == 0) return ok();
+    if ((st = check_ptr(X, "X")) || (st = check_ptr(Y, "Y"))) return st;
+    hts::GemmArgs a{};
+    a.dtype = d->dtype;
+    a.y_dtype = y_dtype;
+    a.M = M;
+    a.N = d->N;
+    a.K = d->K;
+    a.bn = d->bn;
+    a.bk = d->bk;
+    a.index = index;
+    a.values = static_cast<const uint16_t*>(values);
+    a.meta = meta;
+    a.X = static_cast<const uint16_t*>(X);
+    a.ldx = ldx;
+    a.Y = Y;
+    a.ldy = ldy;
+    return run_gemm(a, static_cast<hipStream_t>(stream));
+}
+
+hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, const void* W,
+                          int64_t ldw, void* Y, int64_t ldy, int32_t y_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!is16bit(dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16 or HTS_BF16", dtype);
+    if (!is_out(y_dtype)) return fail(HTS_ERR_DTYPE, "y_dtype %d is not F32, F16 or BF16", y_dtype);
+    if (M < 0 || N <= 0 || K <= 0)
+        return fail(HTS_ERR_SHAPE, "M=%lld N=%lld K=%lld (M >= 0, N and K positive)", (long long)M, (long long)N,
+                    (long long)K);
+    if (N % 64 || K % 64) return fail(HTS_ERR_SHAPE, "N and K must be multiples of 64");
+    hts_status st;
+    if ((st = check_ld(ldx, K, 8, "ldx")) || (st = check_ld(ldw, K, 8, "ldw")) || (st = check_ld(ldy, N, 4, "ldy")))
+        return st;
+    if (M == 0) return ok();
+    if ((st = check_ptr(X, "X")) || (st = check_ptr(W, "W")) || (st = check_ptr(Y, "Y"))) return st;
+    hts::GemmArgs a{};
+    a.dtype = dtype;
+    a.y_dtype = y_dtype;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.bn = 64;
+    a.bk = (K % 128 == 0) ? 128 : 64;
+    a.W = static_cast<const uint16_t*>(W);
+    a.ldw = ldw;
+    a.X = static_cast<const uint16_t*>(X);
+    a.ldx = ldx;
+    a.Y = Y;
+    a.ldy = ldy;
+    return run_gemm(a, static_cast<hipStream_t>(stream));
+}
+
+hts_status hts_col_norms(int32_t dtype, int64_t rows, int64_t K, const void* X, int64_t ldx, float* col_scale,
+                         void* stream) {
+    if (!is16bit(dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16 or HTS_BF16", dtype);
+    if (rows <= 0 || K <= 0) return fail(HTS_ERR_SHAPE, "rows and K must be positive");
+    hts_status st;
+    if ((st = check_ld(ldx, K, 1, "ldx"))) return st;
+    if (!X || !col_scale) return fail(HTS_ERR_INVALID_ARG, "X or col_scale is NULL");
+    if ((reinterpret_cast<uintptr_t>(X) & 1u) || (reinterpret_cast<uintptr_t>(col_scale) & 3u))
+        return fail(HTS_ERR_ALIGN, "X must be 2-byte and col_scale 4-byte aligned");
+    return hip_status(hts::launch_col_norms(dtype, rows, K, static_cast<const uint16_t*>(X), ldx, col_scale,
+                                            static_cast<hipStream_t>(stream)),
+                      "column-norm kernel launch");
+}
+
+hts_status hts_wanda_tile_cost(const hts_desc* d, const void* W, int64_t ldw, const float* col_scale, double* cost,
+                               void* stream) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if ((st = check_ptr(W, "W")) || (st = check_ld(ldw, d->K, 8, "ldw"))) return st;
+    if (!col_scale || !cost) return fail(HTS_ERR_INVALID_ARG, "col_scale or cost is NULL");
+    if ((reinterpret_cast<uintptr_t>(col_scale) & 3u) || (reinterpret_cast<uintptr_t>(cost) & 7u))
+        return fail(HTS_ERR_ALIGN, "col_scale must be 4-byte and cost 8-byte aligned");
+    return hip_status(hts::launch_wanda_cost(*d, static_cast<const uint16_t*>(W), ldw, col_scale, cost,
+                                             static_cast<hipStream_t>(stream)),
+                      "tile-cost kernel launch");
+}
+
+hts_status hts_wanda_map(int64_t T, const double* cost, int64_t n_sparse, uint8_t* map, void* stream) {
+    if (T <= 0) return fail(HTS_ERR_SHAPE, "T must be positive");
+    if (n_sparse < 0 || n_sparse > T) return fail(HTS_ERR_SHAPE, "n_sparse=%lld outside 0..T", (long long)n_sparse);
+    if (!cost || !map) return fail(HTS_ERR_INVALID_ARG, "cost or map is NULL");
+    if (reinterpret_cast<uintptr_t>(cost) & 7u) return fail(HTS_ERR_ALIGN, "cost must be 8-byte aligned");
+    return hip_status(hts::launch_wanda_map(T, cost, n_sparse, map, static_cast<hipStream_t>(stream)),
+                      "tile-map kernel launch");
+}
+
+}  // extern "C"

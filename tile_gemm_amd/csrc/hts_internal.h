@@ -1,0 +1,44 @@
+// Internal declarations shared by the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hts.h"
+
+namespace hts {
+
+// Everything a product kernel needs, by value.  Exactly one weight source is
+// used: the packed hybrid weight (index/values/meta) or a row-major W (W/ldw).
+struct GemmArgs {
+    int32_t dtype;        // HTS_F16 / HTS_BF16 for X and W
+    int32_t y_dtype;      // HTS_F32 / HTS_F16 / HTS_BF16
+    int64_t M, N, K;
+    int32_t bn, bk;       // tile size (a row-major W uses a virtual grid of bn x bk)
+    const hts_tile* index;
+    const uint16_t* values;
+    const uint32_t* meta;
+    const uint16_t* W;    // row-major weight (dense product) or nullptr
+    int64_t ldw;
+    const uint16_t* X;
+    int64_t ldx;
+    void* Y;
+    int64_t ldy;
+};
+
+enum SparsePath { SPARSE_SMFMAC = 0, SPARSE_DECOMPRESS = 1 };
+
+hipError_t launch_pack(const hts_desc& d, const hts_tile* index, const uint16_t* W, int64_t ldw,
+                       const float* col_scale, uint16_t* values, uint32_t* meta, hipStream_t s);
+hipError_t launch_unpack(const hts_desc& d, const hts_tile* index, const uint16_t* values,
+                         const uint32_t* meta, uint16_t* W_out, int64_t ldw, hipStream_t s);
+hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int sparse_path, hipStream_t s);
+hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s);
+hipError_t launch_col_norms(int32_t dtype, int64_t rows, int64_t K, const uint16_t* X, int64_t ldx,
+                            float* out, hipStream_t s);
+hipError_t launch_wanda_cost(const hts_desc& d, const uint16_t* W, int64_t ldw, const float* cs,
+                             double* cost, hipStream_t s);
+hipError_t launch_wanda_map(int64_t T, const double* cost, int64_t n_sparse, uint8_t* map,
+                            hipStream_t s);
+
+}  // namespace hts

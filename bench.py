@@ -1,0 +1,269 @@
+"""Benchmark of the hybrid tile-sparse (dense / 2:4) linear layer on one MI355X.
+
+Default workload: the LLaMA-2-7B MLP up-projection W[11008, 4096] bf16, 128x128
+tiles, 25 % of the tiles 2:4 (12.5 % overall sparsity), X ~ N(0,1) bf16.
+A step is one hybrid product at M = 2048 (the prefill shape) with the packed
+weight already resident in HBM; `value` is its algorithmic throughput
+2*M*(kept weights)/t.  The same run also measures the decode shapes M = 1 and
+M = 16 (HBM-bound; reported in GB/s of algorithmic bytes), the same-library
+dense product on the same shapes (speedup), torch.matmul for context, pack and
+unpack, and the CPU oracle on the host cores.
+
+Weights and activations are synthetic (seeded Gaussian layers of the 7B shape);
+packed-weight copies are rotated so the working set exceeds the 256 MB Infinity
+Cache.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense MFMA, published
+ROTATE_BYTES = 600 << 20       # > 2x the 256 MB Infinity Cache
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="7b_up", help="7b_up | 13b | sweep (other configs are parity cases)")
+    p.add_argument("--layer", type=int, default=0)
+    p.add_argument("--quick", action="store_true", help="profiling run: a few launches of each kernel, no oracle")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the sharding design is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tile_gemm_amd as hts
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = wl.config(args.config)
+    L = cfg.layers[args.layer]
+    M_big = max(cfg.Ms)
+    dec_Ms = [m for m in cfg.Ms if m <= 16]
+    tdt = torch.bfloat16 if L.dtype == "bf16" else torch.float16
+
+    # ---------------- inputs (seeded, synthetic) ----------------
+    W_bits = wl.weight_bits(cfg, L)
+    tmap = wl.tile_map(cfg, L)
+    X_bits = wl.activation_bits(cfg, L, M_big)
+    W = hts.tensor_from_bits(W_bits, L.dtype, dev)
+    X = hts.tensor_from_bits(X_bits, L.dtype, dev)
+    n_sparse = int(tmap.sum())
+    kept = L.N * L.K - n_sparse * L.bn * L.bk // 2
+
+    # pack (timed below as well)
+    pw0 = hts.pack(W, tmap, L.bn, L.bk)
+    torch.cuda.synchronize()
+    packed_bytes = pw0.packed_bytes
+    dense_bytes = 2 * L.N * L.K
+    n_rot = max(2, -(-ROTATE_BYTES // packed_bytes))
+    pws = [pw0] + [hts.PackedWeight(pw0.desc, pw0.index.clone(), pw0.values.clone(), pw0.meta.clone(),
+                                    pw0.sizes, pw0.tile_map) for _ in range(n_rot - 1)]
+    n_rot_d = max(2, -(-ROTATE_BYTES // dense_bytes))
+    Ws = [W] + [W.clone() for _ in range(n_rot_d - 1)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def time_launches(fn, n, reps=3):
+        """Average device time of one launch over n back-to-back launches (HIP events on this stream)."""
+        best = None
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(n):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / n
+            best = t if best is None else min(best, t)
+        return best
+
+    def time_graph(fn, per_graph, replays=20):
+        """Average device time of one launch, launches captured in a HIP graph (no host overhead)."""
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(per_graph):
+                fn(i)                 # warm (outside capture) on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(per_graph):
+                fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / (replays * per_graph)
+            best = t if best is None else min(best, t)
+        return best
+
+    results = {}
+
+    # ---------------- decode shapes (HBM-bound) ----------------
+    decode = []
+    for M in dec_Ms:
+        Xm = X[:M].contiguous()
+        Ys = [torch.empty((M, L.N), dtype=tdt, device=dev) for _ in range(n_rot)]
+        Yd = [torch.empty((M, L.N), dtype=tdt, device=dev) for _ in range(n_rot_d)]
+        hyb = lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n_rot])
+        den = lambda i: hts.dense_gemm(Xm, Ws[i % n_rot_d], out=Yd[i % n_rot_d])
+        mm = lambda i: torch.matmul(Xm, Ws[i % n_rot_d].t(), out=Yd[i % n_rot_d])
+        per = 4 if args.quick else 8 * max(n_rot, n_rot_d)
+        t_h = time_graph(hyb, per, 2 if args.quick else 25)
+        t_d = time_graph(den, per, 2 if args.quick else 25)
+        t_t = time_graph(mm, per, 2 if args.quick else 25)
+        alg_bytes = packed_bytes + 2 * M * L.K + 2 * M * L.N
+        den_bytes = dense_bytes + 2 * M * L.K + 2 * M * L.N
+        decode.append({
+            "M": M, "us": round(t_h * 1e6, 3),
+            "GB/s": round(alg_bytes / t_h / 1e9, 1),
+            "frac_hbm": round(alg_bytes / t_h / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": alg_bytes,
+            "dense_same_library_us": round(t_d * 1e6, 3),
+            "dense_same_library_GB/s": round(den_bytes / t_d / 1e9, 1),
+            "speedup_vs_dense": round(t_d / t_h, 3),
+            "torch_matmul_us": round(t_t * 1e6, 3),
+        })
+
+    # ---------------- prefill shape: the timed step ----------------
+    M = M_big
+    Xm = X
+    Ys = [torch.empty((M, L.N), dtype=tdt, device=dev) for _ in range(2)]
+    step = lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % 2])
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+    alg_flops = 2.0 * M * kept
+    dense_flops = 2.0 * M * L.N * L.K
+    tflops = alg_flops / t_step / 1e12
+
+    Ydd = [torch.empty((M, L.N), dtype=tdt, device=dev) for _ in range(2)]
+    n_pf = 10 if args.quick else 50
+    t_dense = time_launches(lambda i: hts.dense_gemm(Xm, Ws[i % n_rot_d], out=Ydd[i % 2]), n_pf)
+    t_torch = time_launches(lambda i: torch.matmul(Xm, Ws[i % n_rot_d].t(), out=Ydd[i % 2]), n_pf)
+
+    # ---------------- pack / unpack ----------------
+    vals_tmp = torch.empty_like(pw0.values)
+    meta_tmp = torch.empty_like(pw0.meta)
+    t_pack = time_launches(lambda i: hts.hts_pack(pw0.desc, pw0.index, Ws[i % n_rot_d], None, vals_tmp, meta_tmp),
+                           5 if args.quick else 20)
+    Wout = torch.empty_like(W)
+    t_unpack = time_launches(lambda i: hts.hts_unpack(pws[i % n_rot].desc, pws[i % n_rot].index,
+                                                      pws[i % n_rot].values, pws[i % n_rot].meta, Wout),
+                             5 if args.quick else 20)
+    pack_bytes = dense_bytes + packed_bytes
+
+    # ---------------- CPU oracle on the host cores ----------------
+    cpu = None
+    if not (args.quick or args.no_cpu):
+        import oracle
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        # the sample is the whole layer at the step's M (mask + fp64 product), repeated
+        reps, t_cpu = 0, []
+        while reps < 3 or (sum(t_cpu) < 10.0 and reps < 20):
+            t_c0 = time.perf_counter()
+            Wm_full = oracle.masked_weights(W_bits, L.dtype, tmap, L.bn, L.bk)
+            oracle.gemm_ref(X_bits, Wm_full, L.dtype)
+            t_cpu.append(time.perf_counter() - t_c0)
+            reps += 1
+        t_med = float(np.median(t_cpu))
+        cpu = {"value": round(alg_flops / t_med / 1e12, 5), "unit": "TFLOP/s",
+               "cores": int(threads), "kind": "oracle",
+               "sample": f"whole layer at M={M}: oracle mask + fp64 product, median of {reps} runs "
+                         f"({t_med:.2f} s each) on {len(os.sched_getaffinity(0))} visible host cores "
+                         f"({platform.processor() or platform.machine()}), BLAS threads {threads}"}
+
+    prefill = {
+        "M": M, "us": round(t_step * 1e6, 2),
+        "TFLOP/s": round(tflops, 2),
+        "dense_equivalent_TFLOP/s": round(dense_flops / t_step / 1e12, 2),
+        "frac_mfma": round(tflops / MFMA_PEAK_TFLOPS[L.dtype], 4),
+        "dense_same_library_us": round(t_dense * 1e6, 2),
+        "dense_same_library_TFLOP/s": round(dense_flops / t_dense / 1e12, 2),
+        "speedup_vs_dense": round(t_dense / t_step, 3),
+        "torch_matmul_us": round(t_torch * 1e6, 2),
+        "torch_matmul_TFLOP/s": round(dense_flops / t_torch / 1e12, 2),
+    }
+    line = {
+        "metric": "hybrid tile-sparse GEMM TFLOP/s & GB/s (% roofline), speedup vs dense, 7B shapes",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": L.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: W[{L.N}x{L.K}] {L.dtype}, tile {L.bn}x{L.bk}, "
+                               f"{n_sparse}/{L.T} tiles 2:4 ({100.0 * n_sparse * 0.5 / L.T:.1f}% overall sparsity), "
+                               f"X[{M}x{L.K}]; step = one hybrid product at M={M}",
+                   "M": M, "N": L.N, "K": L.K, "tile": [L.bn, L.bk], "sparse_tiles": n_sparse,
+                   "sparse_path": os.environ.get("HTS_SPARSE_PATH", "smfmac")},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS[L.dtype],
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS[L.dtype], 4), "traffic": None,
+                     "kernel": "gemm_prefill_kernel", "algorithmic_flops_per_launch": alg_flops},
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "prefill": prefill,
+        "pack": {"us": round(t_pack * 1e6, 2), "GB/s": round(pack_bytes / t_pack / 1e9, 1),
+                 "frac_hbm": round(pack_bytes / t_pack / 1e9 / HBM_PEAK_GBS, 4)},
+        "unpack": {"us": round(t_unpack * 1e6, 2), "GB/s": round(pack_bytes / t_unpack / 1e9, 1)},
+        "packed_bytes": packed_bytes,
+        "rotation_copies": n_rot,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,6 +26,9 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # no contraction of separate multiplies and adds: bit-exact selection and sums
     "-ffp-contract=off",
+    # matrix-core accumulators in VGPRs: dense and sparse instructions then share them
+    # without AGPR<->VGPR copies at the type branches
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

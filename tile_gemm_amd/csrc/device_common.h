@@ -60,30 +60,32 @@ template <> __device__ __forceinline__ f32x4 mfma_dense<F16T>(u32x4 a, u32x4 b, 
 // e < 8 and B[32+8q+(e-8)][j] for e >= 8.  C as for the dense instruction.
 // (Lane layout measured on gfx950 with one-hot operands.)
 template <typename T, int ABID>
-__device__ __forceinline__ f32x4 mfma_sparse(u32x4 a, u32x4 b_lo, u32x4 b_hi, uint32_t idx, f32x4 c);
+__device__ __forceinline__ f32x4 mfma_sparse(u32x4 a, u32x8 b, uint32_t idx, f32x4 c);
 template <>
-__device__ __forceinline__ f32x4 mfma_sparse<BF16T, 0>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
-    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ f32x4 mfma_sparse<BF16T, 0>(u32x4 a, u32x8 b, uint32_t idx, f32x4 c) {
     return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x16, b), c, (int)idx, 0, 0);
 }
 template <>
-__device__ __forceinline__ f32x4 mfma_sparse<BF16T, 1>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
-    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ f32x4 mfma_sparse<BF16T, 1>(u32x4 a, u32x8 b, uint32_t idx, f32x4 c) {
     return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x16, b), c, (int)idx, 0, 1);
 }
 template <>
-__device__ __forceinline__ f32x4 mfma_sparse<F16T, 0>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
-    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ f32x4 mfma_sparse<F16T, 0>(u32x4 a, u32x8 b, uint32_t idx, f32x4 c) {
     return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x16, b), c, (int)idx, 0, 0);
 }
 template <>
-__device__ __forceinline__ f32x4 mfma_sparse<F16T, 1>(u32x4 a, u32x4 lo, u32x4 hi, uint32_t idx, f32x4 c) {
-    u32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ f32x4 mfma_sparse<F16T, 1>(u32x4 a, u32x8 b, uint32_t idx, f32x4 c) {
     return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x16, b), c, (int)idx, 0, 1);
+}
+
+__device__ __forceinline__ u32x4 lo4(u32x8 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
+__device__ __forceinline__ u32x4 hi4(u32x8 v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
+__device__ __forceinline__ u32x8 cat8(u32x4 a, u32x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Expand two 2:4 groups (4 stored 16-bit values in `v`, codes in the low byte

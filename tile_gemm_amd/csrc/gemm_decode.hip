@@ -75,7 +75,7 @@ __device__ __forceinline__ f32x4 mma_tile(const TileRegs<BK>& R, f32x4 acc, int 
         for (int s = 0; s < BK / 64; ++s) {
             const uint32_t code = R.m[s] >> (16 * (g & 1));
             if (SP == SPARSE_SMFMAC) {
-                acc = mfma_sparse<T, 0>(R.a[s], R.x[2 * s], R.x[2 * s + 1], code, acc);
+                acc = mfma_sparse<T, 0>(R.a[s], cat8(R.x[2 * s], R.x[2 * s + 1]), code, acc);
             } else {
                 const u32x4 v = R.a[s];
                 acc = mfma_dense<T>(expand_two_groups(uint2{v[0], v[1]}, code & 0xFFu), R.x[2 * s], acc);

@@ -85,12 +85,27 @@ int64_t decode_max_m() {
 // Waves per panel of the streaming kernel: enough waves in total to keep HBM busy.
 int decode_ksplit(int64_t N) { return (N / 16 >= 512) ? 4 : 8; }
 
+// Block shape / pipeline depth of the tiled kernel: HTS_PREFILL_TILE = 128s2 (128 X rows per
+// workgroup, 2 stages, two workgroups per CU; default), 256s3, 128s3.
+int prefill_tile(const hts::GemmArgs& a) {
+    (void)a;
+    const char* v = getenv("HTS_PREFILL_TILE");
+    if (v && !strcmp(v, "256s3")) return 0;
+    if (v && !strcmp(v, "128s3")) return 2;
+    return 1;
+}
+
 hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
     hipError_t e;
-    if (a.M <= decode_max_m())
+    if (a.M <= decode_max_m()) {
         e = hts::launch_gemm_decode(a, decode_ksplit(a.N), sparse_path(), s);
-    else
-        e = hts::launch_gemm_prefill(a, sparse_path(), s);
+    } else {
+        const int tile = prefill_tile(a);
+        if (a.index && a.K / a.bk > hts::kPrefillMaxTileCols)
+            return fail(HTS_ERR_UNSUPPORTED, "K/bk=%lld tile columns exceed the %d kept in LDS by the tiled kernel",
+                        (long long)(a.K / a.bk), hts::kPrefillMaxTileCols);
+        e = hts::launch_gemm_prefill(a, sparse_path(), tile, s);
+    }
     return hip_status(e, "product kernel launch");
 }
 

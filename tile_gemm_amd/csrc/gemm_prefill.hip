@@ -27,7 +27,6 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_t;
 
 constexpr int kKS = 64;                 // K elements per slice
-constexpr int kThreads = 256;
 constexpr int kGroupBytes = 64 * 128;   // one 64-row weight group, dense (2:4 uses half)
 constexpr int kMetaGroupBytes = 64 * 8; // codes of one 64-row group for one slice
 constexpr int kMaxTileCols = 256;       // K/bk limit: the tile list of a tile row is kept in LDS
@@ -47,11 +46,17 @@ struct Layout {
     static constexpr int TOTAL = WCNT + 64;
 };
 
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_t*)lds, 16, 0, 0);
+// Dynamic LDS of the tiled kernels; copies address it by byte offset from an LDS-typed base,
+// so no generic-to-LDS pointer conversion is needed per copy.
+extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ lds_u8* lds_base() { return (lds_u8*)smem; }
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t*)(lds_base() + lds_off), 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_t*)lds, 4, 0, 0);
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_off) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t*)(lds_base() + lds_off), 4, 0, 0);
 }
 
 // Everything the copy jobs need, fixed for the whole K loop.  A job moves 1 KiB (64
@@ -66,23 +71,26 @@ struct Ctx {
     int64_t ldw;
     int64_t N, n0;
     int r0;                     // first row of the block inside its tile (0 when BN == bn)
-    int wave;
+    int wave, lane;
     int n_dense;                // dense tiles of the list (they come first)
     const uint2* list;          // {val_off, meta_off} of the tile row's tiles in list order
     int Tk;
-    const uint16_t* xsrc[BM / 32];
-    int d_row[2], d_col[2];     // dense group job rows / chunks (128 B rows)
-    int s_row, s_col;           // 2:4 group job (64 B rows)
-    int m_row, m_w;             // 2:4 codes job (one word per lane)
+    const uint16_t* xsrc[BM / 32];      // per X copy job of this wave
+    int d_off[2];                       // dense group jobs: row * BK + chunk
+    int64_t rm_off[2];                  // row-major weight jobs: row * ldw + chunk
+    int s_off;                          // 2:4 values job
+    int m_off;                          // 2:4 codes job
+    bool meta_to_sink;                  // waves 2, 3 repeat the codes copies of waves 0, 1
     __device__ __forceinline__ bool gvalid(int gi) const { return n0 + 64 * gi < N; }
 };
 
-// Issue the copies of slice ks into one LDS stage.  Every wave issues the same number of
-// copy instructions for every slice, BM/32 + 2 * BN/64, whatever the tile type (a 2:4 group's
-// codes need two 256-byte copies; waves 2 and 3 repeat them into a sink), so the wait for
-// one slice is a fixed count of outstanding copies.
-template <int BK, bool HYB, int BN, int BM, int NSTAGE>
-__device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM>& C, int ks, uint8_t* stage, uint8_t* sink) {
+// Copies of one slice into an LDS stage.  Per 64-row weight group there are 8 copy jobs:
+// dense = 8 x 1 KiB; 2:4 = 4 x 1 KiB of stored values, 2 x 256 B of codes and 2 padding copies
+// of the codes into a sink.  With 4 waves each wave issues BM/32 X copies and 2 copies per
+// group for every slice, whatever the tile types, so the wait for one slice is a fixed count
+// of outstanding copies.  KIND (dense / 2:4) is known at compile time: no branch per copy.
+template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE>
+__device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM>& C, int ks, uint32_t stage) {
     using Lo = Layout<BN, BM, NSTAGE>;
     constexpr int SPT = BK / kKS;
     const int p = ks / SPT, s = ks % SPT;     // list position, slice of the tile
@@ -95,37 +103,30 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM>& C, int k
         moff = __builtin_amdgcn_readfirstlane(e.y);
     }
 #pragma unroll
-    for (int v = 0; v < BM / 32; ++v) {
-        // X columns of list position p: the tile column stored in the list entry (HYB), or p itself
-        dma16(C.xsrc[v], stage + 1024 * (C.wave + 4 * v));
-    }
-    const bool dense = !HYB || p < C.n_dense;
+    for (int v = 0; v < BM / 32; ++v) dma16(C.xsrc[v], stage + 1024 * (C.wave + 4 * v));
 #pragma unroll
     for (int gi = 0; gi < Lo::NG; ++gi) {
-        if (!C.gvalid(gi)) {                    // rows past N: keep the copy count, land in the sink
-            dma16(C.xsrc[0], sink);
-            dma16(C.xsrc[0], sink);
-            continue;
-        }
-        uint8_t* ws = stage + Lo::WOFF + gi * kGroupBytes;
+        const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
         if (!HYB) {
-            const uint16_t* base = C.W + 64 * gi * C.ldw + ks * kKS;
+            if (!C.gvalid(gi)) {                // rows past N: keep the copy count, land in the sink
+                dma16(C.xsrc[0], Lo::SINK);
+                dma16(C.xsrc[0], Lo::SINK);
+                continue;
+            }
 #pragma unroll
             for (int v = 0; v < 2; ++v)
-                dma16(base + (int64_t)C.d_row[v] * C.ldw + 8 * C.d_col[v], ws + 1024 * (C.wave + 4 * v));
+                dma16(C.W + (64 * gi) * C.ldw + ks * kKS + C.rm_off[v], ws + 1024 * (C.wave + 4 * v));
             continue;
         }
-        const int r = C.r0 + 64 * gi;
-        if (dense) {
-            const uint16_t* base = C.values + voff + r * BK + s * kKS;
+        const int r = 64 * gi;                  // a block is one tile row: groups at rows 0, 64
+        if (DENSE) {
 #pragma unroll
             for (int v = 0; v < 2; ++v)
-                dma16(base + C.d_row[v] * BK + 8 * C.d_col[v], ws + 1024 * (C.wave + 4 * v));
+                dma16(C.values + voff + r * BK + s * kKS + C.d_off[v], ws + 1024 * (C.wave + 4 * v));
         } else {
-            const uint16_t* base = C.values + voff + r * (BK / 2) + s * (kKS / 2);
-            dma16(base + C.s_row * (BK / 2) + 8 * C.s_col, ws + 1024 * C.wave);
-            dma4(C.meta + moff + r * (BK / 32) + 2 * s + C.m_row * (BK / 32) + C.m_w,
-                 C.wave < 2 ? stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * C.wave : sink);
+            dma16(C.values + voff + r * (BK / 2) + s * (kKS / 2) + C.s_off, ws + 1024 * C.wave);
+            dma4(C.meta + moff + r * (BK / 32) + 2 * s + C.m_off,
+                 C.meta_to_sink ? (uint32_t)Lo::SINK : stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * C.wave);
         }
     }
 }
@@ -143,8 +144,10 @@ __device__ __forceinline__ void load_x(u32x8 (&Bx)[NBJ], const uint8_t* xs, int 
     for (int bj = 0; bj < NBJ; ++bj) Bx[bj] = cat8(ld16(xs + bj * 2048 + x0), ld16(xs + bj * 2048 + x1));
 }
 
-template <typename T, int SP, int NBJ>
-__device__ __forceinline__ void compute_dense(f32x4 (&acc)[4][NBJ], const uint8_t* xs, const uint8_t* ws, int lane) {
+// Weight fragments of row block b (16 rows) of a wave whose rows start at group g0: groups are
+// 8 KiB apart in LDS, a dense group holds 64 rows x 128 B, a 2:4 group 64 rows x 64 B (+ codes).
+template <typename T, int SP, int NBI, int NBJ>
+__device__ __forceinline__ void compute_dense(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws, int lane) {
     const int i = lane & 15, g = lane >> 4;
     const int c0 = (SP == SPARSE_SMFMAC) ? g : 2 * g;
     const int c1 = (SP == SPARSE_SMFMAC) ? 4 + g : 2 * g + 1;
@@ -154,61 +157,66 @@ __device__ __forceinline__ void compute_dense(f32x4 (&acc)[4][NBJ], const uint8_
     load_x<SP, NBJ>(Bx, xs, lane);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        u32x4 A[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) A[b] = ld16(ws + b * 2048 + (u ? a1 : a0));
+        for (int h = 0; h < NBI / 4; ++h) {
+            u32x4 A[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b) A[b] = ld16(ws + (4 * h + b) * 2048 + (u ? a1 : a0));
 #pragma unroll
-            for (int bj = 0; bj < NBJ; ++bj)
-                acc[b][bj] = mfma_dense<T>(A[b], u ? hi4(Bx[bj]) : lo4(Bx[bj]), acc[b][bj]);
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int bj = 0; bj < NBJ; ++bj)
+                    acc[4 * h + b][bj] = mfma_dense<T>(A[b], u ? hi4(Bx[bj]) : lo4(Bx[bj]), acc[4 * h + b][bj]);
+        }
     }
 }
 
-template <typename T, int SP, int NBJ>
-__device__ __forceinline__ void compute_sparse(f32x4 (&acc)[4][NBJ], const uint8_t* xs, const uint8_t* ws,
+template <typename T, int SP, int NBI, int NBJ>
+__device__ __forceinline__ void compute_sparse(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws,
                                                const uint32_t* ms, int lane) {
     const int i = lane & 15, g = lane >> 4;
     const int s0 = i * 64 + 16 * (g ^ ((i >> 2) & 3));
     u32x8 Bx[NBJ];
     load_x<SP, NBJ>(Bx, xs, lane);
-    if (SP == SPARSE_SMFMAC) {
-        u32x4 A[4];
-        uint32_t idx[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            A[b] = ld16(ws + b * 1024 + s0);
-            idx[b] = ms[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1));
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int bj = 0; bj < NBJ; ++bj) acc[b][bj] = mfma_sparse<T, 0>(A[b], Bx[bj], idx[b], acc[b][bj]);
-    } else {
-        // expansion order: lane group g, substep u covers dense k [16g + 8u, +8) of the slice =
-        // groups 4g + 2u, +1: stored bytes 16g + 8u of the row, codes at bit 16g + 8u
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+    for (int h = 0; h < NBI / 4; ++h) {
+        const uint8_t* wg = ws + h * kGroupBytes;
+        const uint32_t* mg = ms + h * (kMetaGroupBytes / 4);
+        if (SP == SPARSE_SMFMAC) {
             u32x4 A[4];
+            uint32_t idx[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const uint2 v = *reinterpret_cast<const uint2*>(ws + b * 1024 + s0 + 8 * u);
-                const uint32_t code = (ms[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1) + 8 * u)) & 0xFFu;
-                A[b] = expand_two_groups(v, code);
+                A[b] = ld16(wg + b * 1024 + s0);
+                idx[b] = mg[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1));
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int bj = 0; bj < NBJ; ++bj)
-                    acc[b][bj] = mfma_dense<T>(A[b], u ? hi4(Bx[bj]) : lo4(Bx[bj]), acc[b][bj]);
+                    acc[4 * h + b][bj] = mfma_sparse<T, 0>(A[b], Bx[bj], idx[b], acc[4 * h + b][bj]);
+        } else {
+            // expansion order: lane group g, substep u covers dense k [16g + 8u, +8) of the
+            // slice = groups 4g + 2u, +1: stored bytes 16g + 8u of the row, codes at bit 16g + 8u
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                u32x4 A[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(wg + b * 1024 + s0 + 8 * u);
+                    const uint32_t code = (mg[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1) + 8 * u)) & 0xFFu;
+                    A[b] = expand_two_groups(v, code);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int bj = 0; bj < NBJ; ++bj)
+                        acc[4 * h + b][bj] = mfma_dense<T>(A[b], u ? hi4(Bx[bj]) : lo4(Bx[bj]), acc[4 * h + b][bj]);
+            }
         }
     }
 }
 
-// One workgroup = one tile row (BN = bn) x BM rows of X.  Waves: BN/64 along N (one
-// 64-row group each) x the rest along M.  The tile row's tiles are walked as an ordered
-// list -- all dense tiles, then all 2:4 tiles -- so each half of the K loop runs one
-// instruction kind with no branch on the tile type (the sum does not depend on the order).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     // s_waitcnt with vmcnt = N (low 4 bits and bits 14..15), expcnt and lgkmcnt left at their maxima
@@ -216,11 +224,21 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, bool ROT = false>
-__global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB) {
+// Wait until the oldest slice in flight has landed, leaving min(NSTAGE - 2, later) younger
+// slices in flight (`later` = slices issued after it); each slice is PER copies per wave.
+template <int NSTAGE, int PER>
+__device__ __forceinline__ void wait_slice(int later) {
+    const int k = later < NSTAGE - 2 ? later : NSTAGE - 2;
+    if (NSTAGE >= 4 && k >= 2) wait_vm<(NSTAGE >= 4 ? 2 * PER : 0)>();
+    else if (NSTAGE >= 3 && k >= 1) wait_vm<(NSTAGE >= 3 ? PER : 0)>();
+    else wait_vm<0>();
+}
+
+template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE>
+__global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB) {
     using Lo = Layout<BN, BM, NSTAGE>;
-    constexpr int NG = BN / 64, WM = 4 / NG, WTM = BM / WM, NBJ = WTM / 16, SPT = BK / kKS;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int NW = 4;
+    constexpr int NG = BN / 64, WM = NW / NG, WTM = BM / WM, NBJ = WTM / 16, SPT = BK / kKS;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % NG, wm = wave / NG;
@@ -244,17 +262,21 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(const GemmArgs a
     C.W = HYB ? nullptr : a.W + C.n0 * a.ldw;
     C.r0 = 0;
     C.wave = wave;
+    C.lane = lane;
     C.Tk = (int)(a.K / BK);
     const int64_t m0 = (int64_t)mb * BM;
     for (int v = 0; v < 2; ++v) {
-        C.d_row[v] = 8 * (wave + 4 * v) + (lane >> 3);
-        C.d_col[v] = (lane & 7) ^ ((C.d_row[v] >> 1) & 7);
+        const int row = 8 * (wave + 4 * v) + (lane >> 3), col = (lane & 7) ^ ((row >> 1) & 7);
+        C.d_off[v] = row * BK + 8 * col;
+        C.rm_off[v] = (int64_t)row * a.ldw + 8 * col;
     }
-    C.s_row = 16 * wave + (lane >> 2);
-    C.s_col = (lane & 3) ^ ((C.s_row >> 2) & 3);
-    C.m_row = (64 * (wave & 1) + lane) >> 1;
-    C.m_w = lane & 1;
-
+    {
+        const int row = 16 * wave + (lane >> 2), col = (lane & 3) ^ ((row >> 2) & 3);
+        C.s_off = row * (BK / 2) + 8 * col;
+        const int wi = 64 * (wave & 1) + lane;
+        C.m_off = (wi >> 1) * (BK / 32) + (wi & 1);
+        C.meta_to_sink = wave >= 2;
+    }
     // ordered tile list of the tile row (dense first), tile columns kept for the X copies
     uint2* list = reinterpret_cast<uint2*>(smem + Lo::LIST);
     uint16_t* lcol = reinterpret_cast<uint16_t*>(smem + Lo::LCOL);
@@ -262,7 +284,6 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(const GemmArgs a
     C.list = list;
     if (HYB) {
         const int tn = (int)(C.n0 / a.bn);
-        const int rot = ROT ? tn : 0;
         const int t = tid;                         // one tile column per thread (Tk <= 256)
         hts_tile e = {0u, 0u, 0u, 0u};
         const bool have = t < C.Tk;
@@ -273,22 +294,19 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(const GemmArgs a
         const int below_s = __builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0));
         if (lane == 0) {
             wcount[wave] = __popcll(bd);
-            wcount[4 + wave] = __popcll(bs);
+            wcount[NW + wave] = __popcll(bs);
         }
         __syncthreads();
         int nd = 0, pd = 0, ps = 0;
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             nd += wcount[w];
             if (w < wave) {
                 pd += wcount[w];
-                ps += wcount[4 + w];
+                ps += wcount[NW + w];
             }
         }
         if (have) {
-            // each tile row starts its dense run and its 2:4 run at a different tile column, so
-            // the tile rows running together spread their reads over the L2 channels
-            const int ns = C.Tk - nd;
-            const int pos = isd ? (pd + below_d + rot) % nd : nd + (ps + below_s + rot) % ns;
+            const int pos = isd ? pd + below_d : nd + ps + below_s;
             list[pos] = uint2{e.val_off, e.meta_off};
             lcol[pos] = (uint16_t)t;
         }
@@ -299,21 +317,21 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(const GemmArgs a
     }
 
     // per-lane X sources of this wave's copy jobs; the tile column is added per slice
-    int64_t xrow[BM / 32];
-    int xc[BM / 32];
+    constexpr int XJ = BM / 32;            // X copy jobs per wave
+    const uint16_t* xbase[XJ];
 #pragma unroll
-    for (int v = 0; v < BM / 32; ++v) {
-        const int row = 8 * (wave + 4 * v) + (lane >> 3);
-        xc[v] = (lane & 7) ^ ((row >> 1) & 7);
-        int64_t m = m0 + row;
-        xrow[v] = (m < a.M ? m : a.M - 1) * a.ldx;   // rows past M only feed outputs that are not stored
+    for (int v = 0; v < XJ; ++v) {
+        const int row = 8 * (wave + NW * v) + (lane >> 3);
+        const int xc = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t m = m0 + row;
+        xbase[v] = a.X + (m < a.M ? m : a.M - 1) * a.ldx + 8 * xc;   // rows past M only feed unstored outputs
     }
     auto set_x = [&](int ks) {
         const int p = ks / SPT, s = ks % SPT;
         const int tk = HYB ? (int)lcol[p] : p;
         const int64_t k0 = (int64_t)tk * BK + s * kKS;
 #pragma unroll
-        for (int v = 0; v < BM / 32; ++v) C.xsrc[v] = a.X + xrow[v] + k0 + 8 * xc[v];
+        for (int v = 0; v < XJ; ++v) C.xsrc[v] = xbase[v] + k0;
     };
 
     f32x4 acc[4][NBJ];
@@ -325,38 +343,37 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(const GemmArgs a
     const int S = C.Tk * SPT, Sd = C.n_dense * SPT;
     const bool wvalid = C.gvalid(wn);
     const int xoff = wm * WTM * 128;
-    constexpr int PER_SLICE = BM / 32 + 2 * NG;     // copy instructions per wave per slice
-    uint8_t* sink = smem + Lo::SINK;
+    constexpr int PER_SLICE = XJ + 2 * NG;          // copy instructions per wave per slice
+    auto issue = [&](int kn) {
+        set_x(kn);
+        const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
+        if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true>(C, kn, stage);
+        else issue_slice<BK, HYB, BN, BM, NSTAGE, false>(C, kn, stage);
+    };
     // prologue: slices 0 .. NSTAGE-2 in flight
 #pragma unroll
-    for (int k = 0; k < NSTAGE - 1; ++k) {
-        if (k < S) {
-            set_x(k);
-            issue_slice<BK, HYB, BN, BM, NSTAGE>(C, k, smem + k * Lo::STAGE, sink);
-        }
-    }
+    for (int k = 0; k < NSTAGE - 1; ++k)
+        if (k < S) issue(k);
     auto step = [&](int ks) {
         // wait until slice ks has landed: later slices (up to NSTAGE-2 of them) may stay in flight
-        if (NSTAGE == 3 && ks + 1 < S) wait_vm<PER_SLICE>();
-        else wait_vm<0>();
+        wait_slice<NSTAGE, PER_SLICE>(S - 1 - ks);
         __syncthreads();                    // everyone's copies landed; stage of slice ks-1 is free
         const int kn = ks + NSTAGE - 1;
-        if (kn < S) {
-            set_x(kn);
-            issue_slice<BK, HYB, BN, BM, NSTAGE>(C, kn, smem + (kn % NSTAGE) * Lo::STAGE, sink);
-        }
+        if (kn < S) issue(kn);
         return smem + (ks % NSTAGE) * Lo::STAGE;
     };
     int ks = 0;
     for (; ks < Sd; ++ks) {
         const uint8_t* st = step(ks);
-        if (wvalid) compute_dense<T, SP, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
+        if (wvalid) compute_dense<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
     }
-    for (; ks < S; ++ks) {
-        const uint8_t* st = step(ks);
-        if (wvalid)
-            compute_sparse<T, SP, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
-                                       reinterpret_cast<const uint32_t*>(st + Lo::MOFF + wn * kMetaGroupBytes), lane);
+    if constexpr (HYB) {
+        for (; ks < S; ++ks) {
+            const uint8_t* st = step(ks);
+            if (wvalid)
+                compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
+                                           reinterpret_cast<const uint32_t*>(st + Lo::MOFF + wn * kMetaGroupBytes), lane);
+        }
     }
 
     // epilogue: acc[b][bj] lane (j + 16q) holds Y^T rows 4q..4q+3 of block b, column j of block bj
@@ -373,6 +390,296 @@ __global__ __launch_bounds__(kThreads) void gemm_prefill_kernel(const GemmArgs a
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Two tile rows per workgroup.  A 2*bn (weight rows) x BM (X rows) block moves fewer bytes
+// per flop from L2 than one tile row, and the copies from L2 are what bound the product at
+// large M.  The tile columns of the pair are ordered by their pair of tile types --
+// (dense, dense), (dense, 2:4), (2:4, dense), (2:4, 2:4) -- giving four runs; in each run
+// every wave (a wave works on one tile row) runs one instruction kind with no branch on the
+// tile type inside the K loop.
+// ---------------------------------------------------------------------------------------
+// Weight-stationary fragment order for the pair kernel: a wave holds the fragments of all its
+// NBI row blocks for one substep and streams the X fragments column block by column block,
+// keeping the live registers to NBI weight fragments plus one X fragment.
+template <typename T, int SP, int NBI, int NBJ>
+__device__ __forceinline__ void compute_dense_ws(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = (SP == SPARSE_SMFMAC) ? (u ? 4 + g : g) : (2 * g + u);
+        const int off = i * 128 + 16 * (c ^ ((i >> 1) & 7));
+        u32x4 A[NBI];
+#pragma unroll
+        for (int b = 0; b < NBI; ++b) A[b] = ld16(ws + b * 2048 + off);
+#pragma unroll
+        for (int bj = 0; bj < NBJ; ++bj) {
+            const u32x4 B = ld16(xs + bj * 2048 + off);
+#pragma unroll
+            for (int b = 0; b < NBI; ++b) acc[b][bj] = mfma_dense<T>(A[b], B, acc[b][bj]);
+        }
+    }
+}
+
+template <typename T, int SP, int NBI, int NBJ>
+__device__ __forceinline__ void compute_sparse_ws(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws,
+                                                  const uint32_t* ms, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    const int s0 = i * 64 + 16 * (g ^ ((i >> 2) & 3));
+    if (SP == SPARSE_SMFMAC) {
+        const int x0 = i * 128 + 16 * (g ^ ((i >> 1) & 7));
+        const int x1 = i * 128 + 16 * ((4 + g) ^ ((i >> 1) & 7));
+        u32x4 A[NBI];
+        uint32_t idx[NBI];
+#pragma unroll
+        for (int b = 0; b < NBI; ++b) {
+            const int h = b / 4, bb = b % 4;
+            A[b] = ld16(ws + h * kGroupBytes + bb * 1024 + s0);
+            idx[b] = ms[h * (kMetaGroupBytes / 4) + 2 * (16 * bb + i) + (g >> 1)] >> (16 * (g & 1));
+        }
+#pragma unroll
+        for (int bj = 0; bj < NBJ; ++bj) {
+            const u32x8 B = cat8(ld16(xs + bj * 2048 + x0), ld16(xs + bj * 2048 + x1));
+#pragma unroll
+            for (int b = 0; b < NBI; ++b) acc[b][bj] = mfma_sparse<T, 0>(A[b], B, idx[b], acc[b][bj]);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int xo = i * 128 + 16 * ((2 * g + u) ^ ((i >> 1) & 7));
+            u32x4 A[NBI];
+#pragma unroll
+            for (int b = 0; b < NBI; ++b) {
+                const int h = b / 4, bb = b % 4;
+                const uint2 v = *reinterpret_cast<const uint2*>(ws + h * kGroupBytes + bb * 1024 + s0 + 8 * u);
+                const uint32_t code =
+                    (ms[h * (kMetaGroupBytes / 4) + 2 * (16 * bb + i) + (g >> 1)] >> (16 * (g & 1) + 8 * u)) & 0xFFu;
+                A[b] = expand_two_groups(v, code);
+            }
+#pragma unroll
+            for (int bj = 0; bj < NBJ; ++bj) {
+                const u32x4 B = ld16(xs + bj * 2048 + xo);
+#pragma unroll
+                for (int b = 0; b < NBI; ++b) acc[b][bj] = mfma_dense<T>(A[b], B, acc[b][bj]);
+            }
+        }
+    }
+}
+
+template <int BNT, int BM, int NSTAGE>
+struct Layout2 {
+    static constexpr int NG = 2 * BNT / 64;                  // 64-row groups of the pair
+    static constexpr int WOFF = BM * 128;
+    static constexpr int MOFF = WOFF + NG * kGroupBytes;
+    static constexpr int STAGE = MOFF + NG * kMetaGroupBytes;
+    static constexpr int SINK = NSTAGE * STAGE;              // target of the padding copies
+    static constexpr int LIST = SINK + 1024;                 // {valA, metaA, valB, metaB} per position
+    static constexpr int LCOL = LIST + kMaxTileCols * 16;    // tile column of each position
+    static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // per-wave run counts while ordering
+    static constexpr int TOTAL = WCNT + 4 * 16 * 4;
+};
+
+template <typename T, int BK, bool HYB, int SP, int BNT, int BM, int NSTAGE, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_pair_kernel(const GemmArgs a, int NB, int MB) {
+    using Lo = Layout2<BNT, BM, NSTAGE>;
+    constexpr int kThreads = 64 * NW;
+    constexpr int NG = Lo::NG, GPR = BNT / 64, WM = NW / 2, WTM = BM / WM, NBJ = WTM / 16, NBI = BNT / 16;
+    constexpr int SPT = BK / kKS, XJ = BM / (8 * NW), WJ = 8 * NG / NW;
+    static_assert(XJ >= 1 && WJ >= 1 && NBJ >= 1, "block shape");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave & 1, wm = wave >> 1;      // tile row of the pair, X-row block
+
+    // block id -> output block: contiguous ranges per XCD, grouped along N, M fastest
+    const int total = NB * MB, L = blockIdx.x;
+    const int P = total / 8;
+    const int id = (L < 8 * P) ? (L % 8) * P + L / 8 : L;
+    const int gsz = kGroupN * MB;
+    const int grp = id / gsz, inb = id % gsz;
+    const int nb0 = grp * kGroupN;
+    const int gn = (NB - nb0 < kGroupN) ? (NB - nb0) : kGroupN;
+    const int nb = nb0 + inb % gn, mb = inb / gn;
+
+    const int64_t n0 = (int64_t)nb * 2 * BNT, m0 = (int64_t)mb * BM;
+    const bool validB = n0 + BNT < a.N;
+    const int Tk = (int)(a.K / BK);
+    uint4* list = reinterpret_cast<uint4*>(smem + Lo::LIST);
+    uint16_t* lcol = reinterpret_cast<uint16_t*>(smem + Lo::LCOL);
+    int* wcnt = reinterpret_cast<int*>(smem + Lo::WCNT);
+    const uint32_t sink = Lo::SINK;
+
+    // order the tile columns by their pair of types (runs 0..3), tile column order inside a run
+    int rend[4] = {Tk, Tk, Tk, Tk};
+    if (HYB) {
+        const int64_t tnA = n0 / BNT, tnB = tnA + 1;
+        const int t = tid;                          // one tile column per thread (Tk <= 256)
+        const bool have = t < Tk;
+        hts_tile eA = {0u, 0u, 0u, 0u}, eB = {0u, 0u, 0u, 0u};
+        if (have) {
+            eA = a.index[tnA * Tk + t];
+            if (validB) eB = a.index[tnB * Tk + t];
+        }
+        const int combo = 2 * (int)eA.type + (int)eB.type;
+        int below = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint64_t b = __ballot(have && combo == c);
+            if (combo == c)
+                below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+            if (lane == 0) wcnt[c * NW + wave] = __popcll(b);
+        }
+        __syncthreads();
+        int start = 0, mine = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            int cnt = 0, pre = 0;
+            for (int w = 0; w < NW; ++w) {
+                const int x = wcnt[c * NW + w];
+                cnt += x;
+                if (w < wave) pre += x;
+            }
+            if (combo == c) mine = start + pre + below;
+            start += cnt;
+            rend[c] = start;
+        }
+        if (have) {
+            list[mine] = uint4{eA.val_off, eA.meta_off, eB.val_off, eB.meta_off};
+            lcol[mine] = (uint16_t)t;
+        }
+        __syncthreads();
+    }
+
+    // per-lane sources of this wave's copy jobs, fixed for the K loop (8 waves: wave w does job w
+    // of every 64-row group, plus XJ jobs of the X slice)
+    static_assert(NW == 8 && WJ == NG, "one job per group per wave");
+    const uint16_t* xsrc[XJ];
+#pragma unroll
+    for (int v = 0; v < XJ; ++v) {
+        const int row = 8 * (wave + NW * v) + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t m = m0 + row;
+        xsrc[v] = a.X + (m < a.M ? m : a.M - 1) * a.ldx + 8 * c;   // rows past M only feed unstored outputs
+    }
+    const int q = wave;
+    const int drow = 8 * q + (lane >> 3), dcol = (lane & 7) ^ ((drow >> 1) & 7);
+    const int d_off = drow * BK + 8 * dcol;                                    // dense group job
+    const int srow = 16 * (q & 3) + (lane >> 2), scol = (lane & 3) ^ ((srow >> 2) & 3);
+    const int s_off = srow * (BK / 2) + 8 * scol;                              // 2:4 values job (q < 4)
+    const int wi = 64 * (q & 1) + lane;
+    const int m_off = (wi >> 1) * (BK / 32) + (wi & 1);                        // 2:4 codes job (q >= 4)
+    const int64_t rm_off = (int64_t)drow * a.ldw + 8 * dcol;                   // row-major weight job
+
+    // issue the copies of slice ks into a stage (fixed count per wave: XJ + NG)
+    auto issue = [&](int ks, uint32_t stage) {
+        const int p = ks / SPT, s = ks % SPT;
+        uint4 e = {0u, 0u, 0u, 0u};
+        int tk = p;
+        if (HYB) {                          // LDS reads before any copy of this slice
+            e = list[p];
+            e.x = __builtin_amdgcn_readfirstlane(e.x);
+            e.y = __builtin_amdgcn_readfirstlane(e.y);
+            e.z = __builtin_amdgcn_readfirstlane(e.z);
+            e.w = __builtin_amdgcn_readfirstlane(e.w);
+            tk = __builtin_amdgcn_readfirstlane((int)lcol[p]);
+        }
+        const int c = (p >= rend[0]) + (p >= rend[1]) + (p >= rend[2]);
+        const int64_t k0 = (int64_t)tk * BK + s * kKS;
+#pragma unroll
+        for (int v = 0; v < XJ; ++v) dma16(xsrc[v] + k0, stage + 1024 * (wave + NW * v));
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int rs = gi / GPR, r = 64 * (gi % GPR);
+            const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
+            if (rs == 1 && !validB) {
+                dma16(xsrc[0], sink);
+                continue;
+            }
+            if (!HYB) {
+                dma16(a.W + (n0 + 64 * gi) * a.ldw + k0 + rm_off, ws + 1024 * q);
+                continue;
+            }
+            const bool dense = ((rs ? c & 1 : c >> 1) == 0);
+            const uint32_t voff = rs ? e.z : e.x, moff = rs ? e.w : e.y;
+            if (dense) {
+                dma16(a.values + voff + r * BK + s * kKS + d_off, ws + 1024 * q);
+            } else if (q < 4) {
+                dma16(a.values + voff + r * (BK / 2) + s * (kKS / 2) + s_off, ws + 1024 * q);
+            } else {                        // jobs 4, 5: codes; 6, 7: the same into the sink
+                dma4(a.meta + moff + r * (BK / 32) + 2 * s + m_off,
+                     q < 6 ? stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * (q & 1) : sink);
+            }
+        }
+    };
+
+    f32x4 acc[NBI][NBJ];
+#pragma unroll
+    for (int b = 0; b < NBI; ++b)
+#pragma unroll
+        for (int bj = 0; bj < NBJ; ++bj) acc[b][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int S = Tk * SPT;
+    constexpr int PER_SLICE = XJ + WJ;
+#pragma unroll
+    for (int k = 0; k < NSTAGE - 1; ++k)
+        if (k < S) issue(k, k * Lo::STAGE);
+    auto step = [&](int ks) -> const uint8_t* {
+        wait_slice<NSTAGE, PER_SLICE>(S - 1 - ks);
+        __syncthreads();
+        const int kn = ks + NSTAGE - 1;
+        if (kn < S) issue(kn, (kn % NSTAGE) * Lo::STAGE);
+        return smem + (ks % NSTAGE) * Lo::STAGE;
+    };
+    const bool wvalid = wn == 0 || validB;
+    const int xoff = wm * WTM * 128;
+    const int woff = Lo::WOFF + wn * GPR * kGroupBytes, moff = Lo::MOFF + wn * GPR * kMetaGroupBytes;
+    int ks = 0;
+    for (int c = 0; c < 4; ++c) {
+        const int kend = rend[c] * SPT;
+        const bool mydense = ((wn ? c & 1 : c >> 1) == 0);
+        if (!wvalid) {
+            for (; ks < kend; ++ks) step(ks);
+        } else if (mydense) {
+            for (; ks < kend; ++ks) {
+                const uint8_t* st = step(ks);
+                compute_dense_ws<T, SP, NBI, NBJ>(acc, st + xoff, st + woff, lane);
+            }
+        } else {
+            for (; ks < kend; ++ks) {
+                const uint8_t* st = step(ks);
+                compute_sparse_ws<T, SP, NBI, NBJ>(acc, st + xoff, st + woff,
+                                                   reinterpret_cast<const uint32_t*>(st + moff), lane);
+            }
+        }
+    }
+
+    // epilogue: acc[b][bj] lane (j + 16q) holds Y^T rows 4q..4q+3 of block b, column j of block bj
+    if (!wvalid) return;
+    const int j = lane & 15, qd = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < NBI; ++b) {
+        const int64_t n = n0 + wn * BNT + 16 * b + 4 * qd;
+#pragma unroll
+        for (int bj = 0; bj < NBJ; ++bj) {
+            const int64_t m = m0 + wm * WTM + 16 * bj + j;
+            if (m < a.M) store_y4(a.Y, m * a.ldy + n, a.y_dtype, acc[b][bj]);
+        }
+    }
+}
+
+template <typename T, int BK, bool HYB, int SP, int BNT, int BM, int NSTAGE, int NW>
+hipError_t launch_pair(const GemmArgs& a, hipStream_t s) {
+    using Lo = Layout2<BNT, BM, NSTAGE>;
+    auto kern = gemm_pair_kernel<T, BK, HYB, SP, BNT, BM, NSTAGE, NW>;
+    static bool attr_set = false;   // per instantiation; raising the dynamic-LDS limit is idempotent
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Lo::TOTAL);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int NB = (int)((a.N + 2 * BNT - 1) / (2 * BNT)), MB = (int)((a.M + BM - 1) / BM);
+    kern<<<dim3((unsigned)(NB * MB)), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB);
+    return hipGetLastError();
+}
+
 template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     using Lo = Layout<BN, BM, NSTAGE>;
@@ -384,23 +691,27 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
         attr_set = true;
     }
     const int NB = (int)((a.N + BN - 1) / BN), MB = (int)((a.M + BM - 1) / BM);
-    kern<<<dim3((unsigned)(NB * MB)), dim3(kThreads), Lo::TOTAL, s>>>(a, NB, MB);
+    kern<<<dim3((unsigned)(NB * MB)), dim3(256), Lo::TOTAL, s>>>(a, NB, MB);
     return hipGetLastError();
 }
 
 template <typename T, int BK, bool HYB, int SP>
 hipError_t launch4(const GemmArgs& a, int tile, hipStream_t s) {
-    // one tile row per workgroup: BN = bn (a row-major weight uses 128-row blocks)
-    // tile: 0 = 256 X rows, 3 stages; 1 = 128 rows, 2 stages; 2 = 128 rows, 3 stages
+    // tile 0: one tile row x 128 X rows, 4 waves, 2 stages (two workgroups per CU)
+    //      1: two tile rows x 256 X rows, 8 waves, 2 stages;  2: two tile rows x 128 X rows
     const int bn = HYB ? a.bn : 128;
     if (bn == 64) {
-        if (tile == 0) return launch_tile<T, BK, HYB, SP, 64, 256, 3>(a, s);
-        if (tile == 1) return launch_tile<T, BK, HYB, SP, 64, 128, 2>(a, s);
-        return launch_tile<T, BK, HYB, SP, 64, 128, 3>(a, s);
+        switch (tile) {
+            case 1: return launch_pair<T, BK, HYB, SP, 64, 256, 2, 8>(a, s);
+            case 2: return launch_pair<T, BK, HYB, SP, 64, 128, 2, 8>(a, s);
+            default: return launch_tile<T, BK, HYB, SP, 64, 128, 2>(a, s);
+        }
     }
-    if (tile == 0) return launch_tile<T, BK, HYB, SP, 128, 256, 3>(a, s);
-    if (tile == 1) return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
-    return launch_tile<T, BK, HYB, SP, 128, 128, 3>(a, s);
+    switch (tile) {
+        case 1: return launch_pair<T, BK, HYB, SP, 128, 256, 2, 8>(a, s);
+        case 2: return launch_pair<T, BK, HYB, SP, 128, 128, 2, 8>(a, s);
+        default: return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
+    }
 }
 
 template <typename T, int BK, bool HYB>

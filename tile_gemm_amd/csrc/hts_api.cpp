@@ -85,14 +85,17 @@ int64_t decode_max_m() {
 // Waves per panel of the streaming kernel: enough waves in total to keep HBM busy.
 int decode_ksplit(int64_t N) { return (N / 16 >= 512) ? 4 : 8; }
 
-// Block shape / pipeline depth of the tiled kernel: HTS_PREFILL_TILE = 128s2 (128 X rows per
-// workgroup, 2 stages, two workgroups per CU; default), 256s3, 128s3.
+// Block shape of the tiled kernel (HTS_PREFILL_TILE overrides): r128 = one tile row x 128 X
+// rows per workgroup, 4 waves, two workgroups per CU (default); p256 / p128 = two tile rows x
+// 256 / 128 X rows, 8 waves.
 int prefill_tile(const hts::GemmArgs& a) {
     (void)a;
     const char* v = getenv("HTS_PREFILL_TILE");
-    if (v && !strcmp(v, "256s3")) return 0;
-    if (v && !strcmp(v, "128s3")) return 2;
-    return 1;
+    if (v && *v) {
+        if (!strcmp(v, "p256")) return 1;
+        if (!strcmp(v, "p128")) return 2;
+    }
+    return 0;
 }
 
 hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {

@@ -82,8 +82,22 @@ int64_t decode_max_m() {
     return 16;
 }
 
-// Waves per panel of the streaming kernel: enough waves in total to keep HBM busy.
-int decode_ksplit(int64_t N) { return (N / 16 >= 512) ? 4 : 8; }
+// Waves per panel of the streaming kernel (HTS_DECODE_KSPLIT=4|8|16 overrides).
+int decode_ksplit(const hts::GemmArgs& a) {
+    const char* v = getenv("HTS_DECODE_KSPLIT");
+    if (v && (!strcmp(v, "4") || !strcmp(v, "8") || !strcmp(v, "16"))) return atoi(v);
+    (void)a;
+    return 8;
+}
+
+// Tile columns (128 wide) whose loads a wave of the streaming kernel issues together
+// (HTS_DECODE_NT=2|4 overrides).
+int decode_nt(const hts::GemmArgs& a) {
+    const char* v = getenv("HTS_DECODE_NT");
+    if (v && (!strcmp(v, "2") || !strcmp(v, "4"))) return atoi(v);
+    (void)a;
+    return 2;
+}
 
 // Block shape of the tiled kernel (HTS_PREFILL_TILE overrides): r128 = one tile row x 128 X
 // rows per workgroup, 4 waves, two workgroups per CU (default); p256 / p128 = two tile rows x
@@ -101,12 +115,12 @@ int prefill_tile(const hts::GemmArgs& a) {
 hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
     hipError_t e;
     if (a.M <= decode_max_m()) {
-        e = hts::launch_gemm_decode(a, decode_ksplit(a.N), sparse_path(), s);
+        e = hts::launch_gemm_decode(a, decode_ksplit(a), decode_nt(a), sparse_path(), s);
     } else {
         const int tile = prefill_tile(a);
-        if (a.index && a.K / a.bk > hts::kPrefillMaxTileCols)
-            return fail(HTS_ERR_UNSUPPORTED, "K/bk=%lld tile columns exceed the %d kept in LDS by the tiled kernel",
-                        (long long)(a.K / a.bk), hts::kPrefillMaxTileCols);
+        if (a.index && a.K / a.bk > hts::kMaxTileColsPerRow)
+            return fail(HTS_ERR_UNSUPPORTED, "K/bk=%lld tile columns exceed the %d of one tile row the tiled kernel holds",
+                        (long long)(a.K / a.bk), hts::kMaxTileColsPerRow);
         e = hts::launch_gemm_prefill(a, sparse_path(), tile, s);
     }
     return hip_status(e, "product kernel launch");

@@ -17,8 +17,8 @@
 // The tile index of the workgroup's tile rows is read into LDS once, so no
 // weight load waits on an index load.  Workgroups are numbered so that each XCD
 // (own L2) receives a contiguous range of output blocks, walked in groups of 8
-// N-blocks with M fastest: blocks running together on one XCD share their W and
-// X slices in its L2.
+// N-blocks (N fastest inside a group): blocks running together on one XCD share
+// their W and X slices in its L2.
 #include "gemm_common.h"
 
 namespace hts {
@@ -31,6 +31,33 @@ constexpr int kGroupBytes = 64 * 128;   // one 64-row weight group, dense (2:4 u
 constexpr int kMetaGroupBytes = 64 * 8; // codes of one 64-row group for one slice
 constexpr int kMaxTileCols = 256;       // K/bk limit: the tile list of a tile row is kept in LDS
 constexpr int kGroupN = 8;
+
+// Block id -> output block (nb, mb).  ord = xcd | (gsn << 1) | (mfast << 6):
+//   xcd   : 1 = each XCD (block id % 8) receives a contiguous range of the order below
+//   gsn   : N-blocks per group (1..31); groups are walked in order
+//   mfast : inside a group, 1 = M-blocks fastest, 0 = N-blocks fastest
+// Default: contiguous per XCD, groups of 8 N-blocks, N fastest, so that the workgroups running
+// together on one XCD cover about 8 N-blocks x 8 M-blocks and share W and X slices in its L2.
+__device__ __forceinline__ void block_of(int L, int NB, int MB, int ord, int& nb, int& mb) {
+    const int total = NB * MB;
+    int id = L;
+    if (ord & 1) {
+        const int P = total / 8;
+        id = (L < 8 * P) ? (L % 8) * P + L / 8 : L;
+    }
+    const int g = (ord >> 1) & 31, mfast = (ord >> 6) & 1;
+    const int gsz = g * MB;
+    const int grp = id / gsz, inb = id % gsz;
+    const int nb0 = grp * g;
+    const int gn = (NB - nb0 < g) ? (NB - nb0) : g;
+    if (mfast) {
+        nb = nb0 + inb / MB;
+        mb = inb % MB;
+    } else {
+        nb = nb0 + inb % gn;
+        mb = inb / gn;
+    }
+}
 
 // LDS image of one stage: X slice (BM rows x 128 B), BN/64 weight groups, their codes.
 template <int BN, int BM, int NSTAGE>
@@ -235,7 +262,7 @@ __device__ __forceinline__ void wait_slice(int later) {
 }
 
 template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE>
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB) {
+__global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord) {
     using Lo = Layout<BN, BM, NSTAGE>;
     constexpr int NW = 4;
     constexpr int NG = BN / 64, WM = NW / NG, WTM = BM / WM, NBJ = WTM / 16, SPT = BK / kKS;
@@ -243,15 +270,9 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % NG, wm = wave / NG;
 
-    // block id -> output block: contiguous ranges per XCD, grouped along N, M fastest
-    const int total = NB * MB, L = blockIdx.x;
-    const int P = total / 8;
-    const int id = (L < 8 * P) ? (L % 8) * P + L / 8 : L;
-    const int gsz = kGroupN * MB;
-    const int grp = id / gsz, inb = id % gsz;
-    const int nb0 = grp * kGroupN;
-    const int gn = (NB - nb0 < kGroupN) ? (NB - nb0) : kGroupN;
-    const int nb = nb0 + inb % gn, mb = inb / gn;
+    // block id -> output block
+    int nb, mb;
+    block_of(blockIdx.x, NB, MB, ord, nb, mb);
 
     Ctx<BK, HYB, BN, BM> C;
     C.values = a.values;
@@ -479,7 +500,7 @@ struct Layout2 {
 };
 
 template <typename T, int BK, bool HYB, int SP, int BNT, int BM, int NSTAGE, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_pair_kernel(const GemmArgs a, int NB, int MB) {
+__global__ __launch_bounds__(64 * NW) void gemm_pair_kernel(const GemmArgs a, int NB, int MB, int ord) {
     using Lo = Layout2<BNT, BM, NSTAGE>;
     constexpr int kThreads = 64 * NW;
     constexpr int NG = Lo::NG, GPR = BNT / 64, WM = NW / 2, WTM = BM / WM, NBJ = WTM / 16, NBI = BNT / 16;
@@ -489,15 +510,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_kernel(const GemmArgs a, in
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & 1, wm = wave >> 1;      // tile row of the pair, X-row block
 
-    // block id -> output block: contiguous ranges per XCD, grouped along N, M fastest
-    const int total = NB * MB, L = blockIdx.x;
-    const int P = total / 8;
-    const int id = (L < 8 * P) ? (L % 8) * P + L / 8 : L;
-    const int gsz = kGroupN * MB;
-    const int grp = id / gsz, inb = id % gsz;
-    const int nb0 = grp * kGroupN;
-    const int gn = (NB - nb0 < kGroupN) ? (NB - nb0) : kGroupN;
-    const int nb = nb0 + inb % gn, mb = inb / gn;
+    // block id -> output block
+    int nb, mb;
+    block_of(blockIdx.x, NB, MB, ord, nb, mb);
 
     const int64_t n0 = (int64_t)nb * 2 * BNT, m0 = (int64_t)mb * BM;
     const bool validB = n0 + BNT < a.N;
@@ -665,6 +680,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_kernel(const GemmArgs a, in
     }
 }
 
+// Block order of the tiled kernels (HTS_PREFILL_ORDER overrides; see block_of).
+int prefill_order() {
+    const char* e = getenv("HTS_PREFILL_ORDER");
+    const int v = (e && *e) ? atoi(e) : -1;
+    const int g = (v >> 1) & 31;
+    if (v < 0 || v > 127 || g == 0) return 1 | (kGroupN << 1);   // groups of at least one N-block
+    return v;
+}
+
 template <typename T, int BK, bool HYB, int SP, int BNT, int BM, int NSTAGE, int NW>
 hipError_t launch_pair(const GemmArgs& a, hipStream_t s) {
     using Lo = Layout2<BNT, BM, NSTAGE>;
@@ -676,7 +700,7 @@ hipError_t launch_pair(const GemmArgs& a, hipStream_t s) {
         attr_set = true;
     }
     const int NB = (int)((a.N + 2 * BNT - 1) / (2 * BNT)), MB = (int)((a.M + BM - 1) / BM);
-    kern<<<dim3((unsigned)(NB * MB)), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB);
+    kern<<<dim3((unsigned)(NB * MB)), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
     return hipGetLastError();
 }
 
@@ -691,7 +715,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
         attr_set = true;
     }
     const int NB = (int)((a.N + BN - 1) / BN), MB = (int)((a.M + BM - 1) / BM);
-    kern<<<dim3((unsigned)(NB * MB)), dim3(256), Lo::TOTAL, s>>>(a, NB, MB);
+    kern<<<dim3((unsigned)(NB * MB)), dim3(256), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
     return hipGetLastError();
 }
 

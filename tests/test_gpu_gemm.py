@@ -164,3 +164,22 @@ def test_deterministic(M):
     Y2 = hts.gemm(Xt, pw, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("Tk,kind", [(40, "alternate"), (70, "random"), (33, "last_only")])
+def test_tile_rows_of_many_tile_columns(Tk, kind):
+    # tile rows of more than 32 and more than 64 tile columns with mixed types (lists and per-tile
+    # state that span several 32-bit words), at a ragged M
+    N, K, M, bn, bk = 256, 128 * Tk, 300, 128, 128
+    T = (N // bn) * Tk
+    g = np.random.default_rng(Tk)
+    m = {"alternate": np.arange(T) % 2, "random": g.random(T) < 0.5,
+         "last_only": np.arange(T) % Tk == Tk - 1}[kind].astype(np.uint8)
+    W = wl.gaussian_bits((N, K), 0.02, "bf16", g)
+    X = wl.gaussian_bits((M, K), 1.0, "bf16", g)
+    say(f"[gemm-wide] Tk={Tk} {kind}")
+    Y_ref = oracle.hybrid_ref(X, W, "bf16", m, bn, bk)
+    pw = hts.pack(hts.tensor_from_bits(W, "bf16", DEV), m, bn, bk)
+    Y = hts.gemm(hts.tensor_from_bits(X, "bf16", DEV), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), Y_ref, f"Tk={Tk} {kind}")

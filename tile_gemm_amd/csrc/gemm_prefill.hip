@@ -89,9 +89,11 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_off) {
 // Everything the copy jobs need, fixed for the whole K loop.  A job moves 1 KiB (64
 // lanes x 16 B) into contiguous LDS; each lane picks the global chunk whose swizzled
 // LDS position is its slot.
-template <int BK, bool HYB, int BN, int BM>
+template <int BK, bool HYB, int BN, int BM, int NW>
 struct Ctx {
     static constexpr int NG = BN / 64;
+    static constexpr int JPG = 8 / NW;  // copy jobs per 64-row group per wave
+    static constexpr int XJ = BM / (8 * NW);  // X copy jobs per wave
     const uint16_t* values;
     const uint32_t* meta;
     const uint16_t* W;          // row-major weight (dense product), row n0
@@ -102,22 +104,23 @@ struct Ctx {
     int n_dense;                // dense tiles of the list (they come first)
     const uint2* list;          // {val_off, meta_off} of the tile row's tiles in list order
     int Tk;
-    const uint16_t* xsrc[BM / 32];      // per X copy job of this wave
-    int d_off[2];                       // dense group jobs: row * BK + chunk
-    int64_t rm_off[2];                  // row-major weight jobs: row * ldw + chunk
+    const uint16_t* xsrc[XJ];           // per X copy job of this wave
+    int d_off[JPG];                     // dense group jobs: row * BK + chunk
+    int64_t rm_off[JPG];                // row-major weight jobs: row * ldw + chunk
     int s_off;                          // 2:4 values job
     int m_off;                          // 2:4 codes job
-    bool meta_to_sink;                  // waves 2, 3 repeat the codes copies of waves 0, 1
+    bool meta_to_sink;                  // codes jobs 2, 3 repeat jobs 0, 1 into the sink
     __device__ __forceinline__ bool gvalid(int gi) const { return n0 + 64 * gi < N; }
 };
 
 // Copies of one slice into an LDS stage.  Per 64-row weight group there are 8 copy jobs:
 // dense = 8 x 1 KiB; 2:4 = 4 x 1 KiB of stored values, 2 x 256 B of codes and 2 padding copies
-// of the codes into a sink.  With 4 waves each wave issues BM/32 X copies and 2 copies per
+// of the codes into a sink.  Each of the NW waves issues BM/(8 NW) X copies and 8/NW copies per
 // group for every slice, whatever the tile types, so the wait for one slice is a fixed count
 // of outstanding copies.  KIND (dense / 2:4) is known at compile time: no branch per copy.
-template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE>
-__device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM>& C, int ks, uint32_t stage) {
+template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW>
+__device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, int ks, uint32_t stage) {
+    constexpr int JPG = 8 / NW;
     using Lo = Layout<BN, BM, NSTAGE>;
     constexpr int SPT = BK / kKS;
     const int p = ks / SPT, s = ks % SPT;     // list position, slice of the tile
@@ -130,30 +133,35 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM>& C, int k
         moff = __builtin_amdgcn_readfirstlane(e.y);
     }
 #pragma unroll
-    for (int v = 0; v < BM / 32; ++v) dma16(C.xsrc[v], stage + 1024 * (C.wave + 4 * v));
+    for (int v = 0; v < BM / (8 * NW); ++v) dma16(C.xsrc[v], stage + 1024 * (C.wave + NW * v));
 #pragma unroll
     for (int gi = 0; gi < Lo::NG; ++gi) {
         const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
         if (!HYB) {
             if (!C.gvalid(gi)) {                // rows past N: keep the copy count, land in the sink
-                dma16(C.xsrc[0], Lo::SINK);
-                dma16(C.xsrc[0], Lo::SINK);
+#pragma unroll
+                for (int v = 0; v < JPG; ++v) dma16(C.xsrc[0], Lo::SINK);
                 continue;
             }
 #pragma unroll
-            for (int v = 0; v < 2; ++v)
-                dma16(C.W + (64 * gi) * C.ldw + ks * kKS + C.rm_off[v], ws + 1024 * (C.wave + 4 * v));
+            for (int v = 0; v < JPG; ++v)
+                dma16(C.W + (64 * gi) * C.ldw + ks * kKS + C.rm_off[v], ws + 1024 * (C.wave + NW * v));
             continue;
         }
         const int r = 64 * gi;                  // a block is one tile row: groups at rows 0, 64
         if (DENSE) {
 #pragma unroll
-            for (int v = 0; v < 2; ++v)
-                dma16(C.values + voff + r * BK + s * kKS + C.d_off[v], ws + 1024 * (C.wave + 4 * v));
+            for (int v = 0; v < JPG; ++v)
+                dma16(C.values + voff + r * BK + s * kKS + C.d_off[v], ws + 1024 * (C.wave + NW * v));
         } else {
-            dma16(C.values + voff + r * (BK / 2) + s * (kKS / 2) + C.s_off, ws + 1024 * C.wave);
-            dma4(C.meta + moff + r * (BK / 32) + 2 * s + C.m_off,
-                 C.meta_to_sink ? (uint32_t)Lo::SINK : stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * C.wave);
+            // jobs 0-3: stored values; 4, 5: codes; 6, 7: the codes again into the sink.  With 4
+            // waves wave w does jobs w and 4 + w, with 8 waves job w.
+            if (NW == 4 || C.wave < 4)
+                dma16(C.values + voff + r * (BK / 2) + s * (kKS / 2) + C.s_off, ws + 1024 * (C.wave & 3));
+            if (NW == 4 || C.wave >= 4)
+                dma4(C.meta + moff + r * (BK / 32) + 2 * s + C.m_off,
+                     C.meta_to_sink ? (uint32_t)Lo::SINK
+                                    : stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * (C.wave & 1));
         }
     }
 }
@@ -182,6 +190,23 @@ __device__ __forceinline__ void compute_dense(f32x4 (&acc)[NBI][NBJ], const uint
     const int a1 = i * 128 + 16 * (c1 ^ ((i >> 1) & 7));
     u32x8 Bx[NBJ];
     load_x<SP, NBJ>(Bx, xs, lane);
+    if constexpr (NBI == 4) {
+        // every fragment of the slice is read before the first product: one LDS wait per slice
+        u32x4 A[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) A[u][b] = ld16(ws + b * 2048 + (u ? a1 : a0));
+        __builtin_amdgcn_sched_barrier(0);   // keep every read ahead of the products
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int bj = 0; bj < NBJ; ++bj)
+                    acc[b][bj] = mfma_dense<T>(A[u][b], u ? hi4(Bx[bj]) : lo4(Bx[bj]), acc[b][bj]);
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -261,11 +286,12 @@ __device__ __forceinline__ void wait_slice(int later) {
     else wait_vm<0>();
 }
 
-template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE>
-__global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord) {
+template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord) {
     using Lo = Layout<BN, BM, NSTAGE>;
-    constexpr int NW = 4;
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     constexpr int NG = BN / 64, WM = NW / NG, WTM = BM / WM, NBJ = WTM / 16, SPT = BK / kKS;
+    static_assert(NBJ >= 1 && BM % (8 * NW) == 0 && 2 * NW <= 16, "block shape");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % NG, wm = wave / NG;
@@ -274,7 +300,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int
     int nb, mb;
     block_of(blockIdx.x, NB, MB, ord, nb, mb);
 
-    Ctx<BK, HYB, BN, BM> C;
+    Ctx<BK, HYB, BN, BM, NW> C;
     C.values = a.values;
     C.meta = a.meta;
     C.ldw = a.ldw;
@@ -286,17 +312,17 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int
     C.lane = lane;
     C.Tk = (int)(a.K / BK);
     const int64_t m0 = (int64_t)mb * BM;
-    for (int v = 0; v < 2; ++v) {
-        const int row = 8 * (wave + 4 * v) + (lane >> 3), col = (lane & 7) ^ ((row >> 1) & 7);
+    for (int v = 0; v < 8 / NW; ++v) {
+        const int row = 8 * (wave + NW * v) + (lane >> 3), col = (lane & 7) ^ ((row >> 1) & 7);
         C.d_off[v] = row * BK + 8 * col;
         C.rm_off[v] = (int64_t)row * a.ldw + 8 * col;
     }
     {
-        const int row = 16 * wave + (lane >> 2), col = (lane & 3) ^ ((row >> 2) & 3);
+        const int row = 16 * (wave & 3) + (lane >> 2), col = (lane & 3) ^ ((row >> 2) & 3);
         C.s_off = row * (BK / 2) + 8 * col;
         const int wi = 64 * (wave & 1) + lane;
         C.m_off = (wi >> 1) * (BK / 32) + (wi & 1);
-        C.meta_to_sink = wave >= 2;
+        C.meta_to_sink = (NW == 4) ? wave >= 2 : wave >= 6;
     }
     // ordered tile list of the tile row (dense first), tile columns kept for the X copies
     uint2* list = reinterpret_cast<uint2*>(smem + Lo::LIST);
@@ -338,7 +364,7 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int
     }
 
     // per-lane X sources of this wave's copy jobs; the tile column is added per slice
-    constexpr int XJ = BM / 32;            // X copy jobs per wave
+    constexpr int XJ = BM / (8 * NW);      // X copy jobs per wave
     const uint16_t* xbase[XJ];
 #pragma unroll
     for (int v = 0; v < XJ; ++v) {
@@ -364,12 +390,12 @@ __global__ __launch_bounds__(256) void gemm_prefill_kernel(const GemmArgs a, int
     const int S = C.Tk * SPT, Sd = C.n_dense * SPT;
     const bool wvalid = C.gvalid(wn);
     const int xoff = wm * WTM * 128;
-    constexpr int PER_SLICE = XJ + 2 * NG;          // copy instructions per wave per slice
+    constexpr int PER_SLICE = XJ + NG * (8 / NW);   // copy instructions per wave per slice
     auto issue = [&](int kn) {
         set_x(kn);
         const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
-        if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true>(C, kn, stage);
-        else issue_slice<BK, HYB, BN, BM, NSTAGE, false>(C, kn, stage);
+        if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW>(C, kn, stage);
+        else issue_slice<BK, HYB, BN, BM, NSTAGE, false, NW>(C, kn, stage);
     };
     // prologue: slices 0 .. NSTAGE-2 in flight
 #pragma unroll
@@ -502,7 +528,6 @@ struct Layout2 {
 template <typename T, int BK, bool HYB, int SP, int BNT, int BM, int NSTAGE, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_pair_kernel(const GemmArgs a, int NB, int MB, int ord) {
     using Lo = Layout2<BNT, BM, NSTAGE>;
-    constexpr int kThreads = 64 * NW;
     constexpr int NG = Lo::NG, GPR = BNT / 64, WM = NW / 2, WTM = BM / WM, NBJ = WTM / 16, NBI = BNT / 16;
     constexpr int SPT = BK / kKS, XJ = BM / (8 * NW), WJ = 8 * NG / NW;
     static_assert(XJ >= 1 && WJ >= 1 && NBJ >= 1, "block shape");
@@ -704,10 +729,10 @@ hipError_t launch_pair(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE>
+template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW = 4>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     using Lo = Layout<BN, BM, NSTAGE>;
-    auto kern = gemm_prefill_kernel<T, BK, HYB, SP, BN, BM, NSTAGE>;
+    auto kern = gemm_prefill_kernel<T, BK, HYB, SP, BN, BM, NSTAGE, NW>;
     static bool attr_set = false;   // per instantiation; raising the dynamic-LDS limit is idempotent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Lo::TOTAL);
@@ -715,7 +740,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
         attr_set = true;
     }
     const int NB = (int)((a.N + BN - 1) / BN), MB = (int)((a.M + BM - 1) / BM);
-    kern<<<dim3((unsigned)(NB * MB)), dim3(256), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
+    kern<<<dim3((unsigned)(NB * MB)), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
     return hipGetLastError();
 }
 

@@ -29,73 +29,87 @@
 namespace hts {
 namespace {
 
-template <int BK>
+template <int BK, int PP>
 struct TileRegs {
-    u32x4 a[BK / 32];      // dense: BK/32 chunks; 2:4: BK/64 chunks
-    uint32_t m[BK / 64];   // 2:4 metadata words, one per slice
-    u32x4 x[BK / 32];      // X chunks
+    u32x4 a[PP][BK / 32];      // per panel: dense: BK/32 chunks; 2:4: BK/64 chunks
+    uint32_t m[PP][BK / 64];   // per panel: 2:4 metadata words, one per slice
+    u32x4 x[BK / 32];          // X chunks, shared by the PP panels
 };
 
-template <typename T, int BK, bool HYB, int SP>
-__device__ __forceinline__ uint32_t load_tile(TileRegs<BK>& R, const GemmArgs& a, int64_t t0, int tk,
+// Loads of tile column tk for PP consecutive 16-row panels (rows n0 .. n0 + 16 PP - 1, all in
+// one tile row: r0 + 16 PP <= bn) and the matching X chunks.
+template <typename T, int BK, bool HYB, int SP, int PP>
+__device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArgs& a, int64_t t0, int tk,
                                               int64_t n0, int r0, int lane, const uint16_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
     const uint16_t* base;
+    int64_t rstride;
     uint32_t moff = 0;
     if (HYB) {
         const hts_tile e = a.index[t0 + tk];   // uniform: scalar load
         type = e.type;
         moff = e.meta_off;
-        base = a.values + e.val_off + (int64_t)(r0 + i) * (type == HTS_TILE_DENSE ? BK : BK / 2);
+        rstride = type == HTS_TILE_DENSE ? BK : BK / 2;
+        base = a.values + e.val_off + (int64_t)(r0 + i) * rstride;
     } else {
+        rstride = a.ldw;
         base = a.W + (n0 + i) * a.ldw + (int64_t)tk * BK;
     }
     if (type == HTS_TILE_DENSE) {
 #pragma unroll
-        for (int u = 0; u < BK / 32; ++u) R.a[u] = ld16(base + koff<SP>(u, g));
+        for (int q = 0; q < PP; ++q)
+#pragma unroll
+            for (int u = 0; u < BK / 32; ++u) R.a[q][u] = ld16(base + 16 * q * rstride + koff<SP>(u, g));
     } else {
         const uint32_t* mrow = a.meta + moff + (int64_t)(r0 + i) * (BK / 32);
 #pragma unroll
-        for (int s = 0; s < BK / 64; ++s) R.a[s] = ld16(base + 32 * s + 8 * g);
+        for (int q = 0; q < PP; ++q)
 #pragma unroll
-        for (int s = 0; s < BK / 64; ++s) R.m[s] = mrow[2 * s + (g >> 1)];
+            for (int s = 0; s < BK / 64; ++s) R.a[q][s] = ld16(base + 16 * q * rstride + 32 * s + 8 * g);
+#pragma unroll
+        for (int q = 0; q < PP; ++q)
+#pragma unroll
+            for (int s = 0; s < BK / 64; ++s) R.m[q][s] = mrow[16 * q * (BK / 32) + 2 * s + (g >> 1)];
     }
 #pragma unroll
     for (int u = 0; u < BK / 32; ++u) R.x[u] = ld16(xrow + (int64_t)tk * BK + koff<SP>(u, g));
     return type;
 }
 
-template <typename T, int BK, int SP>
-__device__ __forceinline__ f32x4 mma_tile(const TileRegs<BK>& R, uint32_t type, f32x4 acc, int lane) {
+template <typename T, int BK, int SP, int PP>
+__device__ __forceinline__ void mma_tile(const TileRegs<BK, PP>& R, uint32_t type, f32x4 (&acc)[PP], int lane) {
     const int g = lane >> 4;
     if (type == HTS_TILE_DENSE) {
 #pragma unroll
-        for (int u = 0; u < BK / 32; ++u) acc = mfma_dense<T>(R.a[u], R.x[u], acc);
+        for (int q = 0; q < PP; ++q)
+#pragma unroll
+            for (int u = 0; u < BK / 32; ++u) acc[q] = mfma_dense<T>(R.a[q][u], R.x[u], acc[q]);
     } else {
 #pragma unroll
-        for (int s = 0; s < BK / 64; ++s) {
-            const uint32_t code = R.m[s] >> (16 * (g & 1));
-            if (SP == SPARSE_SMFMAC) {
-                acc = mfma_sparse<T, 0>(R.a[s], cat8(R.x[2 * s], R.x[2 * s + 1]), code, acc);
-            } else {
-                const u32x4 v = R.a[s];
-                acc = mfma_dense<T>(expand_two_groups(uint2{v[0], v[1]}, code & 0xFFu), R.x[2 * s], acc);
-                acc = mfma_dense<T>(expand_two_groups(uint2{v[2], v[3]}, (code >> 8) & 0xFFu),
-                                    R.x[2 * s + 1], acc);
+        for (int q = 0; q < PP; ++q)
+#pragma unroll
+            for (int s = 0; s < BK / 64; ++s) {
+                const uint32_t code = R.m[q][s] >> (16 * (g & 1));
+                if (SP == SPARSE_SMFMAC) {
+                    acc[q] = mfma_sparse<T, 0>(R.a[q][s], cat8(R.x[2 * s], R.x[2 * s + 1]), code, acc[q]);
+                } else {
+                    const u32x4 v = R.a[q][s];
+                    acc[q] = mfma_dense<T>(expand_two_groups(uint2{v[0], v[1]}, code & 0xFFu), R.x[2 * s], acc[q]);
+                    acc[q] = mfma_dense<T>(expand_two_groups(uint2{v[2], v[3]}, (code >> 8) & 0xFFu),
+                                           R.x[2 * s + 1], acc[q]);
+                }
             }
-        }
     }
-    return acc;
 }
 
-template <typename T, int BK, bool HYB, int SP, int KS, int NT>
+template <typename T, int BK, bool HYB, int SP, int KS, int NT, int PP>
 __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // XCD x (= blockIdx % 8) takes panels [x*q + min(x, r), ...) in order
+    // XCD x (= blockIdx % 8) takes blocks of PP panels [x*q + min(x, r), ...) in order
     const uint32_t P = gridDim.x, b = blockIdx.x, x = b & 7u, q = P >> 3, r = P & 7u;
-    const int64_t n0 = (int64_t)(x * q + (x < r ? x : r) + (b >> 3)) * 16;
+    const int64_t n0 = (int64_t)(x * q + (x < r ? x : r) + (b >> 3)) * 16 * PP;
     const int64_t tn = n0 / a.bn;
     const int r0 = (int)(n0 - tn * a.bn);
     const int Tk = (int)(a.K / BK);
@@ -105,72 +119,81 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
     const int i = lane & 15;
     const int64_t j = i < a.M ? i : a.M - 1;
     const uint16_t* xrow = a.X + j * a.ldx;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[PP];
+#pragma unroll
+    for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int t = kb; t < ke; t += NT) {
-        TileRegs<BK> R[NT];
+        TileRegs<BK, PP> R[NT];
         uint32_t type[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP>(R[s], a, t0, t + s, n0, r0, lane, xrow);
+            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP, PP>(R[s], a, t0, t + s, n0, r0, lane, xrow);
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) acc = mma_tile<T, BK, SP>(R[s], type[s], acc, lane);
+            if (t + s < ke) mma_tile<T, BK, SP, PP>(R[s], type[s], acc, lane);
     }
 
-    __shared__ f32x4 red[KS][64];
-    red[wave][lane] = acc;
+    __shared__ f32x4 red[KS][PP][64];
+#pragma unroll
+    for (int q2 = 0; q2 < PP; ++q2) red[wave][q2][lane] = acc[q2];
     __syncthreads();
-    if (threadIdx.x < 256) {
-        // output (row rr of the panel, column m of Y^T): lane m + 16*(rr/4), component rr%4
-        const int m = threadIdx.x >> 4, rr = threadIdx.x & 15;
+    for (int o = threadIdx.x; o < 256 * PP; o += 64 * KS) {
+        // output (row rr of panel q2, column m of Y^T): lane m + 16*(rr/4), component rr%4
+        const int q2 = o >> 8, m = (o >> 4) & 15, rr = o & 15;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < KS; ++w) sum += red[w][m + 16 * (rr >> 2)][rr & 3];
-        if (m < a.M) store_y1(a.Y, (int64_t)m * a.ldy + n0 + rr, a.y_dtype, sum);
+        for (int w = 0; w < KS; ++w) sum += red[w][q2][m + 16 * (rr >> 2)][rr & 3];
+        if (m < a.M) store_y1(a.Y, (int64_t)m * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
     }
 }
 
-template <typename T, int BK, bool HYB, int SP, int KS>
+template <typename T, int BK, bool HYB, int SP, int KS, int PP>
 hipError_t launch5(const GemmArgs& a, int nt, hipStream_t s) {
-    const dim3 grid((unsigned)(a.N / 16)), block(64 * KS);
+    const dim3 grid((unsigned)(a.N / (16 * PP))), block(64 * KS);
     // nt counts 128-wide tile columns; a 64-wide tile is half as many bytes.  With 16 waves
     // (at most 128 registers per lane) only the 2-column batch fits without spills.
-    if constexpr (KS < 16) {
+    if constexpr (KS < 16 && PP == 1) {
         if (nt >= 4) {
-            gemm_decode_kernel<T, BK, HYB, SP, KS, 4 * 128 / BK><<<grid, block, 0, s>>>(a);
+            gemm_decode_kernel<T, BK, HYB, SP, KS, 4 * 128 / BK, PP><<<grid, block, 0, s>>>(a);
             return hipGetLastError();
         }
     }
-    gemm_decode_kernel<T, BK, HYB, SP, KS, 2 * 128 / BK><<<grid, block, 0, s>>>(a);
+    gemm_decode_kernel<T, BK, HYB, SP, KS, 2 * 128 / BK, PP><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 
+// pp: 16-row panels per workgroup (1 or 2; 2 shares each X fragment between two panels and
+// needs 32 | N, which tiles of 64 or 128 rows give)
 template <typename T, int BK, bool HYB, int SP>
-hipError_t launch4(const GemmArgs& a, int ksplit, int nt, hipStream_t s) {
-    if (ksplit >= 16) return launch5<T, BK, HYB, SP, 16>(a, nt, s);
-    if (ksplit >= 8) return launch5<T, BK, HYB, SP, 8>(a, nt, s);
-    return launch5<T, BK, HYB, SP, 4>(a, nt, s);
+hipError_t launch4(const GemmArgs& a, int ksplit, int nt, int pp, hipStream_t s) {
+    if (pp == 2) {
+        if (ksplit >= 8) return launch5<T, BK, HYB, SP, 8, 2>(a, nt, s);
+        return launch5<T, BK, HYB, SP, 4, 2>(a, nt, s);
+    }
+    if (ksplit >= 16) return launch5<T, BK, HYB, SP, 16, 1>(a, nt, s);
+    if (ksplit >= 8) return launch5<T, BK, HYB, SP, 8, 1>(a, nt, s);
+    return launch5<T, BK, HYB, SP, 4, 1>(a, nt, s);
 }
 
 template <typename T, int BK, bool HYB>
-hipError_t launch3(const GemmArgs& a, int ksplit, int nt, int sp, hipStream_t s) {
-    return sp == SPARSE_SMFMAC ? launch4<T, BK, HYB, SPARSE_SMFMAC>(a, ksplit, nt, s)
-                               : launch4<T, BK, HYB, SPARSE_DECOMPRESS>(a, ksplit, nt, s);
+hipError_t launch3(const GemmArgs& a, int ksplit, int nt, int pp, int sp, hipStream_t s) {
+    return sp == SPARSE_SMFMAC ? launch4<T, BK, HYB, SPARSE_SMFMAC>(a, ksplit, nt, pp, s)
+                               : launch4<T, BK, HYB, SPARSE_DECOMPRESS>(a, ksplit, nt, pp, s);
 }
 
 template <typename T>
-hipError_t launch2(const GemmArgs& a, int ksplit, int nt, int sp, hipStream_t s) {
+hipError_t launch2(const GemmArgs& a, int ksplit, int nt, int pp, int sp, hipStream_t s) {
     const bool hyb = a.index != nullptr;
     if (a.bk == 128)
-        return hyb ? launch3<T, 128, true>(a, ksplit, nt, sp, s) : launch3<T, 128, false>(a, ksplit, nt, sp, s);
-    return hyb ? launch3<T, 64, true>(a, ksplit, nt, sp, s) : launch3<T, 64, false>(a, ksplit, nt, sp, s);
+        return hyb ? launch3<T, 128, true>(a, ksplit, nt, pp, sp, s) : launch3<T, 128, false>(a, ksplit, nt, pp, sp, s);
+    return hyb ? launch3<T, 64, true>(a, ksplit, nt, pp, sp, s) : launch3<T, 64, false>(a, ksplit, nt, pp, sp, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int sparse_path, hipStream_t s) {
-    return a.dtype == HTS_BF16 ? launch2<BF16T>(a, ksplit, nt, sparse_path, s)
-                               : launch2<F16T>(a, ksplit, nt, sparse_path, s);
+hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s) {
+    return a.dtype == HTS_BF16 ? launch2<BF16T>(a, ksplit, nt, pp, sparse_path, s)
+                               : launch2<F16T>(a, ksplit, nt, pp, sparse_path, s);
 }
 
 }  // namespace hts

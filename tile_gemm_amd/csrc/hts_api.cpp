@@ -82,16 +82,27 @@ int64_t decode_max_m() {
     return 16;
 }
 
-// Waves per panel of the streaming kernel (HTS_DECODE_KSPLIT=4|8|16 overrides).
+// Launch shape of the streaming kernel.  Defaults measured on MI355X (bf16, 128x128 tiles):
+//   panels per workgroup pp: 2 (each X fragment feeds two 16-row panels) when K >= 4608 --
+//     K = 5120: M=16 36.9 -> 29.4 us (13824 rows), 20.1 -> 16.4 us (5120 rows) -- else 1
+//     (K = 4096, 11008 rows: 17.2 us at pp = 1 against 20.2 at pp = 2);
+//   waves per workgroup: 4 when pp = 2 still leaves >= 400 workgroups, else 8;
+//   tile columns per batch of loads: 2.
+// HTS_DECODE_PP=1|2, HTS_DECODE_KSPLIT=4|8|16 and HTS_DECODE_NT=2|4 override.
+int decode_pp(const hts::GemmArgs& a) {
+    if (a.N % 32) return 1;                  // every accepted shape has 32 | N; kept as a guard
+    const char* v = getenv("HTS_DECODE_PP");
+    if (v && !strcmp(v, "2")) return 2;
+    if (v && !strcmp(v, "1")) return 1;
+    return a.K >= 4608 ? 2 : 1;
+}
+
 int decode_ksplit(const hts::GemmArgs& a) {
     const char* v = getenv("HTS_DECODE_KSPLIT");
     if (v && (!strcmp(v, "4") || !strcmp(v, "8") || !strcmp(v, "16"))) return atoi(v);
-    (void)a;
-    return 8;
+    return (decode_pp(a) == 2 && a.N / 32 >= 400) ? 4 : 8;
 }
 
-// Tile columns (128 wide) whose loads a wave of the streaming kernel issues together
-// (HTS_DECODE_NT=2|4 overrides).
 int decode_nt(const hts::GemmArgs& a) {
     const char* v = getenv("HTS_DECODE_NT");
     if (v && (!strcmp(v, "2") || !strcmp(v, "4"))) return atoi(v);
@@ -115,7 +126,7 @@ int prefill_tile(const hts::GemmArgs& a) {
 hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
     hipError_t e;
     if (a.M <= decode_max_m()) {
-        e = hts::launch_gemm_decode(a, decode_ksplit(a), decode_nt(a), sparse_path(), s);
+        e = hts::launch_gemm_decode(a, decode_ksplit(a), decode_nt(a), decode_pp(a), sparse_path(), s);
     } else {
         const int tile = prefill_tile(a);
         if (a.index && a.K / a.bk > hts::kMaxTileColsPerRow)

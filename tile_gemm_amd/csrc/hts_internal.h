@@ -32,8 +32,9 @@ hipError_t launch_pack(const hts_desc& d, const hts_tile* index, const uint16_t*
                        const float* col_scale, uint16_t* values, uint32_t* meta, hipStream_t s);
 hipError_t launch_unpack(const hts_desc& d, const hts_tile* index, const uint16_t* values,
                          const uint32_t* meta, uint16_t* W_out, int64_t ldw, hipStream_t s);
-// ksplit: waves per 16-row panel (4, 8 or 16); nt: 128-wide tile columns per batch of loads (2 or 4)
-hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int sparse_path, hipStream_t s);
+// ksplit: waves per workgroup (4, 8 or 16); nt: 128-wide tile columns per batch of loads (2 or 4);
+// pp: 16-row panels per workgroup (1 or 2; 2 requires N % 32 == 0)
+hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s);
 // Tiled kernel: one tile row per workgroup; tile 0 = 256 X rows per workgroup, 1 = 128.
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, int tile, hipStream_t s);
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the

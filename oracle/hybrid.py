@@ -178,13 +178,18 @@ def plan(tile_map: np.ndarray, N: int, K: int, bn: int, bk: int):
 
 
 def pack(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int, bk: int,
-         col_scale: np.ndarray | None = None):
-    """(values uint16, meta uint32, index uint32[T,4]) of W under the tile map."""
+         col_scale: np.ndarray | None = None, scores: np.ndarray | None = None):
+    """(values uint16, meta uint32, index uint32[T,4]) of W under the tile map.
+
+    scores: float32 [N,K] selection scores to use instead of the magnitude / Wanda scores
+    (see pack_masked)."""
     N, K = W_bits.shape
     index, sizes = plan(tile_map, N, K, bn, bk)
     tmap = index[:, 2]
     tiles = as_tiles(np.asarray(W_bits, dtype=np.uint16), bn, bk)
-    stiles = as_tiles(selection_scores(W_bits, dtype, col_scale), bn, bk)
+    if scores is None:
+        scores = selection_scores(W_bits, dtype, col_scale)
+    stiles = as_tiles(np.asarray(scores, dtype=np.float32), bn, bk)
     values = []
     meta = []
     G = bk // 4
@@ -206,6 +211,54 @@ def pack(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int, bk: int,
     met = np.concatenate(meta).astype(np.uint32) if meta else np.zeros(0, np.uint32)
     assert vals.size == sizes["values"] and met.size == sizes["meta"]
     return vals, met, index
+
+
+# ----------------------------------------------------------------------------
+# Packing from a given element mask
+# ----------------------------------------------------------------------------
+# PATCH page, section 2 ("variants"): in the PATCH-Tile variant the 2:4 patterns are
+# not learned but frozen from a one-shot pruning method, and only the tile choices
+# are learned.  The 2:4 selection is then an input: an element mask that keeps two
+# of every four weights of each group (along K, aligned as above) in the 2:4 tiles.
+# Reading taken for malformed input: the mask is the selection score (1 = marked),
+# so a group marking exactly two weights keeps exactly those two; a group marking
+# some other number keeps the two the rank rule picks (marked before unmarked, lower
+# index first among equals) and is counted as malformed.
+
+def mask_scores(mask: np.ndarray) -> np.ndarray:
+    """float32 selection score of every weight from a keep mask: 1 where marked, else 0."""
+    return (np.asarray(mask) != 0).astype(np.float32)
+
+
+def malformed_groups(mask: np.ndarray, tile_map: np.ndarray, bn: int, bk: int) -> int:
+    """Number of groups of four in the 2:4 tiles whose mask does not mark exactly two weights."""
+    N, K = mask.shape
+    check_grid(N, K, bn, bk)
+    tmap = np.asarray(tile_map, dtype=np.uint8).ravel()
+    m = as_tiles((np.asarray(mask) != 0).astype(np.uint8), bn, bk)[tmap == TILE_SPARSE24]
+    counts = m.reshape(m.shape[0], bn, bk // 4, 4).sum(axis=-1)
+    return int(np.count_nonzero(counts != 2))
+
+
+def pack_masked(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, mask: np.ndarray, bn: int, bk: int):
+    """(values, meta, index, malformed) of W packed with the 2:4 pairs the mask marks."""
+    vals, met, index = pack(W_bits, dtype, tile_map, bn, bk, scores=mask_scores(mask))
+    return vals, met, index, malformed_groups(mask, tile_map, bn, bk)
+
+
+def masked_weights_from_mask(W_bits: np.ndarray, tile_map: np.ndarray, mask: np.ndarray, bn: int,
+                             bk: int) -> np.ndarray:
+    """The weight a masked pack stores: dense tiles unchanged; in 2:4 tiles the weights the
+    selection drops become +0.0 (for a well-formed mask: exactly the unmarked ones)."""
+    N, K = W_bits.shape
+    check_grid(N, K, bn, bk)
+    tmap = np.asarray(tile_map, dtype=np.uint8).ravel()
+    tiles = as_tiles(np.asarray(W_bits, dtype=np.uint16), bn, bk)
+    stiles = as_tiles(mask_scores(mask), bn, bk)
+    for t in np.nonzero(tmap == TILE_SPARSE24)[0]:
+        keep = sparse_tile_keep(stiles[t])
+        tiles[t][~keep] = 0
+    return from_tiles(tiles, N, K)
 
 
 def unpack(values: np.ndarray, meta: np.ndarray, index: np.ndarray, N: int, K: int,

@@ -379,3 +379,105 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert not golden_ok()
     monkeypatch.setattr(oracle.hybrid, "selection_scores", real_scores)
     assert golden_ok()
+
+
+# ---------------------------------------------------------------------------
+# packing from a given element mask
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_golden_pack_from_mask(dtype):
+    gold = json.load(open(os.path.join(GOLD, "pack_masked_2x64.json")))
+    N, K, bn, bk = gold["N"], gold["K"], gold["bn"], gold["bk"]
+    W = _bits([[c + 1 for c in range(K)], [-(c + 1) for c in range(K)]], dtype)
+    mask = np.zeros((N, K), np.uint8)
+    mask[:, 32:] = np.arange(32) % 3 == 0          # ignored: the tile is dense
+    for r, key in enumerate(("mask_pairs_row0", "mask_pairs_row1")):
+        for g, (i0, i1) in enumerate(gold[key]):
+            mask[r, 4 * g + i0] = mask[r, 4 * g + i1] = 1
+    tmap = np.array(gold["tile_map"], np.uint8)
+    vals, meta, index, bad = oracle.pack_masked(W, dtype, tmap, mask, bn, bk)
+    assert bad == 0
+    assert [f"{int(w):08X}" for w in meta] == gold["meta_hex"]
+    assert np.array_equal(vals[:32], _bits(gold["values_tile0"], dtype))
+    assert np.array_equal(vals[32:], W[:, 32:].ravel())
+
+
+def _random_pair_mask(N, K, g):
+    mask = np.zeros((N, K // 4, 4), np.uint8)
+    pick = g.integers(0, 6, size=(N, K // 4))
+    for n in range(6):
+        i0, i1 = PAIRS[n]
+        sel = pick == n
+        mask[sel, i0] = 1
+        mask[sel, i1] = 1
+    return mask.reshape(N, K)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_pack_from_well_formed_mask_brute_force(dtype):
+    g = np.random.default_rng(41)
+    N, K, bn, bk = 8, 128, 4, 32
+    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    mask = _random_pair_mask(N, K, g)
+    tmap = (g.random((N // bn) * (K // bk)) < 0.5).astype(np.uint8)
+    vals, meta, index, bad = oracle.pack_masked(W, dtype, tmap, mask, bn, bk)
+    assert bad == 0
+    back = oracle.unpack(vals, meta, index, N, K, bn, bk)
+    Tk = K // bk
+    for n in range(N):
+        for k in range(K):
+            sparse = tmap[(n // bn) * Tk + k // bk] == 1
+            want = W[n, k] if (not sparse or mask[n, k]) else 0
+            assert back[n, k] == want
+    # codes name the marked positions (found here group by group with np.nonzero)
+    for t in np.nonzero(tmap)[0]:
+        vo, mo, _, _ = index[t]
+        tn, tk = divmod(int(t), Tk)
+        for r in range(bn):
+            for gi in range(bk // 4):
+                pos = np.nonzero(mask[tn * bn + r, tk * bk + 4 * gi: tk * bk + 4 * gi + 4])[0]
+                word = int(meta[mo + r * (bk // 32) + gi // 8])
+                assert (word >> (4 * (gi % 8))) & 0xF == int(pos[0]) | (int(pos[1]) << 2)
+
+
+def test_pack_from_malformed_mask_brute_force():
+    g = np.random.default_rng(43)
+    N, K, bn, bk = 4, 64, 4, 32
+    W = wl.gaussian_bits((N, K), 0.02, "bf16", g)
+    mask = (g.random((N, K)) < 0.5).astype(np.uint8)       # any number marked per group
+    tmap = np.array([1, 1], np.uint8)
+    vals, meta, index, bad = oracle.pack_masked(W, "bf16", tmap, mask, bn, bk)
+    groups = mask.reshape(N, K // 4, 4)
+    assert bad == int(np.count_nonzero(groups.sum(axis=-1) != 2))
+    back = oracle.unpack(vals, meta, index, N, K, bn, bk).reshape(N, K // 4, 4)
+    for n in range(N):
+        for gi in range(K // 4):
+            order = [i for i in range(4) if groups[n, gi, i]] + [i for i in range(4) if not groups[n, gi, i]]
+            kept = sorted(order[:2])              # marked first, lower index first among equals
+            want = np.zeros(4, np.uint16)
+            want[kept] = W[n, 4 * gi + np.array(kept)]
+            assert np.array_equal(back[n, gi], want)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_pack_from_magnitude_mask_equals_magnitude_pack(dtype):
+    # the keep mask of a magnitude pack (read back from its codes), given as the mask, packs the same
+    g = np.random.default_rng(47)
+    N, K, bn, bk = 64, 256, 32, 64
+    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    tmap = (g.random((N // bn) * (K // bk)) < 0.5).astype(np.uint8)
+    _, m, idx = oracle.pack(W, dtype, np.ones_like(tmap), bn, bk)   # magnitude 2:4 in every tile
+    mask = np.zeros((N, K), np.uint8)
+    for t in range(idx.shape[0]):
+        tn, tk = divmod(t, K // bk)
+        words = m[idx[t, 1]: idx[t, 1] + bn * bk // 32].reshape(bn, bk // 32)
+        for r in range(bn):
+            for gi in range(bk // 4):
+                code = (int(words[r, gi // 8]) >> (4 * (gi % 8))) & 0xF
+                mask[tn * bn + r, tk * bk + 4 * gi + (code & 3)] = 1
+                mask[tn * bn + r, tk * bk + 4 * gi + (code >> 2)] = 1
+    a = oracle.pack(W, dtype, tmap, bn, bk)
+    b = oracle.pack_masked(W, dtype, tmap, mask, bn, bk)
+    assert b[3] == 0
+    assert all(np.array_equal(x, y) for x, y in zip(a, b[:3]))

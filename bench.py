@@ -237,6 +237,13 @@ def main():
                                                       pws[i % n_rot].values, pws[i % n_rot].meta, Wout),
                              5 if args.quick else 20)
     pack_bytes = dense_bytes + packed_bytes
+    # packing from a given element mask (frozen 2:4 patterns): reads W, the mask inside the 2:4
+    # tiles and writes the packed weight
+    mask = torch.from_numpy(wl.layer_pair_mask(cfg, L)).to(dev)
+    bad = torch.empty(1, dtype=torch.int32, device=dev)
+    t_pack_masked = time_launches(lambda i: hts.hts_pack_masked(pw0.desc, pw0.index, Ws[i % n_rot_d], mask, vals_tmp,
+                                                                meta_tmp, bad), 5 if args.quick else 20)
+    pack_masked_bytes = dense_bytes + n_sparse * L.bn * L.bk + packed_bytes
 
     if args.calibrate_copy:
         # three plain copies of 256 MiB each (distinct buffers, larger than the Infinity Cache in total)
@@ -310,6 +317,8 @@ def main():
         "pack": {"us": round(t_pack * 1e6, 2), "GB/s": round(pack_bytes / t_pack / 1e9, 1),
                  "frac_hbm": round(pack_bytes / t_pack / 1e9 / HBM_PEAK_GBS, 4)},
         "unpack": {"us": round(t_unpack * 1e6, 2), "GB/s": round(pack_bytes / t_unpack / 1e9, 1)},
+        "pack_masked": {"us": round(t_pack_masked * 1e6, 2), "GB/s": round(pack_masked_bytes / t_pack_masked / 1e9, 1),
+                        "frac_hbm": round(pack_masked_bytes / t_pack_masked / 1e9 / HBM_PEAK_GBS, 4)},
         "packed_bytes": packed_bytes,
         "rotation_copies": n_rot,
         "wall_s_timed_region": round(wall, 4),

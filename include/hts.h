@@ -121,6 +121,22 @@ hts_status hts_pack_plan(const hts_desc* d, const uint8_t* tile_map_host,
 hts_status hts_pack(const hts_desc* d, const hts_tile* index, const void* W, int64_t ldw,
                     const float* col_scale, void* values, uint32_t* meta, void* stream);
 
+/* Device, asynchronous.  hts_pack with the 2:4 selection given as an element mask instead
+ * of selected by score: the PATCH-Tile variant keeps 2:4 patterns frozen from a one-shot
+ * pruning method and learns only the tile choices (page "PATCH: Learnable Tile-level Hybrid
+ * Sparsity for LLMs", section 2, variants).
+ *   mask : device uint8 [N, ldm] row-major, nonzero = keep; read only inside 2:4 tiles, where
+ *          each group of four (along K, aligned at the tile start) should mark exactly two
+ *          weights.  16-byte aligned, ldm >= K and a multiple of 16.
+ *   malformed_groups : device uint32 or NULL.  Set to the number of groups in 2:4 tiles that
+ *          do not mark exactly two weights (written when the stream reaches the call).  Such a
+ *          group keeps the two weights the rank rule picks with the mask as score: marked
+ *          before unmarked, the lower index first among equals.
+ * Other arguments, buffers and the packed format as for hts_pack. */
+hts_status hts_pack_masked(const hts_desc* d, const hts_tile* index, const void* W, int64_t ldw,
+                           const uint8_t* mask, int64_t ldm, void* values, uint32_t* meta,
+                           uint32_t* malformed_groups, void* stream);
+
 /* Device, asynchronous.  Inverse of hts_pack: writes mask(W) into W_out[N,K]
  * (ldw), +0.0 at the dropped positions of 2:4 tiles. */
 hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* values,

@@ -138,3 +138,16 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.hts_wanda_map(10, A8 + 4, 3, A16, None) == 4
     n = ctypes.c_size_t(123)
     assert L.hts_gemm_workspace(by(d), 16, by(n)) == 0 and n.value == 0
+
+
+def test_pack_masked_rejects_bad_arguments():
+    L = hts.lib()
+    by = ctypes.byref
+    d = hts.make_desc(256, 256, 64, 64, "bf16")
+    assert L.hts_pack_masked(by(d), A16, A16, 256, None, 256, A16, A16, None, None) == 1     # no mask
+    assert L.hts_pack_masked(by(d), A16, A16, 256, A8, 256, A16, A16, None, None) == 4       # mask alignment
+    assert L.hts_pack_masked(by(d), A16, A16, 256, A16, 200, A16, A16, None, None) == 3      # ldm < K
+    assert L.hts_pack_masked(by(d), A16, A16, 256, A16, 264, A16, A16, None, None) == 4      # ldm % 16
+    assert L.hts_pack_masked(by(d), A16, A16, 256, A16, 256, A16, A16, A8 + 2, None) == 4    # counter alignment
+    bad = hts.make_desc(256, 200, 64, 64, "bf16")
+    assert L.hts_pack_masked(by(bad), A16, A16, 256, A16, 256, A16, A16, None, None) == 3    # K % bk

@@ -183,3 +183,23 @@ def test_tile_rows_of_many_tile_columns(Tk, kind):
     Y = hts.gemm(hts.tensor_from_bits(X, "bf16", DEV), pw, out_dtype=torch.float32)
     torch.cuda.synchronize()
     _check(Y.cpu().numpy(), Y_ref, f"Tk={Tk} {kind}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_gemm_over_mask_packed_weight(M, sparse_path):
+    # a weight packed from frozen 2:4 patterns feeds the same product
+    c = wl.config("13b")
+    L = c.layers[0]
+    W = weight(c.cfg_id, L.name)
+    tmap = oracle_map(c.cfg_id, L.name)
+    mask = wl.layer_pair_mask(c, L)
+    say(f"[gemm-masked] {c.name}/{L.name} M={M} path={sparse_path}")
+    pw, malformed = hts.pack_masked(hts.tensor_from_bits(W, L.dtype, DEV), tmap, torch.from_numpy(mask).to(DEV),
+                                    L.bn, L.bk)
+    X = activations(c.cfg_id, L.name)[:M]
+    rows = sample_rows(M)
+    Y_ref = oracle.gemm_ref(X[rows], oracle.masked_weights_from_mask(W, tmap, mask, L.bn, L.bk), L.dtype)
+    Y = hts.gemm(hts.tensor_from_bits(np.ascontiguousarray(X), L.dtype, DEV), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(malformed.item()) == 0
+    _check(Y.cpu().numpy()[rows], Y_ref, f"masked M={M}")

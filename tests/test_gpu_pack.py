@@ -130,3 +130,72 @@ def test_wanda_map_ties_and_extremes():
         hts.hts_wanda_map(ct, n_s, m)
         torch.cuda.synchronize()
         assert np.array_equal(m.cpu().numpy(), oracle.wanda_tile_map(cost, n_s))
+
+
+# ---------------------------------------------------------------------------
+# packing from a given element mask (frozen 2:4 patterns)
+# ---------------------------------------------------------------------------
+
+def _check_masked(W, dtype, tmap, mask_np, bn, bk, ldm_pad=0):
+    N, K = W.shape
+    vals, meta, idx, bad = oracle.pack_masked(W, dtype, tmap, mask_np, bn, bk)
+    Wt = hts.tensor_from_bits(W, dtype, DEV)
+    big = torch.zeros((N, K + ldm_pad), dtype=torch.uint8, device=DEV)
+    big[:, :K] = torch.from_numpy(np.ascontiguousarray(mask_np)).to(DEV)
+    pw, malformed = hts.pack_masked(Wt, tmap, big[:, :K], bn, bk)
+    torch.cuda.synchronize()
+    _check_packed(pw, vals, meta, idx)
+    assert int(malformed.item()) == bad
+    back = hts.bits_from_tensor(hts.unpack(pw))
+    assert np.array_equal(back, oracle.masked_weights_from_mask(W, tmap, mask_np, bn, bk))
+    return pw
+
+
+@pytest.mark.parametrize("name", ["tiny/tiny", "7b_up/up_proj", "13b/sq_5120", "sweep/sweep_p0.5"])
+def test_pack_masked_named_layers(name):
+    cname, lname = name.split("/")
+    c = wl.config(cname)
+    L = next(l for l in c.layers if l.name == lname)
+    say(f"[pack-masked] {cname}/{lname}")
+    W = weight(c.cfg_id, L.name)
+    _check_masked(W, L.dtype, oracle_map(c.cfg_id, L.name), wl.layer_pair_mask(c, L), L.bn, L.bk)
+
+
+@pytest.mark.parametrize("dtype,tile", [("bf16", (128, 128)), ("f16", (64, 64)), ("bf16", (128, 64))])
+def test_pack_masked_malformed_and_strided(dtype, tile):
+    bn, bk = tile
+    N, K = 2 * bn, 4 * bk
+    g = np.random.default_rng(zlib.crc32(f"{dtype}{tile}".encode()))
+    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    tmap = (g.random((N // bn) * (K // bk)) < 0.6).astype(np.uint8)
+    say(f"[pack-masked] malformed {dtype} tile={tile}")
+    mask = (g.random((N, K)) < 0.5).astype(np.uint8) * g.integers(1, 255, size=(N, K)).astype(np.uint8)
+    _check_masked(W, dtype, tmap, mask, bn, bk, ldm_pad=48)
+    _check_masked(W, dtype, tmap, wl.pair_mask(N, K, g), bn, bk, ldm_pad=16)
+
+
+def test_pack_masked_with_magnitude_mask_equals_pack():
+    c = wl.config("7b_up")
+    L = c.layers[0]
+    W = weight(c.cfg_id, L.name)
+    tmap = oracle_map(c.cfg_id, L.name)
+    pw = _gpu_pack(W, L.dtype, tmap, L.bn, L.bk)
+    Wall = oracle.masked_weights(W, L.dtype, np.ones_like(tmap), L.bn, L.bk)
+    mask = np.zeros(W.shape, np.uint8)
+    # the magnitude keep pattern, from a pack with every tile 2:4 (zero weights resolved by the codes)
+    pall = _gpu_pack(W, L.dtype, np.ones_like(tmap), L.bn, L.bk)
+    words = pall.meta.cpu().numpy().view(np.uint32)
+    Tk = L.K // L.bk
+    codes = words.reshape(L.N // L.bn, Tk, L.bn, L.bk // 32)           # tiles in order, rows, words
+    nib = (codes[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF
+    nib = nib.reshape(L.N // L.bn, Tk, L.bn, L.bk // 4).transpose(0, 2, 1, 3).reshape(L.N, L.K // 4)
+    rows = np.arange(L.N)[:, None]
+    gbase = 4 * np.arange(L.K // 4)[None, :]
+    mask[rows, gbase + (nib & 3)] = 1
+    mask[rows, gbase + (nib >> 2)] = 1
+    assert np.array_equal(np.where(mask == 1, W, 0), Wall)
+    Wt = hts.tensor_from_bits(W, L.dtype, DEV)
+    pm, malformed = hts.pack_masked(Wt, tmap, torch.from_numpy(mask).to(DEV), L.bn, L.bk)
+    torch.cuda.synchronize()
+    assert int(malformed.item()) == 0
+    assert torch.equal(pm.values, pw.values) and torch.equal(pm.meta, pw.meta)

@@ -55,6 +55,7 @@ _SIGS = {
     "hts_last_error": (ctypes.c_char_p, []),
     "hts_pack_plan": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, ctypes.POINTER(hts_sizes)]),
     "hts_pack": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _I64, _VP, _VP, _VP, _VP]),
+    "hts_pack_masked": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _I64, _VP, _I64, _VP, _VP, _VP, _VP]),
     "hts_unpack": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _VP, _VP, _I64, _VP]),
     "hts_gemm_workspace": (ctypes.c_int, [ctypes.POINTER(hts_desc), _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "hts_gemm": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _I32,
@@ -150,6 +151,13 @@ def hts_pack(desc, index, W, col_scale, values, meta, ldw=None, stream=None) -> 
                           _ptr(col_scale), _ptr(values), _ptr(meta), _stream(stream)))
 
 
+def hts_pack_masked(desc, index, W, mask, values, meta, malformed=None, ldw=None, ldm=None,
+                    stream=None) -> None:
+    _check(lib().hts_pack_masked(ctypes.byref(desc), _ptr(index), _ptr(W), W.stride(0) if ldw is None else ldw,
+                                 _ptr(mask), mask.stride(0) if ldm is None else ldm, _ptr(values), _ptr(meta),
+                                 _ptr(malformed), _stream(stream)))
+
+
 def hts_unpack(desc, index, values, meta, W_out, ldw=None, stream=None) -> None:
     _check(lib().hts_unpack(ctypes.byref(desc), _ptr(index), _ptr(values), _ptr(meta), _ptr(W_out),
                             W_out.stride(0) if ldw is None else ldw, _stream(stream)))
@@ -237,6 +245,23 @@ def pack(W: torch.Tensor, tile_map: np.ndarray, bn: int, bk: int,
     index, values, meta, sizes = _device_buffers(desc, tile_map, W.device)
     hts_pack(desc, index, W, col_scale, values, meta, stream=stream)
     return PackedWeight(desc, index, values, meta, sizes, np.asarray(tile_map, dtype=np.uint8).ravel().copy())
+
+
+def pack_masked(W: torch.Tensor, tile_map: np.ndarray, mask: torch.Tensor, bn: int, bk: int,
+                stream=None):
+    """Pack W with the 2:4 pairs a device uint8 keep mask [N,K] marks (nonzero = keep).
+
+    Returns (PackedWeight, malformed) where malformed is a device uint32 tensor holding the number
+    of groups in 2:4 tiles that do not mark exactly two weights."""
+    N, K = W.shape
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (N, K):
+        raise HTSError(1, "mask must be a uint8 tensor of the shape of W")
+    desc = make_desc(N, K, bn, bk, W.dtype)
+    index, values, meta, sizes = _device_buffers(desc, tile_map, W.device)
+    malformed = torch.empty(1, dtype=torch.int32, device=W.device)
+    hts_pack_masked(desc, index, W, mask, values, meta, malformed, stream=stream)
+    return (PackedWeight(desc, index, values, meta, sizes, np.asarray(tile_map, dtype=np.uint8).ravel().copy()),
+            malformed)
 
 
 def unpack(pw: PackedWeight, stream=None) -> torch.Tensor:

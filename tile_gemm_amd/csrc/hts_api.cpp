@@ -209,6 +209,25 @@ hts_status hts_pack(const hts_desc* d, const hts_tile* index, const void* W, int
                       "pack kernel launch");
 }
 
+hts_status hts_pack_masked(const hts_desc* d, const hts_tile* index, const void* W, int64_t ldw,
+                           const uint8_t* mask, int64_t ldm, void* values, uint32_t* meta,
+                           uint32_t* malformed_groups, void* stream) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if ((st = check_ptr(index, "index")) || (st = check_ptr(W, "W")) || (st = check_ptr(values, "values")) ||
+        (st = check_ptr(mask, "mask")))
+        return st;
+    if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
+    if (malformed_groups && (reinterpret_cast<uintptr_t>(malformed_groups) & 3u))
+        return fail(HTS_ERR_ALIGN, "malformed_groups is not 4-byte aligned");
+    if ((st = check_ld(ldw, d->K, 8, "ldw"))) return st;
+    if ((st = check_ld(ldm, d->K, 16, "ldm"))) return st;
+    return hip_status(hts::launch_pack_masked(*d, index, static_cast<const uint16_t*>(W), ldw, mask, ldm,
+                                              malformed_groups, static_cast<uint16_t*>(values), meta,
+                                              static_cast<hipStream_t>(stream)),
+                      "masked pack kernel launch");
+}
+
 hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta,
                       void* W_out, int64_t ldw, void* stream) {
     hts_status st = check_desc(d);

@@ -30,6 +30,10 @@ enum SparsePath { SPARSE_SMFMAC = 0, SPARSE_DECOMPRESS = 1 };
 
 hipError_t launch_pack(const hts_desc& d, const hts_tile* index, const uint16_t* W, int64_t ldw,
                        const float* col_scale, uint16_t* values, uint32_t* meta, hipStream_t s);
+// mask: uint8 [N, ldm], nonzero = keep (read in 2:4 tiles only); malformed: counter or nullptr
+hipError_t launch_pack_masked(const hts_desc& d, const hts_tile* index, const uint16_t* W, int64_t ldw,
+                              const uint8_t* mask, int64_t ldm, uint32_t* malformed, uint16_t* values,
+                              uint32_t* meta, hipStream_t s);
 hipError_t launch_unpack(const hts_desc& d, const hts_tile* index, const uint16_t* values,
                          const uint32_t* meta, uint16_t* W_out, int64_t ldw, hipStream_t s);
 // ksplit: waves per workgroup (4, 8 or 16); nt: 128-wide tile columns per batch of loads (2 or 4);

@@ -40,12 +40,18 @@ __device__ __forceinline__ void pick_two(const float s[4], uint32_t& i0, uint32_
     i1 = keep[3] ? 3u : (keep[2] ? 2u : 1u);
 }
 
-template <typename T>
+// MASKED: the 2:4 pairs come from an element mask (PATCH page, section 2, variants: the
+// PATCH-Tile variant freezes 2:4 patterns from a one-shot method): the score of a weight is 1
+// where the mask byte is nonzero, else 0, under the same rank rule, so a group marking exactly
+// two weights keeps those two.  Groups marking another number are counted into *malformed.
+template <typename T, bool MASKED>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     const hts_tile* __restrict__ index, int64_t Tk, int bn, int bk,
     const uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ cs,
+    const uint8_t* __restrict__ mask, int64_t ldm, uint32_t* __restrict__ malformed,
     uint16_t* __restrict__ values, uint32_t* __restrict__ meta) {
     const int64_t t = blockIdx.x;
+    uint32_t bad = 0;
     const hts_tile e = index[t];
     const int64_t tn = t / Tk, tk = t % Tk;
     const int wpr = bk / 32;                       // 32-weight chunks per tile row
@@ -65,14 +71,32 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
         }
         uint32_t kept[8];   // 16 kept 16-bit values, two per word
         uint32_t word = 0;
+        u32x4 mk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};   // 32 mask bytes of the chunk
+        if (MASKED) {
+            const uint8_t* msrc = mask + (tn * bn + r) * ldm + k0;
+            mk[0] = *reinterpret_cast<const u32x4*>(msrc);
+            mk[1] = *reinterpret_cast<const u32x4*>(msrc + 16);
+        }
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             // group g = weights 4g..4g+3 of this chunk = dwords 2g, 2g+1
             const uint32_t d0 = q[g / 2][(2 * g) % 4], d1 = q[g / 2][(2 * g + 1) % 4];
             const uint32_t b[4] = {d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16};
             float s[4];
+            if (MASKED) {
+                const uint32_t mw = mk[g / 4][g % 4];            // mask bytes of weights 4g..4g+3
+                int marked = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] = score<T>(b[i], cs, k0 + 4 * g + i);
+                for (int i = 0; i < 4; ++i) {
+                    const bool on = ((mw >> (8 * i)) & 0xFFu) != 0u;
+                    s[i] = on ? 1.0f : 0.0f;
+                    marked += on;
+                }
+                bad += marked != 2;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] = score<T>(b[i], cs, k0 + 4 * g + i);
+            }
             uint32_t i0, i1;
             pick_two(s, i0, i1);
             uint32_t v0 = b[0], v1 = b[1];
@@ -90,7 +114,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
         st16(dst + 8, o1);
         meta[e.meta_off + (int64_t)r * wpr + w] = word;
     }
+    if (MASKED && malformed && bad) atomicAdd(malformed, bad);
 }
+
+__global__ void zero_counter(uint32_t* c) { *c = 0u; }
 
 __global__ __launch_bounds__(kPackThreads) void unpack_kernel(
     const hts_tile* __restrict__ index, int64_t Tk, int bn, int bk,
@@ -128,11 +155,25 @@ hipError_t launch_pack(const hts_desc& d, const hts_tile* index, const uint16_t*
                        const float* col_scale, uint16_t* values, uint32_t* meta, hipStream_t s) {
     const int64_t Tk = d.K / d.bk, T = (d.N / d.bn) * Tk;
     if (d.dtype == HTS_BF16)
-        pack_kernel<BF16T><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(index, Tk, d.bn, d.bk, W, ldw,
-                                                                           col_scale, values, meta);
+        pack_kernel<BF16T, false><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
+            index, Tk, d.bn, d.bk, W, ldw, col_scale, nullptr, 0, nullptr, values, meta);
     else
-        pack_kernel<F16T><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(index, Tk, d.bn, d.bk, W, ldw,
-                                                                          col_scale, values, meta);
+        pack_kernel<F16T, false><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
+            index, Tk, d.bn, d.bk, W, ldw, col_scale, nullptr, 0, nullptr, values, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_masked(const hts_desc& d, const hts_tile* index, const uint16_t* W, int64_t ldw,
+                              const uint8_t* mask, int64_t ldm, uint32_t* malformed, uint16_t* values,
+                              uint32_t* meta, hipStream_t s) {
+    const int64_t Tk = d.K / d.bk, T = (d.N / d.bn) * Tk;
+    if (malformed) zero_counter<<<dim3(1), dim3(1), 0, s>>>(malformed);   // a kernel, not a memset node
+    if (d.dtype == HTS_BF16)
+        pack_kernel<BF16T, true><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
+            index, Tk, d.bn, d.bk, W, ldw, nullptr, mask, ldm, malformed, values, meta);
+    else
+        pack_kernel<F16T, true><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
+            index, Tk, d.bn, d.bk, W, ldw, nullptr, mask, ldm, malformed, values, meta);
     return hipGetLastError();
 }
 

@@ -71,6 +71,21 @@ def exact_map(n_tiles: int, n_sparse: int, g: np.random.Generator) -> np.ndarray
     return m
 
 
+TAG_MASK = 5
+
+
+def pair_mask(N: int, K: int, g: np.random.Generator) -> np.ndarray:
+    """uint8 keep mask [N,K] marking, in every group of four along K, one of the six pairs
+    (uniformly at random): a stand-in for a frozen 2:4 pattern from a one-shot pruning method."""
+    pairs = np.array([[1, 1, 0, 0], [1, 0, 1, 0], [1, 0, 0, 1], [0, 1, 1, 0], [0, 1, 0, 1], [0, 0, 1, 1]], np.uint8)
+    return pairs[g.integers(0, 6, size=(N, K // 4))].reshape(N, K)
+
+
+def layer_pair_mask(cfg: "Config", layer: "Layer") -> np.ndarray:
+    """The seeded pair mask of a named layer."""
+    return pair_mask(layer.N, layer.K, rng(cfg.cfg_id, layer.layer_id, TAG_MASK))
+
+
 def calib_bits(rows: int, K: int, dtype: str, cfg_id: int, layer_id: int,
                outlier_frac: float = 0.01, outlier_scale: float = 20.0) -> np.ndarray:
     """Calibration activations [rows, K] ~ N(0,1) with round(outlier_frac*K) columns scaled by outlier_scale."""

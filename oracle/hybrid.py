@@ -370,6 +370,22 @@ def wanda_tile_map(cost: np.ndarray, n_sparse: int) -> np.ndarray:
     return m
 
 
+def wanda_global_maps(costs, n_sparse: int):
+    """Global allocation over several layers (PATCH page, section 4, ablations: a sparsity
+    target shared by the whole model beats one per layer): the n_sparse tiles of lowest cost
+    among all tiles of all the layers become 2:4, ties broken by layer order then tile number.
+    Every layer's tiles must hold the same number of weights, so that counting tiles counts
+    weights.  Returns one map per layer."""
+    costs = [np.asarray(c, dtype=np.float64) for c in costs]
+    allc = np.concatenate(costs)
+    flat = wanda_tile_map(allc, n_sparse)         # position in the concatenation = (layer, tile) order
+    out, o = [], 0
+    for c in costs:
+        out.append(flat[o: o + c.size].copy())
+        o += c.size
+    return out
+
+
 def density(tile_map: np.ndarray) -> float:
     """Fraction of weights kept: 1 - 0.5 * (fraction of 2:4 tiles) (PATCH section 3: 0..50 % sparsity)."""
     tmap = np.asarray(tile_map)

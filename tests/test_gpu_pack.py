@@ -199,3 +199,24 @@ def test_pack_masked_with_magnitude_mask_equals_pack():
     torch.cuda.synchronize()
     assert int(malformed.item()) == 0
     assert torch.equal(pm.values, pw.values) and torch.equal(pm.meta, pw.meta)
+
+
+def test_wanda_global_maps_of_a_block():
+    # one sparse-tile budget shared by the seven projections of the 7B block (rho = 0.3 overall)
+    c = wl.config("7b_block")
+    Ws, css, ocosts = [], [], []
+    for L in c.layers:
+        Xc, cs = calib_scale(c.cfg_id, L.name)
+        W = weight(c.cfg_id, L.name)
+        Ws.append(hts.tensor_from_bits(W, L.dtype, DEV))
+        css.append(torch.from_numpy(cs).to(DEV))
+        ocosts.append(oracle.wanda_tile_cost(W, L.dtype, cs, L.bn, L.bk))
+    T = sum(L.T for L in c.layers)
+    n_s = int(round(2 * 0.3 * T))
+    say(f"[wanda-global] {len(Ws)} layers, {T} tiles, {n_s} sparse")
+    gm = hts.wanda_global_maps(Ws, css, 128, 128, n_s)
+    torch.cuda.synchronize()
+    om = oracle.wanda_global_maps(ocosts, n_s)
+    for L, a, b in zip(c.layers, gm, om):
+        assert np.array_equal(a.cpu().numpy(), b), L.name
+    assert sum(int(m.sum().item()) for m in gm) == n_s

@@ -481,3 +481,23 @@ def test_pack_from_magnitude_mask_equals_magnitude_pack(dtype):
     b = oracle.pack_masked(W, dtype, tmap, mask, bn, bk)
     assert b[3] == 0
     assert all(np.array_equal(x, y) for x, y in zip(a, b[:3]))
+
+
+# ---------------------------------------------------------------------------
+# global (cross-layer) Wanda allocation
+# ---------------------------------------------------------------------------
+
+def test_wanda_global_allocation_brute_force():
+    g = np.random.default_rng(53)
+    sizes = [12, 30, 7]
+    costs = [np.round(g.random(n) * 8) / 4 for n in sizes]      # many exact ties, across layers too
+    for n_s in (0, 1, 9, 25, sum(sizes)):
+        maps = oracle.wanda_global_maps(costs, n_s)
+        assert [m.size for m in maps] == sizes
+        assert sum(int(m.sum()) for m in maps) == n_s
+        keyed = [(float(costs[l][t]), l, t, int(maps[l][t])) for l in range(3) for t in range(sizes[l])]
+        sparse = [k[:3] for k in keyed if k[3] == 1]
+        dense = [k[:3] for k in keyed if k[3] == 0]
+        assert all(a < b for a in sparse for b in dense)        # (cost, layer, tile) order
+    # one layer: the global allocation is the per-layer one
+    assert np.array_equal(oracle.wanda_global_maps([costs[1]], 11)[0], oracle.wanda_tile_map(costs[1], 11))

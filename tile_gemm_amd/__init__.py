@@ -7,8 +7,8 @@ present, the calls raise.
 
 Low-level functions carry the C names (``hts_pack_plan``, ``hts_pack``,
 ``hts_unpack``, ``hts_gemm``, ``hts_dense_gemm``, ...); ``pack``, ``gemm``,
-``unpack``, ``dense_gemm`` and ``wanda_tile_map`` are tensor-level helpers
-built on them.
+``unpack``, ``dense_gemm``, ``pack_masked``, ``wanda_tile_map`` and
+``wanda_global_maps`` are tensor-level helpers built on them.
 """
 from __future__ import annotations
 
@@ -306,6 +306,26 @@ def wanda_tile_map(W: torch.Tensor, col_scale: torch.Tensor, bn: int, bk: int, n
     m = torch.empty(T, dtype=torch.uint8, device=W.device)
     hts_wanda_map(cost, n_sparse, m, stream=stream)
     return m
+
+
+def wanda_global_maps(Ws, col_scales, bn: int, bk: int, n_sparse: int, stream=None):
+    """Device tile maps of several layers from one shared sparse-tile budget: the n_sparse tiles
+    with the least dropped Wanda mass among all the layers' tiles become 2:4 (ties: layer order,
+    then tile number).  The costs of all layers go into one device buffer, one slice per layer."""
+    descs, Ts = [], []
+    for W in Ws:
+        N, K = W.shape
+        descs.append(make_desc(N, K, bn, bk, W.dtype))
+        Ts.append((N // bn) * (K // bk))
+    cost = torch.empty(sum(Ts), dtype=torch.float64, device=Ws[0].device)
+    off = 0
+    for d, W, cs, T in zip(descs, Ws, col_scales, Ts):
+        _check(lib().hts_wanda_tile_cost(ctypes.byref(d), _ptr(W), W.stride(0), _ptr(cs),
+                                         ctypes.c_void_p(cost.data_ptr() + 8 * off), _stream(stream)))
+        off += T
+    m = torch.empty(sum(Ts), dtype=torch.uint8, device=Ws[0].device)
+    hts_wanda_map(cost, n_sparse, m, stream=stream)
+    return list(torch.split(m, Ts))
 
 
 def tensor_from_bits(bits: np.ndarray, dtype: str, device) -> torch.Tensor:

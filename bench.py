@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--layer", type=int, default=0)
     p.add_argument("--quick", action="store_true", help="profiling run: a few launches of each kernel, no oracle")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    p.add_argument("--no-block", action="store_true", help="skip the decoder-block leg")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run three plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
@@ -81,6 +82,60 @@ def recorded_traffic(workload_key: str):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def run_block(hts, wl, dev, time_graph, quick):
+    """One 7B decoder block's seven projections (+ the gated-MLP step) at M = 2048 on packed weights
+    with Wanda tile maps at 30 % overall sparsity -- per layer and with one global budget -- against
+    the same pipeline on the same-library dense product and on torch (hipBLASLt) for context.
+    Maps are derived on the GPU (column norms of the calibration rows, tile costs, selection)."""
+    import torch
+    import tile_gemm_amd.block as block
+    cfg = wl.config("7b_block")
+    M = 2048
+    Ws, css = {}, {}
+    for L in cfg.layers:
+        Ws[L.name] = hts.tensor_from_bits(wl.weight_bits(cfg, L), L.dtype, dev)
+        css[L.name] = hts.col_norms(hts.tensor_from_bits(wl.layer_calib_bits(cfg, L), L.dtype, dev))
+    maps = {"per_layer": {L.name: hts.wanda_tile_map(Ws[L.name], css[L.name], L.bn, L.bk, L.n_sparse_target)
+                          for L in cfg.layers}}
+    T = sum(L.T for L in cfg.layers)
+    glob = hts.wanda_global_maps([Ws[L.name] for L in cfg.layers], [css[L.name] for L in cfg.layers], 128, 128,
+                                 int(round(2 * 0.3 * T)))
+    maps["global"] = {L.name: m for L, m in zip(cfg.layers, glob)}
+    X = hts.tensor_from_bits(wl.activation_bits(cfg, cfg.layers[0], M), "bf16", dev)
+    reps = 3 if quick else 10
+    out = {"workload": "LLaMA-2-7B decoder block linear layers (q, k, v, o 4096x4096; gate, up 11008x4096; "
+                       "down 4096x11008; bf16) + silu(gate)*up, M=2048; o reads q in place of the attention output",
+           "M": M}
+    dense_bufs = block.buffers(M, Ws, X.dtype, dev)
+    t_dense = time_graph(lambda i: block.forward(X, Ws, dense_bufs), 1, reps)
+    dense_flops = block.kept_flops(M, Ws)
+    for kind, mp in maps.items():
+        packed = {L.name: hts.pack(Ws[L.name], mp[L.name].cpu().numpy(), L.bn, L.bk) for L in cfg.layers}
+        bufs = block.buffers(M, packed, X.dtype, dev)
+        t = time_graph(lambda i: block.forward(X, packed, bufs), 1, reps)
+        flops = block.kept_flops(M, packed)
+        ns = {L.name: int(mp[L.name].sum().item()) for L in cfg.layers}
+        out[kind] = {"us": round(t * 1e6, 1), "TFLOP/s": round(flops / t / 1e12, 1),
+                     "speedup_vs_dense": round(t_dense / t, 3),
+                     "sparse_tiles": ns, "overall_sparsity": round(0.5 * sum(ns.values()) / T, 4)}
+        del packed, bufs
+    out["dense_same_library_us"] = round(t_dense * 1e6, 1)
+    out["dense_same_library_TFLOP/s"] = round(dense_flops / t_dense / 1e12, 1)
+
+    def torch_block(i, bufs=dense_bufs):
+        torch.matmul(X, Ws["q"].t(), out=bufs["q"])
+        torch.matmul(X, Ws["k"].t(), out=bufs["k"])
+        torch.matmul(X, Ws["v"].t(), out=bufs["v"])
+        torch.matmul(bufs["q"], Ws["o"].t(), out=bufs["o"])
+        torch.matmul(X, Ws["gate"].t(), out=bufs["gate"])
+        torch.matmul(X, Ws["up"].t(), out=bufs["up"])
+        torch.mul(torch.nn.functional.silu(bufs["gate"]), bufs["up"], out=bufs["h"])
+        torch.matmul(bufs["h"], Ws["down"].t(), out=bufs["down"])
+    t_torch = time_graph(torch_block, 1, reps)
+    out["torch_us"] = round(t_torch * 1e6, 1)
+    return out
 
 
 def main():
@@ -256,6 +311,9 @@ def main():
         torch.cuda.synchronize()
         del srcs, dsts
 
+    # ---------------- decoder block: the seven projections of a 7B block ----------------
+    block_res = None if args.no_block else run_block(hts, wl, dev, time_graph, args.quick)
+
     # ---------------- CPU oracle on the host cores ----------------
     cpu = None
     if not (args.quick or args.no_cpu):
@@ -319,6 +377,7 @@ def main():
         "unpack": {"us": round(t_unpack * 1e6, 2), "GB/s": round(pack_bytes / t_unpack / 1e9, 1)},
         "pack_masked": {"us": round(t_pack_masked * 1e6, 2), "GB/s": round(pack_masked_bytes / t_pack_masked / 1e9, 1),
                         "frac_hbm": round(pack_masked_bytes / t_pack_masked / 1e9 / HBM_PEAK_GBS, 4)},
+        "block": block_res,
         "packed_bytes": packed_bytes,
         "rotation_copies": n_rot,
         "wall_s_timed_region": round(wall, 4),

@@ -166,6 +166,15 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K,
                           void* Y, int64_t ldy, int32_t y_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Device, asynchronous.  H[M,N] = silu(G) * U elementwise, silu(x) = x / (1 + e^-x), fp32
+ * arithmetic, one round-to-nearest-even to dtype (HTS_F16 / HTS_BF16, shared by G, U and H):
+ * the gated-MLP step between the gate / up projections and the down projection of a decoder
+ * block whose linear layers are hybrid tile-sparse (the pages prune the linear layers of LLaMA
+ * models; this step is the architecture's, not the method's).  N % 8 == 0; G, U, H 16-byte
+ * aligned with leading dimensions (elements) >= N and multiples of 8.  M == 0 is a no-op. */
+hts_status hts_silu_mul(int32_t dtype, int64_t M, int64_t N, const void* G, int64_t ldg, const void* U,
+                        int64_t ldu, void* H, int64_t ldh, void* stream);
+
 /* Device, asynchronous.  Wanda column scale c[k] = ||X[:,k]||_2 of calibration
  * activations X[rows,K] (ldx): squares summed in fp64 over rows in order, one
  * rounding of the square root to fp32 (Wanda section of the SparseGPT-vs-Wanda

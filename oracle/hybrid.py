@@ -370,6 +370,14 @@ def wanda_tile_map(cost: np.ndarray, n_sparse: int) -> np.ndarray:
     return m
 
 
+def silu_mul_ref(G_bits: np.ndarray, U_bits: np.ndarray, dtype: str) -> np.ndarray:
+    """H = silu(G) * U in float64 on the exactly widened 16-bit inputs, silu(x) = x / (1 + e^-x):
+    the gated MLP step between the gate / up projections and the down projection."""
+    g = widen_f64(G_bits, dtype)
+    u = widen_f64(U_bits, dtype)
+    return g / (1.0 + np.exp(-g)) * u
+
+
 def wanda_global_maps(costs, n_sparse: int):
     """Global allocation over several layers (PATCH page, section 4, ablations: a sparsity
     target shared by the whole model beats one per layer): the n_sparse tiles of lowest cost

@@ -151,3 +151,13 @@ def test_pack_masked_rejects_bad_arguments():
     assert L.hts_pack_masked(by(d), A16, A16, 256, A16, 256, A16, A16, A8 + 2, None) == 4    # counter alignment
     bad = hts.make_desc(256, 200, 64, 64, "bf16")
     assert L.hts_pack_masked(by(bad), A16, A16, 256, A16, 256, A16, A16, None, None) == 3    # K % bk
+
+
+def test_silu_mul_rejects_bad_arguments():
+    L = hts.lib()
+    assert L.hts_silu_mul(2, 4, 64, A16, 64, A16, 64, A16, 64, None) == 2       # f32 not supported
+    assert L.hts_silu_mul(1, 4, 60, A16, 64, A16, 64, A16, 64, None) == 3       # N % 8
+    assert L.hts_silu_mul(1, 4, 64, A16, 60, A16, 64, A16, 64, None) == 3       # ldg < N
+    assert L.hts_silu_mul(1, 4, 64, A8, 64, A16, 64, A16, 64, None) == 4        # alignment
+    assert L.hts_silu_mul(1, 4, 64, None, 64, A16, 64, A16, 64, None) == 1      # null
+    assert L.hts_silu_mul(1, 0, 64, None, 64, None, 64, None, 64, None) == 0    # M == 0: nothing to do

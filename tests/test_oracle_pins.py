@@ -501,3 +501,24 @@ def test_wanda_global_allocation_brute_force():
         assert all(a < b for a in sparse for b in dense)        # (cost, layer, tile) order
     # one layer: the global allocation is the per-layer one
     assert np.array_equal(oracle.wanda_global_maps([costs[1]], 11)[0], oracle.wanda_tile_map(costs[1], 11))
+
+
+def test_silu_mul_closed_forms():
+    # silu(x) = x * sigmoid(x).  Pins that are not the formula: tabulated logistic values
+    # (sigmoid(1) = 0.7310585786300049, sigmoid(2) = 0.8807970779778823, sigmoid(-1) = 0.2689414213699951),
+    # the odd-part identity silu(x) - silu(-x) = x, the asymptotes, and linearity in U.
+    xs = np.array([1.0, 2.0, -1.0, 16.0, -16.0], np.float32)
+    one = wl.to_bits(np.ones_like(xs), "f16")
+    h = oracle.silu_mul_ref(wl.to_bits(xs, "f16"), one, "f16")
+    assert np.allclose(h[:3], [0.7310585786300049, 2 * 0.8807970779778823, -0.2689414213699951], rtol=1e-15, atol=0)
+    assert abs(h[3] - 16.0) < 2e-6 and abs(h[4]) < 2e-6
+    g = np.random.default_rng(59)
+    x = wl.gaussian_bits((256,), 3.0, "bf16", g)
+    negx = x ^ np.uint16(0x8000)                           # exact negation of the bit pattern
+    ones = wl.to_bits(np.ones(256, np.float32), "bf16")
+    d = oracle.silu_mul_ref(x, ones, "bf16") - oracle.silu_mul_ref(negx, ones, "bf16")
+    assert np.allclose(d, oracle.widen_f64(x, "bf16"), rtol=1e-14, atol=1e-300)
+    assert oracle.silu_mul_ref(wl.to_bits(np.zeros(3, np.float32), "bf16"), ones[:3], "bf16").tolist() == [0.0] * 3
+    three = wl.to_bits(np.full(256, 3.0, np.float32), "bf16")
+    assert np.allclose(oracle.silu_mul_ref(x, three, "bf16"), 3.0 * oracle.silu_mul_ref(x, ones, "bf16"),
+                       rtol=1e-15, atol=0)

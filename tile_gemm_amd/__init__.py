@@ -62,6 +62,7 @@ _SIGS = {
                                 _VP, ctypes.c_size_t, _VP]),
     "hts_dense_gemm": (ctypes.c_int, [_I32, _I64, _I64, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _I32, _VP,
                                       ctypes.c_size_t, _VP]),
+    "hts_silu_mul": (ctypes.c_int, [_I32, _I64, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _VP]),
     "hts_col_norms": (ctypes.c_int, [_I32, _I64, _I64, _VP, _I64, _VP, _VP]),
     "hts_wanda_tile_cost": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _I64, _VP, _VP, _VP]),
     "hts_wanda_map": (ctypes.c_int, [_I64, _VP, _I64, _VP, _VP]),
@@ -187,6 +188,20 @@ def hts_dense_gemm(X, W, Y, stream=None) -> None:
 def hts_col_norms(X, out, stream=None) -> None:
     rows, K = X.shape
     _check(lib().hts_col_norms(_dt(X.dtype), rows, K, _ptr(X), X.stride(0), _ptr(out), _stream(stream)))
+
+
+def hts_silu_mul(G, U, H, stream=None) -> None:
+    M, N = G.shape
+    _check(lib().hts_silu_mul(_dt(G.dtype), M, N, _ptr(G), G.stride(0), _ptr(U), U.stride(0), _ptr(H), H.stride(0),
+                              _stream(stream)))
+
+
+def silu_mul(G: torch.Tensor, U: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """H = silu(G) * U (the gated-MLP step between the up / gate and down projections)."""
+    if out is None:
+        out = torch.empty_like(G)
+    hts_silu_mul(G, U, out, stream=stream)
+    return out
 
 
 def hts_wanda_tile_cost(desc, W, col_scale, cost, stream=None) -> None:

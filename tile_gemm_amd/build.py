@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhts.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["hts_api.cpp", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "wanda.hip"]
+SOURCES = ["hts_api.cpp", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "wanda.hip", "elementwise.hip"]
 
 ARCH = "gfx950"
 COMMON = [

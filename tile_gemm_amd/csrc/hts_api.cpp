@@ -129,6 +129,10 @@ hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
         e = hts::launch_gemm_decode(a, decode_ksplit(a), decode_nt(a), decode_pp(a), sparse_path(), s);
     } else {
         const int tile = prefill_tile(a);
+        // the tiled kernel addresses X rows (and rows of a row-major W) by 32-bit byte offsets
+        // from its block's first row
+        if (a.ldx > (int64_t(1) << 24) || (!a.index && a.ldw > (int64_t(1) << 24)))
+            return fail(HTS_ERR_UNSUPPORTED, "leading dimension above 2^24 elements at M > %lld", (long long)decode_max_m());
         if (a.index && a.K / a.bk > hts::kMaxTileColsPerRow)
             return fail(HTS_ERR_UNSUPPORTED, "K/bk=%lld tile columns exceed the %d of one tile row the tiled kernel holds",
                         (long long)(a.K / a.bk), hts::kMaxTileColsPerRow);
@@ -313,6 +317,22 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const 
     a.Y = Y;
     a.ldy = ldy;
     return run_gemm(a, static_cast<hipStream_t>(stream));
+}
+
+hts_status hts_silu_mul(int32_t dtype, int64_t M, int64_t N, const void* G, int64_t ldg, const void* U,
+                        int64_t ldu, void* H, int64_t ldh, void* stream) {
+    if (dtype != HTS_F16 && dtype != HTS_BF16) return fail(HTS_ERR_DTYPE, "dtype %d is not F16 or BF16", dtype);
+    if (M < 0 || N <= 0) return fail(HTS_ERR_SHAPE, "M=%lld N=%lld (M >= 0, N positive)", (long long)M, (long long)N);
+    if (N % 8) return fail(HTS_ERR_SHAPE, "N=%lld is not a multiple of 8", (long long)N);
+    if (M == 0) return ok();
+    hts_status st;
+    if ((st = check_ptr(G, "G")) || (st = check_ptr(U, "U")) || (st = check_ptr(H, "H"))) return st;
+    if ((st = check_ld(ldg, N, 8, "ldg")) || (st = check_ld(ldu, N, 8, "ldu")) || (st = check_ld(ldh, N, 8, "ldh")))
+        return st;
+    return hip_status(hts::launch_silu_mul(dtype, M, N, static_cast<const uint16_t*>(G), ldg,
+                                           static_cast<const uint16_t*>(U), ldu, static_cast<uint16_t*>(H), ldh,
+                                           static_cast<hipStream_t>(stream)),
+                      "silu_mul kernel launch");
 }
 
 hts_status hts_col_norms(int32_t dtype, int64_t rows, int64_t K, const void* X, int64_t ldx, float* col_scale,

@@ -44,6 +44,8 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, int tile, hip
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the
 // tiled kernel holds the index records of one tile row in LDS.
 constexpr int kMaxTileColsPerRow = 256;
+hipError_t launch_silu_mul(int32_t dtype, int64_t M, int64_t N, const uint16_t* G, int64_t ldg, const uint16_t* U,
+                           int64_t ldu, uint16_t* H, int64_t ldh, hipStream_t s);
 hipError_t launch_col_norms(int32_t dtype, int64_t rows, int64_t K, const uint16_t* X, int64_t ldx,
                             float* out, hipStream_t s);
 hipError_t launch_wanda_cost(const hts_desc& d, const uint16_t* W, int64_t ldw, const float* cs,

@@ -85,6 +85,20 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_off) {
     __builtin_amdgcn_global_load_lds(g, (lds_t*)(lds_base() + lds_off), 4, 0, 0);
 }
+// The same copies through a buffer resource: a scalar base and byte bound, a per-lane 32-bit
+// offset fixed for the K loop and a scalar offset per slice -- no 64-bit address arithmetic per
+// copy.  Lanes past the bound read zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ void buf16(rsrc_t r, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)(lds_base() + lds_off), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf4(rsrc_t r, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)(lds_base() + lds_off), 4, voff, soff, 0, 0);
+}
 
 // Everything the copy jobs need, fixed for the whole K loop.  A job moves 1 KiB (64
 // lanes x 16 B) into contiguous LDS; each lane picks the global chunk whose swizzled
@@ -103,15 +117,28 @@ struct Ctx {
     int wave, lane;
     int n_dense;                // dense tiles of the list (they come first)
     const uint2* list;          // {val_off, meta_off} of the tile row's tiles in list order
+    // the ordered list in registers: entry p = lane p % 64 of register p / 64 (K / bk <= 256)
+    uint32_t lv[4], lm[4], lc[4];
     int Tk;
-    const uint16_t* xsrc[XJ];           // per X copy job of this wave
-    int d_off[JPG];                     // dense group jobs: row * BK + chunk
-    int64_t rm_off[JPG];                // row-major weight jobs: row * ldw + chunk
-    int s_off;                          // 2:4 values job
-    int m_off;                          // 2:4 codes job
+    rsrc_t xr;                          // X rows m0 .. M-1
+    rsrc_t wr;                          // values of the tile row from its first tile (or W rows n0 ..)
+    rsrc_t mr;                          // codes of the tile row from its first tile
+    uint32_t vbase, mbase;              // first value / code word of the tile row
+    uint32_t xso;                       // bytes: tile column and slice of the X copies of a slice
+    uint32_t xvo[XJ];                   // per-lane byte offsets: X jobs
+    uint32_t dvo[JPG];                  // dense group jobs (row * BK + chunk, or row * ldw + chunk)
+    uint32_t svo;                       // 2:4 values job
+    uint32_t mvo;                       // 2:4 codes job
     bool meta_to_sink;                  // codes jobs 2, 3 repeat jobs 0, 1 into the sink
     __device__ __forceinline__ bool gvalid(int gi) const { return n0 + 64 * gi < N; }
 };
+
+// Entry p of a list held one entry per lane in four registers (a uniform read: no LDS access).
+__device__ __forceinline__ uint32_t list_entry(const uint32_t (&r)[4], int p) {
+    const int w = p >> 6;
+    const uint32_t v = w == 0 ? r[0] : (w == 1 ? r[1] : (w == 2 ? r[2] : r[3]));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, p & 63);
+}
 
 // Copies of one slice into an LDS stage.  Per 64-row weight group there are 8 copy jobs:
 // dense = 8 x 1 KiB; 2:4 = 4 x 1 KiB of stored values, 2 x 256 B of codes and 2 padding copies
@@ -127,41 +154,37 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
     // read the list entry before any copy is issued: an LDS read after a copy into LDS makes
     // the compiler wait for every copy in flight
     uint32_t voff = 0, moff = 0;
-    if (HYB) {
-        const uint2 e = C.list[p];            // every group of the block is in the same tile
-        voff = __builtin_amdgcn_readfirstlane(e.x);
-        moff = __builtin_amdgcn_readfirstlane(e.y);
+    if (HYB) {                                // every group of the block is in the same tile
+        voff = list_entry(C.lv, p);
+        moff = list_entry(C.lm, p);
     }
 #pragma unroll
-    for (int v = 0; v < BM / (8 * NW); ++v) dma16(C.xsrc[v], stage + 1024 * (C.wave + NW * v));
+    for (int v = 0; v < BM / (8 * NW); ++v) buf16(C.xr, stage + 1024 * (C.wave + NW * v), C.xvo[v], C.xso);
 #pragma unroll
     for (int gi = 0; gi < Lo::NG; ++gi) {
         const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
-        if (!HYB) {
-            if (!C.gvalid(gi)) {                // rows past N: keep the copy count, land in the sink
-#pragma unroll
-                for (int v = 0; v < JPG; ++v) dma16(C.xsrc[0], Lo::SINK);
-                continue;
-            }
+        if (!HYB) {                             // rows past N read zeros (bound of the resource)
 #pragma unroll
             for (int v = 0; v < JPG; ++v)
-                dma16(C.W + (64 * gi) * C.ldw + ks * kKS + C.rm_off[v], ws + 1024 * (C.wave + NW * v));
+                buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v],
+                      (uint32_t)(2 * (64 * gi * C.ldw + (int64_t)ks * kKS)));
             continue;
         }
-        const int r = 64 * gi;                  // a block is one tile row: groups at rows 0, 64
+        const uint32_t r = 64 * gi;             // a block is one tile row: groups at rows 0, 64
         if (DENSE) {
+            const uint32_t so = 2 * (voff - C.vbase + r * BK + s * kKS);
 #pragma unroll
-            for (int v = 0; v < JPG; ++v)
-                dma16(C.values + voff + r * BK + s * kKS + C.d_off[v], ws + 1024 * (C.wave + NW * v));
+            for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
         } else {
             // jobs 0-3: stored values; 4, 5: codes; 6, 7: the codes again into the sink.  With 4
             // waves wave w does jobs w and 4 + w, with 8 waves job w.
             if (NW == 4 || C.wave < 4)
-                dma16(C.values + voff + r * (BK / 2) + s * (kKS / 2) + C.s_off, ws + 1024 * (C.wave & 3));
+                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, 2 * (voff - C.vbase + r * (BK / 2) + s * (kKS / 2)));
             if (NW == 4 || C.wave >= 4)
-                dma4(C.meta + moff + r * (BK / 32) + 2 * s + C.m_off,
+                buf4(C.mr,
                      C.meta_to_sink ? (uint32_t)Lo::SINK
-                                    : stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * (C.wave & 1));
+                                    : stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * (C.wave & 1),
+                     C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + 2 * s));
         }
     }
 }
@@ -312,16 +335,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     C.lane = lane;
     C.Tk = (int)(a.K / BK);
     const int64_t m0 = (int64_t)mb * BM;
+    // copy sources: X rows m0 .. M-1 (rows past M read zeros and feed only unstored outputs);
+    // the packed tile row from its first tile (offsets within a tile row fit 32 bits: K/bk <= 256
+    // tiles of at most 32 KiB), or W rows n0 .. N-1 of the dense product
+    C.xr = make_rsrc(a.X + m0 * a.ldx, (uint64_t)(a.M - m0) * a.ldx * 2);
+    if (HYB) {
+        const hts_tile first = a.index[(C.n0 / a.bn) * C.Tk];
+        C.vbase = first.val_off;
+        C.mbase = first.meta_off;
+        C.wr = make_rsrc(a.values + C.vbase, (uint64_t)C.Tk * BN * BK * 2);
+        C.mr = make_rsrc(a.meta + C.mbase, (uint64_t)C.Tk * BN * BK / 8);
+    } else {
+        C.vbase = C.mbase = 0;
+        C.wr = make_rsrc(a.W + C.n0 * a.ldw, (uint64_t)(a.N - C.n0) * a.ldw * 2);
+        C.mr = C.wr;
+    }
+    C.xso = 0;
     for (int v = 0; v < 8 / NW; ++v) {
         const int row = 8 * (wave + NW * v) + (lane >> 3), col = (lane & 7) ^ ((row >> 1) & 7);
-        C.d_off[v] = row * BK + 8 * col;
-        C.rm_off[v] = (int64_t)row * a.ldw + 8 * col;
+        C.dvo[v] = HYB ? (uint32_t)(2 * (row * BK + 8 * col)) : (uint32_t)(2 * ((int64_t)row * a.ldw + 8 * col));
     }
     {
         const int row = 16 * (wave & 3) + (lane >> 2), col = (lane & 3) ^ ((row >> 2) & 3);
-        C.s_off = row * (BK / 2) + 8 * col;
+        C.svo = (uint32_t)(2 * (row * (BK / 2) + 8 * col));
         const int wi = 64 * (wave & 1) + lane;
-        C.m_off = (wi >> 1) * (BK / 32) + (wi & 1);
+        C.mvo = (uint32_t)(4 * ((wi >> 1) * (BK / 32) + (wi & 1)));
         C.meta_to_sink = (NW == 4) ? wave >= 2 : wave >= 6;
     }
     // ordered tile list of the tile row (dense first), tile columns kept for the X copies
@@ -359,26 +397,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         }
         C.n_dense = nd;
         __syncthreads();
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int q = 64 * w + lane;
+            const bool in = q < C.Tk;
+            C.lv[w] = in ? list[q].x : 0u;
+            C.lm[w] = in ? list[q].y : 0u;
+            C.lc[w] = in ? (uint32_t)lcol[q] : 0u;
+        }
     } else {
         C.n_dense = C.Tk;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) C.lv[w] = C.lm[w] = C.lc[w] = 0u;
     }
 
     // per-lane X sources of this wave's copy jobs; the tile column is added per slice
     constexpr int XJ = BM / (8 * NW);      // X copy jobs per wave
-    const uint16_t* xbase[XJ];
 #pragma unroll
     for (int v = 0; v < XJ; ++v) {
         const int row = 8 * (wave + NW * v) + (lane >> 3);
         const int xc = (lane & 7) ^ ((row >> 1) & 7);
-        const int64_t m = m0 + row;
-        xbase[v] = a.X + (m < a.M ? m : a.M - 1) * a.ldx + 8 * xc;   // rows past M only feed unstored outputs
+        C.xvo[v] = (uint32_t)(2 * ((int64_t)row * a.ldx + 8 * xc));
     }
     auto set_x = [&](int ks) {
         const int p = ks / SPT, s = ks % SPT;
-        const int tk = HYB ? (int)lcol[p] : p;
-        const int64_t k0 = (int64_t)tk * BK + s * kKS;
-#pragma unroll
-        for (int v = 0; v < XJ; ++v) C.xsrc[v] = xbase[v] + k0;
+        const int tk = HYB ? (int)list_entry(C.lc, p) : p;
+        C.xso = (uint32_t)(2 * (tk * BK + s * kKS));
     };
 
     f32x4 acc[4][NBJ];

@@ -117,7 +117,9 @@ struct Ctx {
     int wave, lane;
     int n_dense;                // dense tiles of the list (they come first)
     const uint2* list;          // {val_off, meta_off} of the tile row's tiles in list order
-    // the ordered list in registers: entry p = lane p % 64 of register p / 64 (K / bk <= 256)
+    // the ordered list in registers, 64 entries per register (K / bk <= 256).  It is read in order,
+    // and after each block of 64 entries the registers move down by one (shift_list), so entry p
+    // is always lane p % 64 of the first register: one lane read, no register select.
     uint32_t lv[4], lm[4], lc[4];
     int Tk;
     rsrc_t xr;                          // X rows m0 .. M-1
@@ -131,13 +133,21 @@ struct Ctx {
     uint32_t mvo;                       // 2:4 codes job
     bool meta_to_sink;                  // codes jobs 2, 3 repeat jobs 0, 1 into the sink
     __device__ __forceinline__ bool gvalid(int gi) const { return n0 + 64 * gi < N; }
+    __device__ __forceinline__ void shift_list() {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            lv[w] = lv[w + 1];
+            lm[w] = lm[w + 1];
+            lc[w] = lc[w + 1];
+        }
+        lv[3] = lm[3] = lc[3] = 0u;
+    }
 };
 
-// Entry p of a list held one entry per lane in four registers (a uniform read: no LDS access).
+// Entry p of a list held one entry per lane (a uniform read: no LDS access); the caller has
+// shifted the registers so that the block of entry p is in the first one.
 __device__ __forceinline__ uint32_t list_entry(const uint32_t (&r)[4], int p) {
-    const int w = p >> 6;
-    const uint32_t v = w == 0 ? r[0] : (w == 1 ? r[1] : (w == 2 ? r[2] : r[3]));
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, p & 63);
+    return (uint32_t)__builtin_amdgcn_readlane((int)r[0], p & 63);
 }
 
 // Copies of one slice into an LDS stage.  Per 64-row weight group there are 8 copy jobs:
@@ -435,7 +445,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     const bool wvalid = C.gvalid(wn);
     const int xoff = wm * WTM * 128;
     constexpr int PER_SLICE = XJ + NG * (8 / NW);   // copy instructions per wave per slice
-    auto issue = [&](int kn) {
+    auto issue = [&](int kn) {   // called for kn = 0, 1, 2, ... in order
+        if (HYB && kn > 0 && kn % (64 * SPT) == 0) C.shift_list();
         set_x(kn);
         const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
         if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW>(C, kn, stage);

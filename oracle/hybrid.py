@@ -27,7 +27,12 @@ Readings where the pages are silent (each also listed in the design notes):
   * Products are evaluated in fp64 on the 16-bit inputs widened exactly.
 
 All 16-bit arrays are numpy uint16 bit patterns with a dtype tag "f16" (IEEE
-binary16) or "bf16" (bfloat16).
+binary16) or "bf16" (bfloat16).  The 8-bit variant (prune, then quantize: the
+FAQ of the SparseGPT-vs-Wanda page pairs 2:4 pruning with low-precision
+weights) stores numpy uint8 patterns with the tag "fp8": the OCP 8-bit E4M3
+format (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals,
+no infinities, 0x7F and 0xFF are NaN).  Every E4M3 value is exact in binary32,
+so every rule above applies unchanged to the decoded values.
 """
 from __future__ import annotations
 
@@ -40,8 +45,30 @@ TILE_SPARSE24 = 1
 # 16-bit storage types, widened exactly
 # ----------------------------------------------------------------------------
 
+def storage_type(dtype: str):
+    """numpy type of the stored bit patterns of a weight / activation dtype."""
+    if dtype == "fp8":
+        return np.uint8
+    if dtype in ("f16", "bf16"):
+        return np.uint16
+    raise ValueError(f"unknown storage type {dtype!r}")
+
+
+def e4m3_value(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 value of OCP E4M3 bytes: (-1)^s * 2^(e-7) * (1 + m/8) for e > 0,
+    (-1)^s * 2^-6 * (m/8) for e = 0; the two all-ones patterns 0x7F / 0xFF are NaN."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
 def widen_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float32 value of every 16-bit pattern (both formats embed in binary32)."""
+    """Exact float32 value of every stored pattern (all three formats embed in binary32)."""
+    if dtype == "fp8":
+        return e4m3_value(bits).astype(np.float32)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == "f16":
         return bits.view(np.float16).astype(np.float32)
@@ -130,11 +157,11 @@ def masked_weights(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int
     tmap = np.asarray(tile_map, dtype=np.uint8).ravel()
     assert tmap.size == (N // bn) * (K // bk)
     assert np.all(tmap <= 1), "tile map entries must be 0 (dense) or 1 (2:4)"
-    tiles = as_tiles(np.asarray(W_bits, dtype=np.uint16), bn, bk)
+    tiles = as_tiles(np.asarray(W_bits, dtype=storage_type(dtype)), bn, bk)
     stiles = as_tiles(selection_scores(W_bits, dtype, col_scale), bn, bk)
     for t in np.nonzero(tmap == TILE_SPARSE24)[0]:
         keep = sparse_tile_keep(stiles[t])
-        tiles[t][~keep] = 0  # +0.0 in both formats
+        tiles[t][~keep] = 0  # +0.0 in every format
     return from_tiles(tiles, N, K)
 
 
@@ -155,8 +182,9 @@ def masked_weights(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int
 VALID_NIBBLES = frozenset({0x4, 0x8, 0xC, 0x9, 0xD, 0xE})
 
 
-def plan(tile_map: np.ndarray, N: int, K: int, bn: int, bk: int):
-    """Tile index [T,4] uint32 and buffer sizes for a tile map (sizes in elements/words/bytes)."""
+def plan(tile_map: np.ndarray, N: int, K: int, bn: int, bk: int, elem_bytes: int = 2):
+    """Tile index [T,4] uint32 and buffer sizes for a tile map (sizes in elements/words/bytes;
+    elem_bytes is 2 for the 16-bit types, 1 for fp8)."""
     check_grid(N, K, bn, bk)
     tmap = np.asarray(tile_map, dtype=np.uint8).ravel()
     T = (N // bn) * (K // bk)
@@ -172,21 +200,23 @@ def plan(tile_map: np.ndarray, N: int, K: int, bn: int, bk: int):
         else:
             val_off += bn * bk
     n_sparse = int(tmap.sum())
-    sizes = {"values": val_off, "meta": meta_off, "values_bytes": 2 * val_off,
+    sizes = {"values": val_off, "meta": meta_off, "values_bytes": elem_bytes * val_off,
              "meta_bytes": 4 * meta_off, "index_bytes": 16 * T, "n_sparse": n_sparse}
     return index, sizes
 
 
 def pack(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int, bk: int,
          col_scale: np.ndarray | None = None, scores: np.ndarray | None = None):
-    """(values uint16, meta uint32, index uint32[T,4]) of W under the tile map.
+    """(values, meta uint32, index uint32[T,4]) of W under the tile map (values in the storage
+    type of dtype: uint16, or uint8 for fp8).
 
     scores: float32 [N,K] selection scores to use instead of the magnitude / Wanda scores
     (see pack_masked)."""
     N, K = W_bits.shape
+    st = storage_type(dtype)
     index, sizes = plan(tile_map, N, K, bn, bk)
     tmap = index[:, 2]
-    tiles = as_tiles(np.asarray(W_bits, dtype=np.uint16), bn, bk)
+    tiles = as_tiles(np.asarray(W_bits, dtype=st), bn, bk)
     if scores is None:
         scores = selection_scores(W_bits, dtype, col_scale)
     stiles = as_tiles(np.asarray(scores, dtype=np.float32), bn, bk)
@@ -207,7 +237,7 @@ def pack(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int, bk: int,
         shifts = (4 * np.arange(8)).astype(np.uint32)
         words = np.bitwise_or.reduce(nib << shifts, axis=-1)  # [bn, bk/32]
         meta.append(words.ravel())
-    vals = np.concatenate(values).astype(np.uint16) if values else np.zeros(0, np.uint16)
+    vals = np.concatenate(values).astype(st) if values else np.zeros(0, st)
     met = np.concatenate(meta).astype(np.uint32) if meta else np.zeros(0, np.uint32)
     assert vals.size == sizes["values"] and met.size == sizes["meta"]
     return vals, met, index
@@ -253,7 +283,7 @@ def masked_weights_from_mask(W_bits: np.ndarray, tile_map: np.ndarray, mask: np.
     N, K = W_bits.shape
     check_grid(N, K, bn, bk)
     tmap = np.asarray(tile_map, dtype=np.uint8).ravel()
-    tiles = as_tiles(np.asarray(W_bits, dtype=np.uint16), bn, bk)
+    tiles = as_tiles(np.asarray(W_bits), bn, bk)
     stiles = as_tiles(mask_scores(mask), bn, bk)
     for t in np.nonzero(tmap == TILE_SPARSE24)[0]:
         keep = sparse_tile_keep(stiles[t])
@@ -263,12 +293,14 @@ def masked_weights_from_mask(W_bits: np.ndarray, tile_map: np.ndarray, mask: np.
 
 def unpack(values: np.ndarray, meta: np.ndarray, index: np.ndarray, N: int, K: int,
            bn: int, bk: int) -> np.ndarray:
-    """Inverse of pack: W'[N,K] bits with +0.0 at dropped positions of sparse tiles."""
+    """Inverse of pack: W'[N,K] bits (the storage type of values) with +0.0 at dropped
+    positions of sparse tiles."""
     check_grid(N, K, bn, bk)
     T = (N // bn) * (K // bk)
     assert index.shape == (T, 4)
     G = bk // 4
-    tiles = np.zeros((T, bn, bk), dtype=np.uint16)
+    values = np.asarray(values)
+    tiles = np.zeros((T, bn, bk), dtype=values.dtype)
     for t in range(T):
         val_off, meta_off, typ, _ = (int(x) for x in index[t])
         if typ == TILE_DENSE:
@@ -280,7 +312,7 @@ def unpack(values: np.ndarray, meta: np.ndarray, index: np.ndarray, N: int, K: i
         nib = nib.reshape(bn, G)
         i0 = (nib & 3).astype(np.int64)
         i1 = (nib >> 2).astype(np.int64)
-        groups = np.zeros((bn, G, 4), dtype=np.uint16)
+        groups = np.zeros((bn, G, 4), dtype=values.dtype)
         np.put_along_axis(groups, i0[..., None], pairs[..., 0:1], axis=-1)
         np.put_along_axis(groups, i1[..., None], pairs[..., 1:2], axis=-1)
         tiles[t] = groups.reshape(bn, bk)
@@ -292,7 +324,7 @@ def unpack(values: np.ndarray, meta: np.ndarray, index: np.ndarray, N: int, K: i
 # ----------------------------------------------------------------------------
 
 def gemm_ref(X_bits: np.ndarray, Wm_bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Y[M,N] = X . Wm^T in float64 on the exactly widened 16-bit inputs."""
+    """Y[M,N] = X . Wm^T in float64 on the exactly widened inputs."""
     X = widen_f64(X_bits, dtype)
     W = widen_f64(Wm_bits, dtype)
     assert X.shape[1] == W.shape[1]

@@ -39,8 +39,15 @@ PAIRS = list(itertools.combinations(range(4), 2))   # the six 2:4 patterns, lexi
 
 
 def exact_value(bits16, dtype):
-    """Exact rational value of one 16-bit pattern, decoded field by field."""
+    """Exact rational value of one stored pattern, decoded field by field."""
     b = int(bits16)
+    if dtype == "fp8":   # OCP E4M3: s eeee mmm, bias 7, subnormals, 0x7F / 0xFF NaN
+        sign = -1 if b >> 7 else 1
+        e, m = (b >> 3) & 0xF, b & 0x7
+        assert (b & 0x7F) != 0x7F, "finite inputs only"
+        if e == 0:
+            return sign * Fraction(m, 8) * Fraction(2) ** -6
+        return sign * (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
     sign = -1 if b >> 15 else 1
     if dtype == "f16":
         e, m, bias, mb = (b >> 10) & 0x1F, b & 0x3FF, 15, 10
@@ -106,7 +113,8 @@ def brute_mask_and_pack(Wb, dtype, tmap, bn, bk, c=None):
                         word, nword = 0, nword + 1
             voff += bn * bk // 2
             moff += bn * bk // 32
-    return (np.array(Wm, dtype=np.uint16), np.array(values, dtype=np.uint16),
+    st = np.uint8 if dtype == "fp8" else np.uint16
+    return (np.array(Wm, dtype=st), np.array(values, dtype=st),
             np.array(meta, dtype=np.uint32), np.array(index, dtype=np.uint32).reshape(-1, 4))
 
 
@@ -115,7 +123,7 @@ def tie_heavy_bits(shape, dtype, g):
     choices = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 3.0, 0.25], dtype=np.float32)
     x = choices[g.integers(0, len(choices), size=shape)]
     b = wl.to_bits(x, dtype)
-    sub = np.uint16(0x0001 if dtype == "f16" else 0x0001)   # smallest positive subnormal of each format
+    sub = b.dtype.type(0x0001)   # smallest positive subnormal of each format
     flip = g.random(shape) < 0.03
     b[flip] = sub
     return b
@@ -522,3 +530,99 @@ def test_silu_mul_closed_forms():
     three = wl.to_bits(np.full(256, 3.0, np.float32), "bf16")
     assert np.allclose(oracle.silu_mul_ref(x, three, "bf16"), 3.0 * oracle.silu_mul_ref(x, ones, "bf16"),
                        rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# the 8-bit (OCP E4M3) variant
+# ---------------------------------------------------------------------------
+
+def test_e4m3_values_from_the_format_definition():
+    # hand-derived from the field layout s eeee mmm, bias 7
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+             0x3C: 1.5, 0x40: 2.0, 0x44: 3.0, 0x48: 4.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    got = oracle.e4m3_value(np.array(list(table), dtype=np.uint8))
+    assert np.array_equal(got, np.array(list(table.values())))
+    z = oracle.e4m3_value(np.array([0x80], dtype=np.uint8))
+    assert z[0] == 0.0 and np.signbit(z[0])
+    assert np.all(np.isnan(oracle.e4m3_value(np.array([0x7F, 0xFF], dtype=np.uint8))))
+
+
+def test_e4m3_decode_matches_torch_for_every_byte():
+    torch = pytest.importorskip("torch")
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_value(b)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # and the brute force's own field decoder agrees with torch on every finite byte
+    assert all(float(exact_value(int(x), "fp8")) == float(r) for x, r in zip(b[~nan], ref[~nan]))
+
+
+def test_e4m3_rounding_of_the_input_generator_is_nearest():
+    # the generator's rounding picks, for every input, a representable value at the least distance
+    g = np.random.default_rng(5)
+    x = (g.standard_normal(20000) * np.exp(g.uniform(-10, 6, 20000))).astype(np.float32)
+    vals = oracle.e4m3_value(np.arange(256, dtype=np.uint8))
+    finite = np.sort(np.unique(vals[~np.isnan(vals)]))
+    q = oracle.e4m3_value(wl.to_bits(x, "fp8"))
+    xs = np.clip(x.astype(np.float64), -448.0, 448.0)
+    best = np.min(np.abs(finite[None, :] - xs[:, None]), axis=1)
+    assert np.array_equal(np.abs(q - xs), best)
+
+
+def fp8_tie_heavy(shape, g):
+    choices = np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 3.0, 0.25, 448.0, 2.0 ** -9], dtype=np.float32)
+    return wl.to_bits(choices[g.integers(0, len(choices), size=shape)], "fp8")
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("scaled", [False, True])
+def test_brute_force_mask_and_pack_fp8(seed, scaled):
+    g = np.random.default_rng(2000 + seed)
+    N, K, bn, bk = 8, 64, 4, 32
+    W = fp8_tie_heavy((N, K), g) if seed % 2 == 0 else wl.gaussian_bits((N, K), 1.0, "fp8", g)
+    tmap = (g.random((N // bn) * (K // bk)) < 0.6).astype(np.uint8)
+    c = np.array(g.choice([0.0, 0.5, 1.0, 2.0, 3.0, 1.5], size=K), dtype=np.float32) if scaled else None
+    Wm_b, vals_b, meta_b, idx_b = brute_mask_and_pack(W, "fp8", tmap, bn, bk, c)
+    vals, meta, idx = oracle.pack(W, "fp8", tmap, bn, bk, c)
+    assert vals.dtype == np.uint8
+    assert np.array_equal(oracle.masked_weights(W, "fp8", tmap, bn, bk, c), Wm_b)
+    assert np.array_equal(vals, vals_b)
+    assert np.array_equal(meta, meta_b)
+    assert np.array_equal(idx, idx_b)
+    assert np.array_equal(oracle.unpack(vals, meta, idx, N, K, bn, bk), Wm_b)
+
+
+def test_brute_force_product_fp8():
+    g = np.random.default_rng(4)
+    M, N, K, bn, bk = 3, 8, 64, 4, 32
+    X = wl.gaussian_bits((M, K), 1.0, "fp8", g)
+    W = wl.gaussian_bits((N, K), 1.0, "fp8", g)
+    tmap = np.array([0, 1, 1, 0], dtype=np.uint8)
+    Wm_b, *_ = brute_mask_and_pack(W, "fp8", tmap, bn, bk)
+    Y = oracle.hybrid_ref(X, W, "fp8", tmap, bn, bk)
+    for m in range(M):
+        for n in range(N):
+            # products of two E4M3 values have at most 8 significant bits: the fp64 sum is exact
+            exact = sum(exact_value(X[m, k], "fp8") * exact_value(Wm_b[n, k], "fp8") for k in range(K))
+            assert Fraction(Y[m, n]) == exact
+
+
+def test_fp8_packed_sizes_and_invariants():
+    g = np.random.default_rng(9)
+    N, K, bn, bk = 256, 384, 128, 128
+    W = wl.gaussian_bits((N, K), 1.0, "fp8", g)
+    tmap = np.array([1, 0, 1, 1, 0, 0], dtype=np.uint8)
+    vals, meta, idx = oracle.pack(W, "fp8", tmap, bn, bk)
+    _, sizes = oracle.plan(tmap, N, K, bn, bk, elem_bytes=1)
+    assert vals.size == sizes["values"] == sizes["values_bytes"] == 3 * bn * bk // 2 + 3 * bn * bk
+    assert meta.size == 3 * bn * bk // 32
+    nib = (meta[:, None] >> (4 * np.arange(8, dtype=np.uint32))) & np.uint32(0xF)
+    assert set(np.unique(nib).tolist()) <= set(oracle.VALID_NIBBLES)
+    Wm = oracle.masked_weights(W, "fp8", tmap, bn, bk)
+    assert np.array_equal(oracle.unpack(vals, meta, idx, N, K, bn, bk), Wm)
+    t = oracle.as_tiles(Wm, bn, bk)
+    nz = (oracle.e4m3_value(t) != 0).reshape(t.shape[0], bn, bk // 4, 4).sum(-1)
+    assert np.all(nz[tmap == 1] <= 2)

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for the hybrid tile-sparse (dense / 2:4) linear layer.
 
 This module holds NO arithmetic of the method itself: it only draws random
-numbers, rounds them to the 16-bit storage type, and draws tile maps.  Both the
+numbers, rounds them to the storage type (16-bit, or 8-bit E4M3), and draws
+tile maps.  Both the
 CPU oracle (through the tests) and the GPU library (through the tests, the
 benchmark and the smoke check) take their inputs from here, so neither side
 ever supplies inputs to the other.
@@ -25,7 +26,7 @@ import numpy as np
 
 TAG_X, TAG_W, TAG_MAP, TAG_CALIB, TAG_OUTLIER = 0, 1, 2, 3, 4
 
-F16, BF16 = "f16", "bf16"
+F16, BF16, FP8 = "f16", "bf16", "fp8"
 
 
 def rng(cfg_id: int, layer_id: int, tag: int, extra: Sequence[int] = ()) -> np.random.Generator:
@@ -45,16 +46,36 @@ def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to OCP E4M3 (round to nearest, ties to even; magnitudes past
+    448, the largest finite value, saturate to 448); returns uint8 bits."""
+    a64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    neg = np.signbit(a64)
+    a = np.minimum(np.abs(a64), 448.0)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))            # a = f * 2^ex with f in [0.5, 1)
+    q = np.ldexp(1.0, ex - 1 - 3)                          # spacing of the 3-bit mantissa at a
+    r = np.minimum(np.round(a / q) * q, 448.0)             # numpy rounds halves to even
+    _, er = np.frexp(np.maximum(r, 2.0 ** -6))
+    e = er - 1                                             # exponent of r (at least -6)
+    sub = r < 2.0 ** -6
+    m = np.where(sub, r * 2.0 ** 9, (np.ldexp(r, -e) - 1.0) * 8.0)
+    ebits = np.where(sub, 0, e + 7)
+    bits = (neg.astype(np.int64) << 7) | (ebits.astype(np.int64) << 3) | np.round(m).astype(np.int64)
+    return bits.astype(np.uint8)
+
+
 def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == BF16:
         return f32_to_bf16_bits(x)
     if dtype == F16:
         return f32_to_f16_bits(x)
+    if dtype == FP8:
+        return f32_to_e4m3_bits(x)
     raise ValueError(dtype)
 
 
 def gaussian_bits(shape: Tuple[int, ...], sigma: float, dtype: str, g: np.random.Generator) -> np.ndarray:
-    """N(0, sigma^2) drawn in float32 and rounded to the 16-bit type (uint16 bit patterns)."""
+    """N(0, sigma^2) drawn in float32 and rounded to the storage type (uint16 or uint8 bits)."""
     x = g.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma)
     return to_bits(x, dtype)
 

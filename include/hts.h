@@ -54,13 +54,20 @@ typedef enum {
     HTS_ERR_HIP = 8            /* the HIP runtime reported an error (launch failure, no device) */
 } hts_status;
 
-typedef enum { HTS_F16 = 0, HTS_BF16 = 1, HTS_F32 = 2 } hts_dtype;
+/* HTS_FP8_E4M3: the 8-bit OCP E4M3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, no infinities; 0x7F and 0xFF are NaN, whose products are unspecified).  It serves
+ * the prune-then-quantize combination (page "SparseGPT vs Wanda: one-shot LLM pruning without
+ * retraining", FAQ: pruning combines with low-precision weights): W and X both 8-bit, products
+ * on the 8-bit matrix instructions with fp32 accumulation, 128x128 tiles only.  Y is written as
+ * HTS_F32, HTS_F16 or HTS_BF16.  The Wanda helpers and hts_silu_mul stay 16-bit. */
+typedef enum { HTS_F16 = 0, HTS_BF16 = 1, HTS_F32 = 2, HTS_FP8_E4M3 = 3 } hts_dtype;
 
 enum { HTS_TILE_DENSE = 0, HTS_TILE_SPARSE24 = 1 };
 
-/* Shape of a tiled weight.  dtype is HTS_F16 or HTS_BF16 (W and X share it).
- * bn, bk in {64, 128}; N % bn == 0 and K % bk == 0 (tiles cover W exactly);
- * N*K < 2^32. */
+/* Shape of a tiled weight.  dtype is HTS_F16, HTS_BF16 or HTS_FP8_E4M3 (W and X share it).
+ * bn, bk in {64, 128} (both 128 for HTS_FP8_E4M3); N % bn == 0 and K % bk == 0 (tiles cover W
+ * exactly); N*K < 2^32.  Element sizes: 2 bytes, 1 byte for HTS_FP8_E4M3; leading dimensions
+ * (in elements) must be multiples of 8, of 16 for HTS_FP8_E4M3 (16 bytes either way). */
 typedef struct {
     int64_t N, K;
     int32_t bn, bk;
@@ -69,7 +76,7 @@ typedef struct {
 } hts_desc;
 
 /* One record per tile, tiles in row-major tile order t = tn*(K/bk) + tk.
- *   val_off  : first element of the tile in `values` (16-bit elements)
+ *   val_off  : first element of the tile in `values` (elements of the weight's type)
  *   meta_off : first 32-bit word of the tile in `meta` (sparse tiles only; for a
  *              dense tile it equals the next sparse tile's offset)
  *   type     : HTS_TILE_DENSE or HTS_TILE_SPARSE24

@@ -48,12 +48,12 @@ def _maps():
     return out
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(len(_maps())))
 def test_plan_matches_oracle(case):
     L, m = _maps()[case]
     desc = hts.make_desc(L.N, L.K, L.bn, L.bk, L.dtype)
     index, sizes = hts.hts_pack_plan(desc, m)
-    o_index, o_sizes = oracle.plan(m, L.N, L.K, L.bn, L.bk)
+    o_index, o_sizes = oracle.plan(m, L.N, L.K, L.bn, L.bk, elem_bytes=1 if L.dtype == "fp8" else 2)
     assert np.array_equal(index, o_index)
     assert sizes["values_bytes"] == o_sizes["values_bytes"]
     assert sizes["meta_bytes"] == o_sizes["meta_bytes"]
@@ -161,3 +161,27 @@ def test_silu_mul_rejects_bad_arguments():
     assert L.hts_silu_mul(1, 4, 64, A8, 64, A16, 64, A16, 64, None) == 4        # alignment
     assert L.hts_silu_mul(1, 4, 64, None, 64, A16, 64, A16, 64, None) == 1      # null
     assert L.hts_silu_mul(1, 0, 64, None, 64, None, 64, None, 64, None) == 0    # M == 0: nothing to do
+
+
+def test_fp8_arguments():
+    L = hts.lib()
+    by = ctypes.byref
+    # 8-bit weights take 128x128 tiles only, and sizes count one byte per element
+    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 64, 64, "fp8"), np.zeros(16, np.uint8))) == 7
+    m = np.array([1, 0, 0, 1], np.uint8)
+    idx, sz = hts.hts_pack_plan(hts.make_desc(256, 256, 128, 128, "fp8"), m)
+    assert np.array_equal(idx, oracle.plan(m, 256, 256, 128, 128, elem_bytes=1)[0])
+    assert sz["values_bytes"] == 256 * 256 - 2 * 128 * 128 // 2
+    assert sz["meta_bytes"] == 2 * 128 * 128 // 8
+    d = hts.make_desc(256, 256, 128, 128, "fp8")
+    # leading dimensions are whole 16-byte chunks: multiples of 16 one-byte elements
+    assert L.hts_pack(by(d), A16, A16, 264, None, A16, A16, None) == 4
+    assert L.hts_unpack(by(d), A16, A16, A16, A16, 264, None) == 4
+    assert L.hts_gemm(by(d), A16, A16, A16, 4, A16, 264, A16, 256, 2, None, 0, None) == 4
+    assert L.hts_gemm(by(d), A16, A16, A16, 4, A16, 256, A16, 256, 3, None, 0, None) == 2   # Y is never 8-bit
+    # the Wanda helpers stay 16-bit
+    assert L.hts_wanda_tile_cost(by(d), A16, 256, A16, A16, None) == 2
+    assert L.hts_col_norms(3, 4, 256, A16, 256, A16, None) == 2
+    # the 8-bit dense product needs N and K in whole 128-wide tiles
+    assert L.hts_dense_gemm(3, 4, 192, 256, A16, 256, A16, 256, A16, 256, 2, None, 0, None) == 3
+    assert L.hts_dense_gemm(3, 0, 256, 256, A16, 256, A16, 256, A16, 256, 2, None, 0, None) == 0

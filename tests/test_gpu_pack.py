@@ -151,7 +151,7 @@ def _check_masked(W, dtype, tmap, mask_np, bn, bk, ldm_pad=0):
     return pw
 
 
-@pytest.mark.parametrize("name", ["tiny/tiny", "7b_up/up_proj", "13b/sq_5120", "sweep/sweep_p0.5"])
+@pytest.mark.parametrize("name", ["tiny/tiny", "7b_up/up_proj", "13b/sq_5120", "sweep/sweep_p0.5", "7b_up_fp8/up_proj_fp8"])
 def test_pack_masked_named_layers(name):
     cname, lname = name.split("/")
     c = wl.config(cname)

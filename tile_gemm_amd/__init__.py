@@ -23,7 +23,7 @@ import torch  # loads the HIP runtime that libhts binds to (same soname)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhts.so")
 
-HTS_F16, HTS_BF16, HTS_F32 = 0, 1, 2
+HTS_F16, HTS_BF16, HTS_F32, HTS_FP8_E4M3 = 0, 1, 2, 3
 HTS_TILE_DENSE, HTS_TILE_SPARSE24 = 0, 1
 STATUS_NAMES = {0: "HTS_OK", 1: "HTS_ERR_INVALID_ARG", 2: "HTS_ERR_DTYPE", 3: "HTS_ERR_SHAPE",
                 4: "HTS_ERR_ALIGN", 5: "HTS_ERR_MAP", 6: "HTS_ERR_WORKSPACE", 7: "HTS_ERR_UNSUPPORTED",
@@ -94,14 +94,16 @@ def _check(status: int) -> None:
 
 def _dt(t) -> int:
     m = {torch.float16: HTS_F16, torch.bfloat16: HTS_BF16, torch.float32: HTS_F32,
-         "f16": HTS_F16, "bf16": HTS_BF16, "f32": HTS_F32}
+         torch.float8_e4m3fn: HTS_FP8_E4M3,
+         "f16": HTS_F16, "bf16": HTS_BF16, "f32": HTS_F32, "fp8": HTS_FP8_E4M3}
     if t not in m:
         raise HTSError(2, f"unsupported element type {t}")
     return m[t]
 
 
 def _torch_dt(code: int):
-    return {HTS_F16: torch.float16, HTS_BF16: torch.bfloat16, HTS_F32: torch.float32}[code]
+    return {HTS_F16: torch.float16, HTS_BF16: torch.bfloat16, HTS_F32: torch.float32,
+            HTS_FP8_E4M3: torch.float8_e4m3fn}[code]
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -247,14 +249,18 @@ class PackedWeight:
 def _device_buffers(desc: hts_desc, tile_map: np.ndarray, device):
     index_np, sizes = hts_pack_plan(desc, tile_map)
     index = torch.from_numpy(index_np.view(np.int32).copy()).to(device)
-    values = torch.empty(max(sizes["values_bytes"] // 2, 8), dtype=torch.int16, device=device)
+    if desc.dtype == HTS_FP8_E4M3:
+        values = torch.empty(max(sizes["values_bytes"], 16), dtype=torch.uint8, device=device)
+    else:
+        values = torch.empty(max(sizes["values_bytes"] // 2, 8), dtype=torch.int16, device=device)
     meta = torch.empty(max(sizes["meta_bytes"] // 4, 4), dtype=torch.int32, device=device)
     return index, values, meta, sizes
 
 
 def pack(W: torch.Tensor, tile_map: np.ndarray, bn: int, bk: int,
          col_scale: Optional[torch.Tensor] = None, stream=None) -> PackedWeight:
-    """Pack a row-major 16-bit W[N,K] on the GPU under a host tile map (uint8, row-major tiles)."""
+    """Pack a row-major W[N,K] (16-bit, or 8-bit E4M3) on the GPU under a host tile map (uint8,
+    row-major tiles)."""
     N, K = W.shape
     desc = make_desc(N, K, bn, bk, W.dtype)
     index, values, meta, sizes = _device_buffers(desc, tile_map, W.device)
@@ -290,16 +296,21 @@ def gemm(X: torch.Tensor, pw: PackedWeight, out_dtype=None, out: Optional[torch.
     """Y[M,N] = X[M,K] . mask(W)^T from the packed weight (fp32 accumulation)."""
     M = X.shape[0]
     if out is None:
-        out = torch.empty((M, pw.N), dtype=out_dtype or X.dtype, device=X.device)
+        out = torch.empty((M, pw.N), dtype=out_dtype or _default_out(X.dtype), device=X.device)
     hts_gemm(pw.desc, pw.index, pw.values, pw.meta, X, out, stream=stream)
     return out
+
+
+def _default_out(dt):
+    """Output type when none is given: the input type, fp32 for 8-bit inputs."""
+    return torch.float32 if dt == torch.float8_e4m3fn else dt
 
 
 def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype=None, out: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     """The same-library dense product Y = X . W^T (no tile index)."""
     if out is None:
-        out = torch.empty((X.shape[0], W.shape[0]), dtype=out_dtype or X.dtype, device=X.device)
+        out = torch.empty((X.shape[0], W.shape[0]), dtype=out_dtype or _default_out(X.dtype), device=X.device)
     hts_dense_gemm(X, W, out, stream=stream)
     return out
 
@@ -344,10 +355,14 @@ def wanda_global_maps(Ws, col_scales, bn: int, bk: int, n_sparse: int, stream=No
 
 
 def tensor_from_bits(bits: np.ndarray, dtype: str, device) -> torch.Tensor:
-    """A 16-bit torch tensor holding exactly these bit patterns."""
+    """A torch tensor (16-bit, or float8_e4m3fn for "fp8") holding exactly these bit patterns."""
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).view(torch.float8_e4m3fn).to(device)
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
     return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(device)
 
 
 def bits_from_tensor(t: torch.Tensor) -> np.ndarray:
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return t.detach().contiguous().view(torch.uint8).cpu().numpy()
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

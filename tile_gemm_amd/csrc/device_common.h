@@ -82,6 +82,56 @@ __device__ __forceinline__ f32x4 mfma_sparse<F16T, 1>(u32x4 a, u32x8 b, uint32_t
                                                    __builtin_bit_cast(f16x16, b), c, (int)idx, 0, 1);
 }
 
+// ---- 8-bit OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits) ----
+struct FP8T { static constexpr int id = 3; };
+
+// Exact value of one E4M3 byte (every E4M3 value is a binary32 value); the NaN patterns 0x7F /
+// 0xFF decode as 480 -- their products are unspecified.
+__device__ __forceinline__ float widen_e4m3(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -mag : mag;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Dense 16x16x32 8-bit MFMA (E4M3 x E4M3): lane (i + 16g) holds 8 values of row i of A for the
+// instruction's k slot g, B lane (j + 16q) the 8 values of column j for slot q.  Any one k order
+// shared by A and B gives the same product, so the data keeps the chunk layout of the sparse
+// 16x16x128 instruction below (lane group g: 16-byte chunks g and 4 + g of a 128-byte row) and
+// each 16-byte chunk feeds two of these instructions, one per 8-byte half: every k is used once.
+// (The 16x16x128 dense form, with unit block scales, gave wrong sums on gfx950 when its
+// accumulator was copied between dependent products, so it is not used.)
+__device__ __forceinline__ f32x4 mfma_fp8_dense32(uint2 a, uint2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)__builtin_bit_cast(uint64_t, a),
+                                                      (long)__builtin_bit_cast(uint64_t, b), c, 0, 0, 0);
+}
+// One 16-byte chunk per lane group of A and B: two 8-bit 16x16x32 products.
+template <>
+__device__ __forceinline__ f32x4 mfma_dense<FP8T>(u32x4 a, u32x4 b, f32x4 c) {
+    c = mfma_fp8_dense32(uint2{a[0], a[1]}, uint2{b[0], b[1]}, c);
+    return mfma_fp8_dense32(uint2{a[2], a[3]}, uint2{b[2], b[3]}, c);
+}
+
+// Sparse 16x16x128 8-bit SMFMAC: A lane (i + 16h) holds the 16 stored values of row i for dense
+// k in [32h, 32h+32): value v belongs to group v/2 at position 4*(v/2) + idx_v, idx_v = bits
+// [2v+1:2v] of the whole 32-bit index.  B lane (j + 16q) holds B[16q+e][j] for e < 16 and
+// B[64+16q+(e-16)][j] for e >= 16.  (Lane layouts measured on gfx950 with random small-integer
+// operands against every candidate order.)
+__device__ __forceinline__ f32x4 mfma_fp8_sparse(u32x4 a, u32x8 b, uint32_t idx, f32x4 c) {
+    return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x8, b), c,
+                                                        (int)idx, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma_sparse<FP8T, 0>(u32x4 a, u32x8 b, uint32_t idx, f32x4 c) {
+    return mfma_fp8_sparse(a, b, idx, c);
+}
+
+// Bytes per element and K elements per 128-byte row slice of the tiled kernels.
+template <typename T> struct Elem { static constexpr int bytes = 2; };
+template <> struct Elem<FP8T> { static constexpr int bytes = 1; };
+
 __device__ __forceinline__ u32x4 lo4(u32x8 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
 __device__ __forceinline__ u32x4 hi4(u32x8 v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
 __device__ __forceinline__ u32x8 cat8(u32x4 a, u32x4 b) {

@@ -189,9 +189,144 @@ hipError_t launch2(const GemmArgs& a, int ksplit, int nt, int pp, int sp, hipStr
     return hyb ? launch3<T, 64, true>(a, ksplit, nt, pp, sp, s) : launch3<T, 64, false>(a, ksplit, nt, pp, sp, s);
 }
 
+// ---------------------------------------------------------------------------------------
+// 8-bit (E4M3) weights and activations, 128x128 tiles.  Same schedule as above; a tile of a
+// 16-row panel is one 16x16x128 instruction.  Lane L = i + 16g (weights: row i; X: row j = i):
+//   dense tile: bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the 128-byte tile row, and the
+//               same bytes of the X row's 128-byte tile column
+//   2:4 tile  : stored bytes [16g, 16g+16) of the 64-byte tile row (dense k in [32g, 32g+32))
+//               and code word g of the row's four words -- exactly the sparse instruction's A
+//               operand and index; X as for a dense tile.
+template <int PP>
+struct TileRegs8 {
+    u32x4 a[PP][2];   // per panel: dense: the two chunks; 2:4: a[q][0] = 16 stored bytes
+    uint32_t m[PP];   // per panel: 2:4 code word
+    u32x4 x[2];       // X chunks, shared by the PP panels
+};
+
+template <bool HYB, int PP>
+__device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs& a, int64_t t0, int tk, int64_t n0,
+                                               int r0, int lane, const uint8_t* xrow) {
+    const int i = lane & 15, g = lane >> 4;
+    uint32_t type = HTS_TILE_DENSE;
+    const uint8_t* base;
+    int64_t rstride;
+    uint32_t moff = 0;
+    if (HYB) {
+        const hts_tile e = a.index[t0 + tk];   // uniform: scalar load
+        type = e.type;
+        moff = e.meta_off;
+        rstride = type == HTS_TILE_DENSE ? 128 : 64;
+        base = reinterpret_cast<const uint8_t*>(a.values) + e.val_off + (int64_t)(r0 + i) * rstride;
+    } else {
+        rstride = a.ldw;
+        base = reinterpret_cast<const uint8_t*>(a.W) + (n0 + i) * a.ldw + (int64_t)tk * 128;
+    }
+    if (type == HTS_TILE_DENSE) {
+#pragma unroll
+        for (int q = 0; q < PP; ++q) {
+            R.a[q][0] = ld16(base + 16 * q * rstride + 16 * g);
+            R.a[q][1] = ld16(base + 16 * q * rstride + 64 + 16 * g);
+        }
+    } else {
+        const uint32_t* mrow = a.meta + moff + (int64_t)(r0 + i) * 4;
+#pragma unroll
+        for (int q = 0; q < PP; ++q) R.a[q][0] = ld16(base + 16 * q * rstride + 16 * g);
+#pragma unroll
+        for (int q = 0; q < PP; ++q) R.m[q] = mrow[64 * q + g];
+    }
+    R.x[0] = ld16(xrow + (int64_t)tk * 128 + 16 * g);
+    R.x[1] = ld16(xrow + (int64_t)tk * 128 + 64 + 16 * g);
+    return type;
+}
+
+template <int PP>
+__device__ __forceinline__ void mma_tile8(const TileRegs8<PP>& R, uint32_t type, f32x4 (&acc)[PP]) {
+    const u32x8 xb = cat8(R.x[0], R.x[1]);
+    if (type == HTS_TILE_DENSE) {
+#pragma unroll
+        for (int q = 0; q < PP; ++q) {
+            acc[q] = mfma_dense<FP8T>(R.a[q][0], R.x[0], acc[q]);
+            acc[q] = mfma_dense<FP8T>(R.a[q][1], R.x[1], acc[q]);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < PP; ++q) acc[q] = mfma_fp8_sparse(R.a[q][0], xb, R.m[q], acc[q]);
+    }
+}
+
+template <bool HYB, int KS, int NT, int PP>
+__global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t P = gridDim.x, b = blockIdx.x, x = b & 7u, q = P >> 3, r = P & 7u;
+    const int64_t n0 = (int64_t)(x * q + (x < r ? x : r) + (b >> 3)) * 16 * PP;
+    const int64_t tn = n0 / a.bn;
+    const int r0 = (int)(n0 - tn * a.bn);
+    const int Tk = (int)(a.K / 128);
+    const int64_t t0 = tn * Tk;
+    const int kb = Tk * wave / KS, ke = Tk * (wave + 1) / KS;
+
+    const int i = lane & 15;
+    const int64_t j = i < a.M ? i : a.M - 1;
+    const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.X) + j * a.ldx;
+    f32x4 acc[PP];
+#pragma unroll
+    for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = kb; t < ke; t += NT) {
+        TileRegs8<PP> R[NT];
+        uint32_t type[NT];
+#pragma unroll
+        for (int s = 0; s < NT; ++s)
+            if (t + s < ke) type[s] = load_tile8<HYB, PP>(R[s], a, t0, t + s, n0, r0, lane, xrow);
+#pragma unroll
+        for (int s = 0; s < NT; ++s)
+            if (t + s < ke) mma_tile8<PP>(R[s], type[s], acc);
+    }
+
+    __shared__ f32x4 red[KS][PP][64];
+#pragma unroll
+    for (int q2 = 0; q2 < PP; ++q2) red[wave][q2][lane] = acc[q2];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 256 * PP; o += 64 * KS) {
+        const int q2 = o >> 8, m = (o >> 4) & 15, rr = o & 15;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < KS; ++w) sum += red[w][q2][m + 16 * (rr >> 2)][rr & 3];
+        if (m < a.M) store_y1(a.Y, (int64_t)m * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
+    }
+}
+
+template <bool HYB, int KS, int PP>
+hipError_t launch8_nt(const GemmArgs& a, int nt, hipStream_t s) {
+    const dim3 grid((unsigned)(a.N / (16 * PP))), block(64 * KS);
+    // nt counts 16-bit 128x128 tile columns; an 8-bit tile column is half the bytes
+    if constexpr (KS < 16 && PP == 1) {
+        if (nt >= 4) {
+            gemm_decode8_kernel<HYB, KS, 8, PP><<<grid, block, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
+    gemm_decode8_kernel<HYB, KS, 4, PP><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <bool HYB>
+hipError_t launch8(const GemmArgs& a, int ksplit, int nt, int pp, hipStream_t s) {
+    if (pp == 2) {
+        if (ksplit >= 8) return launch8_nt<HYB, 8, 2>(a, nt, s);
+        return launch8_nt<HYB, 4, 2>(a, nt, s);
+    }
+    if (ksplit >= 16) return launch8_nt<HYB, 16, 1>(a, nt, s);
+    if (ksplit >= 8) return launch8_nt<HYB, 8, 1>(a, nt, s);
+    return launch8_nt<HYB, 4, 1>(a, nt, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s) {
+    if (a.dtype == HTS_FP8_E4M3)   // 8-bit: the sparse instruction only (no expansion fallback)
+        return a.index ? launch8<true>(a, ksplit, nt, pp, s) : launch8<false>(a, ksplit, nt, pp, s);
     return a.dtype == HTS_BF16 ? launch2<BF16T>(a, ksplit, nt, pp, sparse_path, s)
                                : launch2<F16T>(a, ksplit, nt, pp, sparse_path, s);
 }

@@ -26,9 +26,14 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_t;
 
-constexpr int kKS = 64;                 // K elements per slice
+constexpr int kKS = 64;                 // K elements per slice (16-bit elements: 128 bytes per row)
 constexpr int kGroupBytes = 64 * 128;   // one 64-row weight group, dense (2:4 uses half)
-constexpr int kMetaGroupBytes = 64 * 8; // codes of one 64-row group for one slice
+constexpr int kMetaGroupBytes = 64 * 8; // codes of one 64-row group for one slice (16-bit elements)
+// The single-tile-row kernel also takes 8-bit elements: a slice is always 128 bytes of every
+// row (64 16-bit or 128 8-bit elements), so the LDS image of X and of the weights is the same;
+// only the codes grow, to 16 bytes per row and slice.
+template <int ES> constexpr int slice_k() { return 128 / ES; }
+template <int ES> constexpr int meta_group_bytes() { return 64 * slice_k<ES>() / 8; }
 constexpr int kMaxTileCols = 256;       // K/bk limit: the tile list of a tile row is kept in LDS
 constexpr int kGroupN = 8;
 
@@ -60,12 +65,12 @@ __device__ __forceinline__ void block_of(int L, int NB, int MB, int ord, int& nb
 }
 
 // LDS image of one stage: X slice (BM rows x 128 B), BN/64 weight groups, their codes.
-template <int BN, int BM, int NSTAGE>
+template <int BN, int BM, int NSTAGE, int MGB = kMetaGroupBytes>
 struct Layout {
     static constexpr int NG = BN / 64;
     static constexpr int WOFF = BM * 128;
     static constexpr int MOFF = WOFF + NG * kGroupBytes;
-    static constexpr int STAGE = MOFF + NG * kMetaGroupBytes;
+    static constexpr int STAGE = MOFF + NG * MGB;
     static constexpr int SINK = NSTAGE * STAGE;              // target of the padding copies
     static constexpr int LIST = SINK + 1024;                 // ordered tile list: {val_off, meta_off}
     static constexpr int LCOL = LIST + kMaxTileCols * 8;     // ... and the tile column of each entry
@@ -108,9 +113,6 @@ struct Ctx {
     static constexpr int NG = BN / 64;
     static constexpr int JPG = 8 / NW;  // copy jobs per 64-row group per wave
     static constexpr int XJ = BM / (8 * NW);  // X copy jobs per wave
-    const uint16_t* values;
-    const uint32_t* meta;
-    const uint16_t* W;          // row-major weight (dense product), row n0
     int64_t ldw;
     int64_t N, n0;
     int r0;                     // first row of the block inside its tile (0 when BN == bn)
@@ -131,7 +133,8 @@ struct Ctx {
     uint32_t dvo[JPG];                  // dense group jobs (row * BK + chunk, or row * ldw + chunk)
     uint32_t svo;                       // 2:4 values job
     uint32_t mvo;                       // 2:4 codes job
-    bool meta_to_sink;                  // codes jobs 2, 3 repeat jobs 0, 1 into the sink
+    bool meta_to_sink;                  // a codes job past the codes of a slice repeats one into the sink
+    int mjob;                           // this wave's codes job (256 bytes each)
     __device__ __forceinline__ bool gvalid(int gi) const { return n0 + 64 * gi < N; }
     __device__ __forceinline__ void shift_list() {
 #pragma unroll
@@ -155,11 +158,12 @@ __device__ __forceinline__ uint32_t list_entry(const uint32_t (&r)[4], int p) {
 // of the codes into a sink.  Each of the NW waves issues BM/(8 NW) X copies and 8/NW copies per
 // group for every slice, whatever the tile types, so the wait for one slice is a fixed count
 // of outstanding copies.  KIND (dense / 2:4) is known at compile time: no branch per copy.
-template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW>
+template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW, int ES = 2>
 __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, int ks, uint32_t stage) {
     constexpr int JPG = 8 / NW;
-    using Lo = Layout<BN, BM, NSTAGE>;
-    constexpr int SPT = BK / kKS;
+    constexpr int KSL = slice_k<ES>(), MGB = meta_group_bytes<ES>();
+    using Lo = Layout<BN, BM, NSTAGE, MGB>;
+    constexpr int SPT = BK / KSL;
     const int p = ks / SPT, s = ks % SPT;     // list position, slice of the tile
     // read the list entry before any copy is issued: an LDS read after a copy into LDS makes
     // the compiler wait for every copy in flight
@@ -177,24 +181,25 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
 #pragma unroll
             for (int v = 0; v < JPG; ++v)
                 buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v],
-                      (uint32_t)(2 * (64 * gi * C.ldw + (int64_t)ks * kKS)));
+                      (uint32_t)(ES * 64 * gi * C.ldw + 128 * (int64_t)ks));
             continue;
         }
         const uint32_t r = 64 * gi;             // a block is one tile row: groups at rows 0, 64
         if (DENSE) {
-            const uint32_t so = 2 * (voff - C.vbase + r * BK + s * kKS);
+            const uint32_t so = ES * (voff - C.vbase + r * BK) + 128 * s;
 #pragma unroll
             for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
         } else {
-            // jobs 0-3: stored values; 4, 5: codes; 6, 7: the codes again into the sink.  With 4
-            // waves wave w does jobs w and 4 + w, with 8 waves job w.
+            // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
+            // codes, then the same two again into the sink).  With 4 waves wave w does jobs w and
+            // 4 + w, with 8 waves job w.
             if (NW == 4 || C.wave < 4)
-                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, 2 * (voff - C.vbase + r * (BK / 2) + s * (kKS / 2)));
+                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 64 * s);
             if (NW == 4 || C.wave >= 4)
                 buf4(C.mr,
                      C.meta_to_sink ? (uint32_t)Lo::SINK
-                                    : stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * (C.wave & 1),
-                     C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + 2 * s));
+                                    : stage + Lo::MOFF + gi * MGB + 256 * C.mjob,
+                     C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
         }
     }
 }
@@ -266,14 +271,16 @@ __device__ __forceinline__ void compute_sparse(f32x4 (&acc)[NBI][NBJ], const uin
 #pragma unroll
     for (int h = 0; h < NBI / 4; ++h) {
         const uint8_t* wg = ws + h * kGroupBytes;
-        const uint32_t* mg = ms + h * (kMetaGroupBytes / 4);
+        const uint32_t* mg = ms + h * (meta_group_bytes<Elem<T>::bytes>() / 4);
         if (SP == SPARSE_SMFMAC) {
             u32x4 A[4];
             uint32_t idx[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 A[b] = ld16(wg + b * 1024 + s0);
-                idx[b] = mg[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1));
+                // 16-bit: a 16-bit half of the row's word g/2; 8-bit: the row's whole word g
+                idx[b] = Elem<T>::bytes == 1 ? mg[4 * (16 * b + i) + g]
+                                             : mg[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1));
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b)
@@ -321,9 +328,10 @@ __device__ __forceinline__ void wait_slice(int later) {
 
 template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord) {
-    using Lo = Layout<BN, BM, NSTAGE>;
+    constexpr int ES = Elem<T>::bytes, KSL = slice_k<ES>(), MGB = meta_group_bytes<ES>();
+    using Lo = Layout<BN, BM, NSTAGE, MGB>;
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-    constexpr int NG = BN / 64, WM = NW / NG, WTM = BM / WM, NBJ = WTM / 16, SPT = BK / kKS;
+    constexpr int NG = BN / 64, WM = NW / NG, WTM = BM / WM, NBJ = WTM / 16, SPT = BK / KSL;
     static_assert(NBJ >= 1 && BM % (8 * NW) == 0 && 2 * NW <= 16, "block shape");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -334,12 +342,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     block_of(blockIdx.x, NB, MB, ord, nb, mb);
 
     Ctx<BK, HYB, BN, BM, NW> C;
-    C.values = a.values;
-    C.meta = a.meta;
     C.ldw = a.ldw;
     C.N = a.N;
     C.n0 = (int64_t)nb * BN;
-    C.W = HYB ? nullptr : a.W + C.n0 * a.ldw;
     C.r0 = 0;
     C.wave = wave;
     C.lane = lane;
@@ -348,29 +353,38 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     // copy sources: X rows m0 .. M-1 (rows past M read zeros and feed only unstored outputs);
     // the packed tile row from its first tile (offsets within a tile row fit 32 bits: K/bk <= 256
     // tiles of at most 32 KiB), or W rows n0 .. N-1 of the dense product
-    C.xr = make_rsrc(a.X + m0 * a.ldx, (uint64_t)(a.M - m0) * a.ldx * 2);
+    // (byte addresses: the element pointers of GemmArgs are 16-bit typed, elements are ES bytes)
+    const uint8_t* Xb = reinterpret_cast<const uint8_t*>(a.X);
+    const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.values);
+    const uint8_t* Wb = reinterpret_cast<const uint8_t*>(a.W);
+    C.xr = make_rsrc(Xb + ES * m0 * a.ldx, (uint64_t)(a.M - m0) * a.ldx * ES);
     if (HYB) {
         const hts_tile first = a.index[(C.n0 / a.bn) * C.Tk];
         C.vbase = first.val_off;
         C.mbase = first.meta_off;
-        C.wr = make_rsrc(a.values + C.vbase, (uint64_t)C.Tk * BN * BK * 2);
+        C.wr = make_rsrc(Vb + (uint64_t)ES * C.vbase, (uint64_t)C.Tk * BN * BK * ES);
         C.mr = make_rsrc(a.meta + C.mbase, (uint64_t)C.Tk * BN * BK / 8);
     } else {
         C.vbase = C.mbase = 0;
-        C.wr = make_rsrc(a.W + C.n0 * a.ldw, (uint64_t)(a.N - C.n0) * a.ldw * 2);
+        C.wr = make_rsrc(Wb + ES * C.n0 * a.ldw, (uint64_t)(a.N - C.n0) * a.ldw * ES);
         C.mr = C.wr;
     }
     C.xso = 0;
     for (int v = 0; v < 8 / NW; ++v) {
         const int row = 8 * (wave + NW * v) + (lane >> 3), col = (lane & 7) ^ ((row >> 1) & 7);
-        C.dvo[v] = HYB ? (uint32_t)(2 * (row * BK + 8 * col)) : (uint32_t)(2 * ((int64_t)row * a.ldw + 8 * col));
+        C.dvo[v] = HYB ? (uint32_t)(ES * row * BK + 16 * col) : (uint32_t)(ES * (int64_t)row * a.ldw + 16 * col);
     }
     {
         const int row = 16 * (wave & 3) + (lane >> 2), col = (lane & 3) ^ ((row >> 2) & 3);
-        C.svo = (uint32_t)(2 * (row * (BK / 2) + 8 * col));
-        const int wi = 64 * (wave & 1) + lane;
-        C.mvo = (uint32_t)(4 * ((wi >> 1) * (BK / 32) + (wi & 1)));
-        C.meta_to_sink = (NW == 4) ? wave >= 2 : wave >= 6;
+        C.svo = (uint32_t)(ES * row * (BK / 2) + 16 * col);
+        // codes jobs of 256 bytes: 64 rows x (KSL / 32) words per slice; job j covers words
+        // 64 j .. 64 j + 63 of that row-major block
+        constexpr int WPR = KSL / 32, NCJ = MGB / 256;
+        const int cj = ((NW == 4) ? wave : wave - 4) & 3;  // this wave's codes job 0..3
+        C.mjob = cj % NCJ;
+        const int wi = 64 * C.mjob + lane;
+        C.mvo = (uint32_t)(4 * ((wi / WPR) * (BK / 32) + (wi % WPR)));
+        C.meta_to_sink = cj >= NCJ;
     }
     // ordered tile list of the tile row (dense first), tile columns kept for the X copies
     uint2* list = reinterpret_cast<uint2*>(smem + Lo::LIST);
@@ -427,12 +441,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     for (int v = 0; v < XJ; ++v) {
         const int row = 8 * (wave + NW * v) + (lane >> 3);
         const int xc = (lane & 7) ^ ((row >> 1) & 7);
-        C.xvo[v] = (uint32_t)(2 * ((int64_t)row * a.ldx + 8 * xc));
+        C.xvo[v] = (uint32_t)(ES * (int64_t)row * a.ldx + 16 * xc);
     }
     auto set_x = [&](int ks) {
         const int p = ks / SPT, s = ks % SPT;
         const int tk = HYB ? (int)list_entry(C.lc, p) : p;
-        C.xso = (uint32_t)(2 * (tk * BK + s * kKS));
+        C.xso = (uint32_t)(ES * tk * BK + 128 * s);
     };
 
     f32x4 acc[4][NBJ];
@@ -449,8 +463,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         if (HYB && kn > 0 && kn % (64 * SPT) == 0) C.shift_list();
         set_x(kn);
         const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
-        if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW>(C, kn, stage);
-        else issue_slice<BK, HYB, BN, BM, NSTAGE, false, NW>(C, kn, stage);
+        if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW, ES>(C, kn, stage);
+        else issue_slice<BK, HYB, BN, BM, NSTAGE, false, NW, ES>(C, kn, stage);
     };
     // prologue: slices 0 .. NSTAGE-2 in flight
 #pragma unroll
@@ -474,7 +488,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
             const uint8_t* st = step(ks);
             if (wvalid)
                 compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
-                                           reinterpret_cast<const uint32_t*>(st + Lo::MOFF + wn * kMetaGroupBytes), lane);
+                                           reinterpret_cast<const uint32_t*>(st + Lo::MOFF + wn * MGB), lane);
         }
     }
 
@@ -786,7 +800,7 @@ hipError_t launch_pair(const GemmArgs& a, hipStream_t s) {
 
 template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW = 4>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
-    using Lo = Layout<BN, BM, NSTAGE>;
+    using Lo = Layout<BN, BM, NSTAGE, meta_group_bytes<Elem<T>::bytes>()>;
     auto kern = gemm_prefill_kernel<T, BK, HYB, SP, BN, BM, NSTAGE, NW>;
     static bool attr_set = false;   // per instantiation; raising the dynamic-LDS limit is idempotent
     if (!attr_set) {
@@ -803,6 +817,11 @@ template <typename T, int BK, bool HYB, int SP>
 hipError_t launch4(const GemmArgs& a, int tile, hipStream_t s) {
     // tile 0: one tile row x 128 X rows, 4 waves, 2 stages (two workgroups per CU)
     //      1: two tile rows x 256 X rows, 8 waves, 2 stages;  2: two tile rows x 128 X rows
+    // (8-bit elements: the single-tile-row block only)
+    if constexpr (Elem<T>::bytes == 1) {
+        (void)tile;
+        return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
+    } else {
     const int bn = HYB ? a.bn : 128;
     if (bn == 64) {
         switch (tile) {
@@ -816,12 +835,18 @@ hipError_t launch4(const GemmArgs& a, int tile, hipStream_t s) {
         case 2: return launch_pair<T, BK, HYB, SP, 128, 128, 2, 8>(a, s);
         default: return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     }
+    }
 }
 
 template <typename T, int BK, bool HYB>
 hipError_t launch3(const GemmArgs& a, int sp, int tile, hipStream_t s) {
-    return sp == SPARSE_SMFMAC ? launch4<T, BK, HYB, SPARSE_SMFMAC>(a, tile, s)
-                               : launch4<T, BK, HYB, SPARSE_DECOMPRESS>(a, tile, s);
+    if constexpr (Elem<T>::bytes == 1) {
+        (void)sp;
+        return launch4<T, BK, HYB, SPARSE_SMFMAC>(a, tile, s);   // 8-bit: no expansion path
+    } else {
+        return sp == SPARSE_SMFMAC ? launch4<T, BK, HYB, SPARSE_SMFMAC>(a, tile, s)
+                                   : launch4<T, BK, HYB, SPARSE_DECOMPRESS>(a, tile, s);
+    }
 }
 
 template <typename T>
@@ -835,6 +860,8 @@ hipError_t launch2(const GemmArgs& a, int sp, int tile, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, int tile, hipStream_t s) {
+    if (a.dtype == HTS_FP8_E4M3)   // 128x128 tiles only
+        return a.index ? launch3<FP8T, 128, true>(a, sparse_path, tile, s) : launch3<FP8T, 128, false>(a, sparse_path, tile, s);
     return a.dtype == HTS_BF16 ? launch2<BF16T>(a, sparse_path, tile, s)
                                : launch2<F16T>(a, sparse_path, tile, s);
 }

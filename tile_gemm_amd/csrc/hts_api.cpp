@@ -30,16 +30,21 @@ hts_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool is16bit(int32_t dt) { return dt == HTS_F16 || dt == HTS_BF16; }
+bool is_in(int32_t dt) { return is16bit(dt) || dt == HTS_FP8_E4M3; }
+int elem_bytes(int32_t dt) { return dt == HTS_FP8_E4M3 ? 1 : 2; }
+int ld_mult(int32_t dt) { return 16 / elem_bytes(dt); }   // leading dimensions: whole 16-byte chunks
 bool is_out(int32_t dt) { return dt == HTS_F16 || dt == HTS_BF16 || dt == HTS_F32; }
 
 hts_status check_desc(const hts_desc* d) {
     if (!d) return fail(HTS_ERR_INVALID_ARG, "descriptor is NULL");
-    if (!is16bit(d->dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16 or HTS_BF16", d->dtype);
+    if (!is_in(d->dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16, HTS_BF16 or HTS_FP8_E4M3", d->dtype);
     if (d->reserved != 0) return fail(HTS_ERR_INVALID_ARG, "descriptor reserved field must be 0");
     if (d->N <= 0 || d->K <= 0) return fail(HTS_ERR_SHAPE, "N=%lld K=%lld must be positive", (long long)d->N,
                                             (long long)d->K);
     if (!((d->bn == 64 || d->bn == 128) && (d->bk == 64 || d->bk == 128)))
         return fail(HTS_ERR_UNSUPPORTED, "tile %dx%d: bn and bk must each be 64 or 128", d->bn, d->bk);
+    if (d->dtype == HTS_FP8_E4M3 && (d->bn != 128 || d->bk != 128))
+        return fail(HTS_ERR_UNSUPPORTED, "tile %dx%d: 8-bit weights use 128x128 tiles", d->bn, d->bk);
     if (d->N % d->bn || d->K % d->bk)
         return fail(HTS_ERR_SHAPE, "N=%lld K=%lld are not multiples of the %dx%d tile", (long long)d->N,
                     (long long)d->K, d->bn, d->bk);
@@ -191,7 +196,7 @@ hts_status hts_pack_plan(const hts_desc* d, const uint8_t* tile_map_host, hts_ti
             voff += dense;
         }
     }
-    sizes->values_bytes = 2 * voff;
+    sizes->values_bytes = (uint64_t)elem_bytes(d->dtype) * voff;
     sizes->meta_bytes = 4 * moff;
     sizes->index_bytes = 16 * (uint64_t)T;
     sizes->n_sparse = ns;
@@ -207,7 +212,7 @@ hts_status hts_pack(const hts_desc* d, const hts_tile* index, const void* W, int
     if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
     if (col_scale && (reinterpret_cast<uintptr_t>(col_scale) & 3u))
         return fail(HTS_ERR_ALIGN, "col_scale is not 4-byte aligned");
-    if ((st = check_ld(ldw, d->K, 8, "ldw"))) return st;
+    if ((st = check_ld(ldw, d->K, ld_mult(d->dtype), "ldw"))) return st;
     return hip_status(hts::launch_pack(*d, index, static_cast<const uint16_t*>(W), ldw, col_scale,
                                        static_cast<uint16_t*>(values), meta, static_cast<hipStream_t>(stream)),
                       "pack kernel launch");
@@ -224,7 +229,7 @@ hts_status hts_pack_masked(const hts_desc* d, const hts_tile* index, const void*
     if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
     if (malformed_groups && (reinterpret_cast<uintptr_t>(malformed_groups) & 3u))
         return fail(HTS_ERR_ALIGN, "malformed_groups is not 4-byte aligned");
-    if ((st = check_ld(ldw, d->K, 8, "ldw"))) return st;
+    if ((st = check_ld(ldw, d->K, ld_mult(d->dtype), "ldw"))) return st;
     if ((st = check_ld(ldm, d->K, 16, "ldm"))) return st;
     return hip_status(hts::launch_pack_masked(*d, index, static_cast<const uint16_t*>(W), ldw, mask, ldm,
                                               malformed_groups, static_cast<uint16_t*>(values), meta,
@@ -239,7 +244,7 @@ hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* valu
     if ((st = check_ptr(index, "index")) || (st = check_ptr(values, "values")) || (st = check_ptr(W_out, "W_out")))
         return st;
     if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
-    if ((st = check_ld(ldw, d->K, 8, "ldw"))) return st;
+    if ((st = check_ld(ldw, d->K, ld_mult(d->dtype), "ldw"))) return st;
     return hip_status(hts::launch_unpack(*d, index, static_cast<const uint16_t*>(values), meta,
                                          static_cast<uint16_t*>(W_out), ldw, static_cast<hipStream_t>(stream)),
                       "unpack kernel launch");
@@ -265,7 +270,7 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
     if (!is_out(y_dtype)) return fail(HTS_ERR_DTYPE, "y_dtype %d is not F32, F16 or BF16", y_dtype);
     if ((st = check_ptr(index, "index")) || (st = check_ptr(values, "values"))) return st;
     if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
-    if ((st = check_ld(ldx, d->K, 8, "ldx")) || (st = check_ld(ldy, d->N, 4, "ldy"))) return st;
+    if ((st = check_ld(ldx, d->K, ld_mult(d->dtype), "ldx")) || (st = check_ld(ldy, d->N, 4, "ldy"))) return st;
     if (M == 0) return ok();
     if ((st = check_ptr(X, "X")) || (st = check_ptr(Y, "Y"))) return st;
     hts::GemmArgs a{};
@@ -291,14 +296,17 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const 
                           size_t workspace_bytes, void* stream) {
     (void)workspace;
     (void)workspace_bytes;
-    if (!is16bit(dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16 or HTS_BF16", dtype);
+    if (!is_in(dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16, HTS_BF16 or HTS_FP8_E4M3", dtype);
     if (!is_out(y_dtype)) return fail(HTS_ERR_DTYPE, "y_dtype %d is not F32, F16 or BF16", y_dtype);
     if (M < 0 || N <= 0 || K <= 0)
         return fail(HTS_ERR_SHAPE, "M=%lld N=%lld K=%lld (M >= 0, N and K positive)", (long long)M, (long long)N,
                     (long long)K);
     if (N % 64 || K % 64) return fail(HTS_ERR_SHAPE, "N and K must be multiples of 64");
+    if (dtype == HTS_FP8_E4M3 && (N % 128 || K % 128))
+        return fail(HTS_ERR_SHAPE, "8-bit products need N and K multiples of 128");
     hts_status st;
-    if ((st = check_ld(ldx, K, 8, "ldx")) || (st = check_ld(ldw, K, 8, "ldw")) || (st = check_ld(ldy, N, 4, "ldy")))
+    const int lm = ld_mult(dtype);
+    if ((st = check_ld(ldx, K, lm, "ldx")) || (st = check_ld(ldw, K, lm, "ldw")) || (st = check_ld(ldy, N, 4, "ldy")))
         return st;
     if (M == 0) return ok();
     if ((st = check_ptr(X, "X")) || (st = check_ptr(W, "W")) || (st = check_ptr(Y, "Y"))) return st;
@@ -353,6 +361,7 @@ hts_status hts_wanda_tile_cost(const hts_desc* d, const void* W, int64_t ldw, co
                                void* stream) {
     hts_status st = check_desc(d);
     if (st) return st;
+    if (!is16bit(d->dtype)) return fail(HTS_ERR_DTYPE, "tile costs take HTS_F16 or HTS_BF16 weights");
     if ((st = check_ptr(W, "W")) || (st = check_ld(ldw, d->K, 8, "ldw"))) return st;
     if (!col_scale || !cost) return fail(HTS_ERR_INVALID_ARG, "col_scale or cost is NULL");
     if ((reinterpret_cast<uintptr_t>(col_scale) & 3u) || (reinterpret_cast<uintptr_t>(cost) & 7u))

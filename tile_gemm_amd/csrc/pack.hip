@@ -117,6 +117,80 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     if (MASKED && malformed && bad) atomicAdd(malformed, bad);
 }
 
+// The same pass for 8-bit E4M3 weights: a thread takes 32 consecutive bytes of a tile row (two
+// 16-byte loads); a 2:4 chunk becomes 16 kept bytes (one 16-byte store) and the same 32-bit code
+// word as above.  The score is |w| decoded exactly (times the column scale when given).
+template <bool MASKED>
+__global__ __launch_bounds__(kPackThreads) void pack8_kernel(
+    const hts_tile* __restrict__ index, int64_t Tk, int bn, int bk,
+    const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ cs,
+    const uint8_t* __restrict__ mask, int64_t ldm, uint32_t* __restrict__ malformed,
+    uint8_t* __restrict__ values, uint32_t* __restrict__ meta) {
+    const int64_t t = blockIdx.x;
+    uint32_t bad = 0;
+    const hts_tile e = index[t];
+    const int64_t tn = t / Tk, tk = t % Tk;
+    const int wpr = bk / 32;
+    const int items = bn * wpr;
+    for (int it = threadIdx.x; it < items; it += kPackThreads) {
+        const int r = it / wpr, w = it % wpr;
+        const int64_t k0 = tk * bk + 32 * w;
+        const uint8_t* src = W + (tn * bn + r) * ldw + k0;
+        const u32x4 q0 = ld16(src), q1 = ld16(src + 16);
+        if (e.type == HTS_TILE_DENSE) {
+            uint8_t* dst = values + e.val_off + (int64_t)r * bk + 32 * w;
+            st16(dst, q0);
+            st16(dst + 16, q1);
+            continue;
+        }
+        const uint32_t d[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};   // group g = d[g]
+        u32x4 mk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+        if (MASKED) {
+            const uint8_t* msrc = mask + (tn * bn + r) * ldm + k0;
+            mk[0] = *reinterpret_cast<const u32x4*>(msrc);
+            mk[1] = *reinterpret_cast<const u32x4*>(msrc + 16);
+        }
+        uint32_t kept[8];   // kept pair of group g: low byte = lower index
+        uint32_t word = 0;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const uint32_t b[4] = {d[g] & 0xFFu, (d[g] >> 8) & 0xFFu, (d[g] >> 16) & 0xFFu, d[g] >> 24};
+            float sc[4];
+            if (MASKED) {
+                const uint32_t mw = mk[g / 4][g % 4];
+                int marked = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool on = ((mw >> (8 * i)) & 0xFFu) != 0u;
+                    sc[i] = on ? 1.0f : 0.0f;
+                    marked += on;
+                }
+                bad += marked != 2;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a = fabsf(widen_e4m3(b[i]));
+                    sc[i] = cs ? a * cs[k0 + 4 * g + i] : a;
+                }
+            }
+            uint32_t i0, i1;
+            pick_two(sc, i0, i1);
+            uint32_t v0 = b[0], v1 = b[1];
+            v0 = (i0 == 1u) ? b[1] : v0;
+            v0 = (i0 == 2u) ? b[2] : v0;
+            v1 = (i1 == 2u) ? b[2] : v1;
+            v1 = (i1 == 3u) ? b[3] : v1;
+            kept[g] = v0 | (v1 << 8);
+            word |= (i0 | (i1 << 2)) << (4 * g);
+        }
+        uint8_t* dst = values + e.val_off + (int64_t)r * (bk / 2) + 16 * w;
+        st16(dst, u32x4{kept[0] | (kept[1] << 16), kept[2] | (kept[3] << 16), kept[4] | (kept[5] << 16),
+                        kept[6] | (kept[7] << 16)});
+        meta[e.meta_off + (int64_t)r * wpr + w] = word;
+    }
+    if (MASKED && malformed && bad) atomicAdd(malformed, bad);
+}
+
 __global__ void zero_counter(uint32_t* c) { *c = 0u; }
 
 __global__ __launch_bounds__(kPackThreads) void unpack_kernel(
@@ -149,12 +223,48 @@ __global__ __launch_bounds__(kPackThreads) void unpack_kernel(
     }
 }
 
+__global__ __launch_bounds__(kPackThreads) void unpack8_kernel(
+    const hts_tile* __restrict__ index, int64_t Tk, int bn, int bk,
+    const uint8_t* __restrict__ values, const uint32_t* __restrict__ meta,
+    uint8_t* __restrict__ W, int64_t ldw) {
+    const int64_t t = blockIdx.x;
+    const hts_tile e = index[t];
+    const int64_t tn = t / Tk, tk = t % Tk;
+    const int wpr = bk / 32;
+    const int items = bn * wpr;
+    for (int it = threadIdx.x; it < items; it += kPackThreads) {
+        const int r = it / wpr, w = it % wpr;
+        uint8_t* dst = W + (tn * bn + r) * ldw + tk * bk + 32 * w;
+        if (e.type == HTS_TILE_DENSE) {
+            const uint8_t* src = values + e.val_off + (int64_t)r * bk + 32 * w;
+            st16(dst, ld16(src));
+            st16(dst + 16, ld16(src + 16));
+            continue;
+        }
+        const u32x4 kv = ld16(values + e.val_off + (int64_t)r * (bk / 2) + 16 * w);
+        const uint32_t word = meta[e.meta_off + (int64_t)r * wpr + w];
+        uint32_t out[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {   // group g: kept bytes 2g, 2g+1 of the chunk
+            const uint32_t pair = (kv[g / 2] >> (16 * (g & 1))) & 0xFFFFu;
+            const uint32_t code = (word >> (4 * g)) & 0xFu, i0 = code & 3u, i1 = code >> 2;
+            out[g] = ((pair & 0xFFu) << (8 * i0)) | ((pair >> 8) << (8 * i1));
+        }
+        st16(dst, u32x4{out[0], out[1], out[2], out[3]});
+        st16(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
+    }
+}
+
 }  // namespace
 
 hipError_t launch_pack(const hts_desc& d, const hts_tile* index, const uint16_t* W, int64_t ldw,
                        const float* col_scale, uint16_t* values, uint32_t* meta, hipStream_t s) {
     const int64_t Tk = d.K / d.bk, T = (d.N / d.bn) * Tk;
-    if (d.dtype == HTS_BF16)
+    if (d.dtype == HTS_FP8_E4M3)
+        pack8_kernel<false><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
+            index, Tk, d.bn, d.bk, reinterpret_cast<const uint8_t*>(W), ldw, col_scale, nullptr, 0, nullptr,
+            reinterpret_cast<uint8_t*>(values), meta);
+    else if (d.dtype == HTS_BF16)
         pack_kernel<BF16T, false><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
             index, Tk, d.bn, d.bk, W, ldw, col_scale, nullptr, 0, nullptr, values, meta);
     else
@@ -168,7 +278,11 @@ hipError_t launch_pack_masked(const hts_desc& d, const hts_tile* index, const ui
                               uint32_t* meta, hipStream_t s) {
     const int64_t Tk = d.K / d.bk, T = (d.N / d.bn) * Tk;
     if (malformed) zero_counter<<<dim3(1), dim3(1), 0, s>>>(malformed);   // a kernel, not a memset node
-    if (d.dtype == HTS_BF16)
+    if (d.dtype == HTS_FP8_E4M3)
+        pack8_kernel<true><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
+            index, Tk, d.bn, d.bk, reinterpret_cast<const uint8_t*>(W), ldw, nullptr, mask, ldm, malformed,
+            reinterpret_cast<uint8_t*>(values), meta);
+    else if (d.dtype == HTS_BF16)
         pack_kernel<BF16T, true><<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
             index, Tk, d.bn, d.bk, W, ldw, nullptr, mask, ldm, malformed, values, meta);
     else
@@ -180,6 +294,12 @@ hipError_t launch_pack_masked(const hts_desc& d, const hts_tile* index, const ui
 hipError_t launch_unpack(const hts_desc& d, const hts_tile* index, const uint16_t* values,
                          const uint32_t* meta, uint16_t* W_out, int64_t ldw, hipStream_t s) {
     const int64_t Tk = d.K / d.bk, T = (d.N / d.bn) * Tk;
+    if (d.dtype == HTS_FP8_E4M3) {
+        unpack8_kernel<<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(
+            index, Tk, d.bn, d.bk, reinterpret_cast<const uint8_t*>(values), meta, reinterpret_cast<uint8_t*>(W_out),
+            ldw);
+        return hipGetLastError();
+    }
     unpack_kernel<<<dim3((unsigned)T), dim3(kPackThreads), 0, s>>>(index, Tk, d.bn, d.bk, values, meta,
                                                                    W_out, ldw);
     return hipGetLastError();

@@ -184,6 +184,10 @@ CONFIGS: Tuple[Config, ...] = (
                       Layer("up_13824", 13824, 5120, BF16, 128, 128, "exact", 0.5, layer_id=1)), (1, 16, 4096)),
     Config(4, "sweep", _sweep_layers(), (1, 2048)),
     Config(5, "7b_block", _block_layers(), (2048,)),
+    # prune then quantize: the 7B up-projection with 8-bit E4M3 weights and activations, drawn at
+    # unit scale (a per-tensor scale would sit outside the product)
+    Config(6, "7b_up_fp8", (Layer("up_proj_fp8", 11008, 4096, FP8, 128, 128, "exact", 0.25),), (1, 16, 2048),
+           x_sigma=1.0, w_sigma=1.0),
 )
 
 
@@ -230,7 +234,8 @@ def small_layer(N: int, K: int, dtype: str, bn: int, bk: int, seed: int) -> Tupl
 
 
 def numpy_of_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float32 view of 16-bit patterns (for inspection and for feeding float APIs)."""
+    """Exact float32 view of 16-bit patterns (for inspection and for feeding float APIs; 8-bit
+    patterns go to torch as float8_e4m3fn instead)."""
     if dtype == F16:
         return bits.view(np.float16).astype(np.float32)
     if dtype == BF16:

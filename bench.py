@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense MFMA, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}   # dense MFMA, published
 ROTATE_BYTES = 600 << 20       # > 2x the 256 MB Infinity Cache
 
 
@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--quick", action="store_true", help="profiling run: a few launches of each kernel, no oracle")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     p.add_argument("--no-block", action="store_true", help="skip the decoder-block leg")
+    p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit (E4M3) leg")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run three plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
@@ -82,6 +83,51 @@ def recorded_traffic(workload_key: str):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def run_fp8(hts, wl, dev, time_graph, time_launches, quick):
+    """The 7B up-projection with 8-bit E4M3 weights and activations (prune then quantize), 25 % of
+    the tiles 2:4: decode shapes (HBM-bound, graph-timed) and M = 2048, against the same-library
+    dense 8-bit product.  Y is bf16."""
+    import torch
+    cfg = wl.config("7b_up_fp8")
+    L = cfg.layers[0]
+    W = hts.tensor_from_bits(wl.weight_bits(cfg, L), "fp8", dev)
+    tmap = wl.tile_map(cfg, L)
+    Xall = hts.tensor_from_bits(wl.activation_bits(cfg, L, max(cfg.Ms)), "fp8", dev)
+    pw0 = hts.pack(W, tmap, L.bn, L.bk)
+    torch.cuda.synchronize()
+    packed = pw0.packed_bytes
+    dense = L.N * L.K
+    n_rot = max(2, -(-ROTATE_BYTES // packed))
+    pws = [pw0] + [hts.PackedWeight(pw0.desc, pw0.index.clone(), pw0.values.clone(), pw0.meta.clone(),
+                                    pw0.sizes, pw0.tile_map) for _ in range(n_rot - 1)]
+    n_rot_d = max(2, -(-ROTATE_BYTES // dense))
+    Ws = [W] + [W.clone() for _ in range(n_rot_d - 1)]
+    kept = L.N * L.K - int(tmap.sum()) * L.bn * L.bk // 2
+    out = {"workload": f"{L.name}: W[{L.N}x{L.K}] E4M3, 128x128 tiles, {int(tmap.sum())}/{L.T} tiles 2:4, "
+                       "X E4M3, Y bf16", "packed_bytes": packed, "dense_bytes": dense, "decode": []}
+    for M in [m for m in cfg.Ms if m <= 16]:
+        Xm = Xall[:M].contiguous()
+        Ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for _ in range(max(n_rot, n_rot_d))]
+        per = 4 if quick else 8 * max(n_rot, n_rot_d)
+        t_h = time_graph(lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n_rot]), per, 2 if quick else 25)
+        t_d = time_graph(lambda i: hts.dense_gemm(Xm, Ws[i % n_rot_d], out=Ys[i % n_rot_d]), per, 2 if quick else 25)
+        alg = packed + M * L.K + 2 * M * L.N
+        out["decode"].append({"M": M, "us": round(t_h * 1e6, 3), "GB/s": round(alg / t_h / 1e9, 1),
+                              "frac_hbm": round(alg / t_h / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg,
+                              "dense_same_library_us": round(t_d * 1e6, 3), "speedup_vs_dense": round(t_d / t_h, 3)})
+    M = max(cfg.Ms)
+    Ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    n = 10 if quick else 50
+    t_h = time_launches(lambda i: hts.gemm(Xall, pws[i % n_rot], out=Ys[i % 2]), n)
+    t_d = time_launches(lambda i: hts.dense_gemm(Xall, Ws[i % n_rot_d], out=Ys[i % 2]), n)
+    out["prefill"] = {"M": M, "us": round(t_h * 1e6, 2), "TFLOP/s": round(2.0 * M * kept / t_h / 1e12, 1),
+                      "frac_mfma_fp8": round(2.0 * M * kept / t_h / 1e12 / MFMA_PEAK_TFLOPS["fp8"], 4),
+                      "dense_same_library_us": round(t_d * 1e6, 2),
+                      "dense_same_library_TFLOP/s": round(2.0 * M * L.N * L.K / t_d / 1e12, 1),
+                      "speedup_vs_dense": round(t_d / t_h, 3)}
+    return out
 
 
 def run_block(hts, wl, dev, time_graph, quick):
@@ -314,6 +360,9 @@ def main():
     # ---------------- decoder block: the seven projections of a 7B block ----------------
     block_res = None if args.no_block else run_block(hts, wl, dev, time_graph, args.quick)
 
+    # ---------------- 8-bit E4M3 variant of the same layer ----------------
+    fp8_res = None if args.no_fp8 else run_fp8(hts, wl, dev, time_graph, time_launches, args.quick)
+
     # ---------------- CPU oracle on the host cores ----------------
     cpu = None
     if not (args.quick or args.no_cpu):
@@ -378,6 +427,7 @@ def main():
         "pack_masked": {"us": round(t_pack_masked * 1e6, 2), "GB/s": round(pack_masked_bytes / t_pack_masked / 1e9, 1),
                         "frac_hbm": round(pack_masked_bytes / t_pack_masked / 1e9 / HBM_PEAK_GBS, 4)},
         "block": block_res,
+        "fp8": fp8_res,
         "packed_bytes": packed_bytes,
         "rotation_copies": n_rot,
         "wall_s_timed_region": round(wall, 4),

@@ -39,7 +39,7 @@ struct TileRegs {
 // Loads of tile column tk for PP consecutive 16-row panels (rows n0 .. n0 + 16 PP - 1, all in
 // one tile row: r0 + 16 PP <= bn) and the matching X chunks.
 template <typename T, int BK, bool HYB, int SP, int PP>
-__device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArgs& a, int64_t t0, int tk,
+__device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArgs& a, const hts_tile& e, int tk,
                                               int64_t n0, int r0, int lane, const uint16_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
@@ -47,7 +47,6 @@ __device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArg
     int64_t rstride;
     uint32_t moff = 0;
     if (HYB) {
-        const hts_tile e = a.index[t0 + tk];   // uniform: scalar load
         type = e.type;
         moff = e.meta_off;
         rstride = type == HTS_TILE_DENSE ? BK : BK / 2;
@@ -75,6 +74,14 @@ __device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArg
 #pragma unroll
     for (int u = 0; u < BK / 32; ++u) R.x[u] = ld16(xrow + (int64_t)tk * BK + koff<SP>(u, g));
     return type;
+}
+
+// Index records of the NT tiles of a batch starting at tile column t (clamped to the wave's last
+// tile, which exists: kb < ke): independent scalar loads, issued together.
+template <int NT>
+__device__ __forceinline__ void load_entries(hts_tile (&E)[NT], const GemmArgs& a, int64_t t0, int t, int ke) {
+#pragma unroll
+    for (int s = 0; s < NT; ++s) E[s] = a.index[t0 + (t + s < ke ? t + s : ke - 1)];
 }
 
 template <typename T, int BK, int SP, int PP>
@@ -122,12 +129,17 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
     f32x4 acc[PP];
 #pragma unroll
     for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the index records of a batch are read one batch ahead, so their latency hides under the
+    // weight loads of the batch before instead of preceding them
+    hts_tile E[NT] = {};
+    if (HYB && kb < ke) load_entries<NT>(E, a, t0, kb, ke);
     for (int t = kb; t < ke; t += NT) {
         TileRegs<BK, PP> R[NT];
         uint32_t type[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP, PP>(R[s], a, t0, t + s, n0, r0, lane, xrow);
+            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP, PP>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
+        if (HYB && t + NT < ke) load_entries<NT>(E, a, t0, t + NT, ke);
 #pragma unroll
         for (int s = 0; s < NT; ++s)
             if (t + s < ke) mma_tile<T, BK, SP, PP>(R[s], type[s], acc, lane);
@@ -205,15 +217,14 @@ struct TileRegs8 {
 };
 
 template <bool HYB, int PP>
-__device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs& a, int64_t t0, int tk, int64_t n0,
-                                               int r0, int lane, const uint8_t* xrow) {
+__device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs& a, const hts_tile& e, int tk,
+                                               int64_t n0, int r0, int lane, const uint8_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
     const uint8_t* base;
     int64_t rstride;
     uint32_t moff = 0;
     if (HYB) {
-        const hts_tile e = a.index[t0 + tk];   // uniform: scalar load
         type = e.type;
         moff = e.meta_off;
         rstride = type == HTS_TILE_DENSE ? 128 : 64;
@@ -273,12 +284,15 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a)
     f32x4 acc[PP];
 #pragma unroll
     for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    hts_tile E[NT] = {};
+    if (HYB && kb < ke) load_entries<NT>(E, a, t0, kb, ke);
     for (int t = kb; t < ke; t += NT) {
         TileRegs8<PP> R[NT];
         uint32_t type[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) type[s] = load_tile8<HYB, PP>(R[s], a, t0, t + s, n0, r0, lane, xrow);
+            if (t + s < ke) type[s] = load_tile8<HYB, PP>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
+        if (HYB && t + NT < ke) load_entries<NT>(E, a, t0, t + NT, ke);
 #pragma unroll
         for (int s = 0; s < NT; ++s)
             if (t + s < ke) mma_tile8<PP>(R[s], type[s], acc);

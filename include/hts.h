@@ -65,7 +65,7 @@ typedef enum { HTS_F16 = 0, HTS_BF16 = 1, HTS_F32 = 2, HTS_FP8_E4M3 = 3 } hts_dt
 enum { HTS_TILE_DENSE = 0, HTS_TILE_SPARSE24 = 1 };
 
 /* Shape of a tiled weight.  dtype is HTS_F16, HTS_BF16 or HTS_FP8_E4M3 (W and X share it).
- * bn, bk in {64, 128} (both 128 for HTS_FP8_E4M3); N % bn == 0 and K % bk == 0 (tiles cover W
+ * bn, bk in {32, 64, 128} (both 128 for HTS_FP8_E4M3); N % bn == 0 and K % bk == 0 (tiles cover W
  * exactly); N*K < 2^32.  Element sizes: 2 bytes, 1 byte for HTS_FP8_E4M3; leading dimensions
  * (in elements) must be multiples of 8, of 16 for HTS_FP8_E4M3 (16 bytes either way). */
 typedef struct {
@@ -149,8 +149,12 @@ hts_status hts_pack_masked(const hts_desc* d, const hts_tile* index, const void*
 hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* values,
                       const uint32_t* meta, void* W_out, int64_t ldw, void* stream);
 
-/* Host only.  Bytes of device workspace hts_gemm needs for this shape and M
- * (currently always 0; pass NULL/0). */
+/* Host only.  Bytes of device workspace hts_gemm needs for this shape and M: 0, except for
+ * tiles of 32 rows or 32 columns at M above the streaming range (M > 16), where the product
+ * unpacks the weight into the workspace (N*K elements, row-major) and runs the same-library
+ * dense product on it -- the tiled kernel works on 64-row weight groups and 64-wide slices.
+ * Execution tiles below 128x128 are the tile-size ablation of the PATCH page (sections 2 and
+ * 4): finer maps, less matrix-core efficiency. */
 hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes);
 
 /* Device, asynchronous.  Y[M,N] = X[M,K] . mask(W)^T from the packed weight,
@@ -159,7 +163,9 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes);
  * sparse MFMA (or in-register expansion to dense MFMA when the environment
  * variable HTS_SPARSE_PATH=decompress), both into one accumulator per output
  * tile.  M == 0 is a no-op.  ldx, ldy: multiples of 8 and 4 with ldx >= K and
- * ldy >= N. */
+ * ldy >= N.  workspace: the hts_gemm_workspace() bytes, 16-byte aligned (NULL when that is 0);
+ * HTS_ERR_WORKSPACE when it is missing or smaller.  Calls that share a workspace must not
+ * overlap. */
 hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values,
                     const uint32_t* meta, int64_t M, const void* X, int64_t ldx,
                     void* Y, int64_t ldy, int32_t y_dtype,

@@ -81,7 +81,7 @@ def test_plan_rejects_bad_arguments():
     m = np.zeros(16, np.uint8)
     assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 64, 64, "f16"), np.full(16, 2, np.uint8))) == 5
     assert _err(lambda: hts.hts_pack_plan(hts.make_desc(250, 256, 64, 64, "f16"), m)) == 3
-    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 32, 64, "f16"), np.zeros(32, np.uint8))) == 7
+    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 16, 64, "f16"), np.zeros(64, np.uint8))) == 7
     d = hts.make_desc(256, 256, 64, 64, "f16")
     d.dtype = 2
     assert _err(lambda: hts.hts_pack_plan(d, m)) == 2
@@ -185,3 +185,27 @@ def test_fp8_arguments():
     # the 8-bit dense product needs N and K in whole 128-wide tiles
     assert L.hts_dense_gemm(3, 4, 192, 256, A16, 256, A16, 256, A16, 256, 2, None, 0, None) == 3
     assert L.hts_dense_gemm(3, 0, 256, 256, A16, 256, A16, 256, A16, 256, 2, None, 0, None) == 0
+
+
+def test_small_tiles_plan_and_workspace():
+    L = hts.lib()
+    by = ctypes.byref
+    # 32x32, 32x128 and 128x32 tiles: the plan as for any tile; the streaming range needs no
+    # workspace, larger M an unpacked copy of the weight
+    for bn, bk in ((32, 32), (32, 128), (128, 32)):
+        N, K = 256, 384
+        g = np.random.default_rng(bn + bk)
+        m = (g.random((N // bn) * (K // bk)) < 0.5).astype(np.uint8)
+        d = hts.make_desc(N, K, bn, bk, "bf16")
+        idx, sz = hts.hts_pack_plan(d, m)
+        o_idx, o_sz = oracle.plan(m, N, K, bn, bk)
+        assert np.array_equal(idx, o_idx) and sz["values_bytes"] == o_sz["values_bytes"]
+        assert sz["meta_bytes"] == o_sz["meta_bytes"]
+        assert hts.hts_gemm_workspace(d, 16) == 0
+        assert hts.hts_gemm_workspace(d, 17) == N * K * 2
+        # missing or short workspace: HTS_ERR_WORKSPACE, misaligned: HTS_ERR_ALIGN, before any launch
+        assert L.hts_gemm(by(d), A16, A16, A16, 17, A16, K, A16, N, 2, None, 0, None) == 6
+        assert L.hts_gemm(by(d), A16, A16, A16, 17, A16, K, A16, N, 2, A16, N * K, None) == 6
+        assert L.hts_gemm(by(d), A16, A16, A16, 17, A16, K, A16, N, 2, A8, N * K * 2, None) == 4
+    assert hts.hts_gemm_workspace(hts.make_desc(256, 384, 128, 128, "bf16"), 2048) == 0
+    assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 32, 32, "fp8"), np.zeros(64, np.uint8))) == 7

@@ -292,12 +292,17 @@ def unpack(pw: PackedWeight, stream=None) -> torch.Tensor:
 
 
 def gemm(X: torch.Tensor, pw: PackedWeight, out_dtype=None, out: Optional[torch.Tensor] = None,
-         stream=None) -> torch.Tensor:
-    """Y[M,N] = X[M,K] . mask(W)^T from the packed weight (fp32 accumulation)."""
+         stream=None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y[M,N] = X[M,K] . mask(W)^T from the packed weight (fp32 accumulation).  A workspace the
+    library asks for (tiles of 32 rows or columns at M > 16) is allocated here when none is given."""
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, pw.N), dtype=out_dtype or _default_out(X.dtype), device=X.device)
-    hts_gemm(pw.desc, pw.index, pw.values, pw.meta, X, out, stream=stream)
+    if workspace is None:
+        nbytes = hts_gemm_workspace(pw.desc, M)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    hts_gemm(pw.desc, pw.index, pw.values, pw.meta, X, out, workspace=workspace, stream=stream)
     return out
 
 

@@ -336,11 +336,138 @@ hipError_t launch8(const GemmArgs& a, int ksplit, int nt, int pp, hipStream_t s)
     return launch8_nt<HYB, 4, 1>(a, nt, s);
 }
 
+// ---------------------------------------------------------------------------------------
+// 16-bit weights in 32-wide tiles (bk = 32).  A tile of a 16-row panel is one 16x16x32 MFMA:
+// lane L = i + 16g takes k in [8g, 8g+8) of the tile, weights of row i and X of row j = i.
+// A 2:4 tile row holds 16 stored values and one code word; lane group g expands groups 2g and
+// 2g+1 (stored values 4g..4g+3, code byte g) in registers into its 8 dense weights -- the
+// sparse instruction spans 64 k, two such tiles of which may differ in type.
+template <int PP>
+struct TileRegs32 {
+    u32x4 a[PP];      // per panel: dense: 8 weights; 2:4: the 4 stored values in a[q][0..1]
+    uint32_t m[PP];   // per panel: 2:4 code word of the row
+    u32x4 x;          // X: 8 values of row j
+};
+
+template <bool HYB, int PP>
+__device__ __forceinline__ uint32_t load_tile32(TileRegs32<PP>& R, const GemmArgs& a, const hts_tile& e, int tk,
+                                                int64_t n0, int r0, int lane, const uint16_t* xrow) {
+    const int i = lane & 15, g = lane >> 4;
+    uint32_t type = HTS_TILE_DENSE;
+    const uint16_t* base;
+    int64_t rstride;
+    uint32_t moff = 0;
+    if (HYB) {
+        type = e.type;
+        moff = e.meta_off;
+        rstride = type == HTS_TILE_DENSE ? 32 : 16;
+        base = a.values + e.val_off + (int64_t)(r0 + i) * rstride;
+    } else {
+        rstride = a.ldw;
+        base = a.W + (n0 + i) * a.ldw + (int64_t)tk * 32;
+    }
+    if (type == HTS_TILE_DENSE) {
+#pragma unroll
+        for (int q = 0; q < PP; ++q) R.a[q] = ld16(base + 16 * q * rstride + 8 * g);
+    } else {
+        const uint32_t* mrow = a.meta + moff + (r0 + i);
+#pragma unroll
+        for (int q = 0; q < PP; ++q) {
+            const uint2 v = *reinterpret_cast<const uint2*>(base + 16 * q * rstride + 4 * g);
+            R.a[q] = u32x4{v.x, v.y, 0u, 0u};
+            R.m[q] = mrow[16 * q];
+        }
+    }
+    R.x = ld16(xrow + (int64_t)tk * 32 + 8 * g);
+    return type;
+}
+
+template <typename T, int PP>
+__device__ __forceinline__ void mma_tile32(const TileRegs32<PP>& R, uint32_t type, f32x4 (&acc)[PP], int lane) {
+    const int g = lane >> 4;
+    if (type == HTS_TILE_DENSE) {
+#pragma unroll
+        for (int q = 0; q < PP; ++q) acc[q] = mfma_dense<T>(R.a[q], R.x, acc[q]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < PP; ++q)
+            acc[q] = mfma_dense<T>(expand_two_groups(uint2{R.a[q][0], R.a[q][1]}, (R.m[q] >> (8 * g)) & 0xFFu),
+                                   R.x, acc[q]);
+    }
+}
+
+template <typename T, bool HYB, int KS, int NT, int PP>
+__global__ __launch_bounds__(64 * KS) void gemm_decode32_kernel(const GemmArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t P = gridDim.x, b = blockIdx.x, x = b & 7u, q = P >> 3, r = P & 7u;
+    const int64_t n0 = (int64_t)(x * q + (x < r ? x : r) + (b >> 3)) * 16 * PP;
+    const int64_t tn = n0 / a.bn;
+    const int r0 = (int)(n0 - tn * a.bn);
+    const int Tk = (int)(a.K / 32);
+    const int64_t t0 = tn * Tk;
+    const int kb = Tk * wave / KS, ke = Tk * (wave + 1) / KS;
+
+    const int i = lane & 15;
+    const int64_t j = i < a.M ? i : a.M - 1;
+    const uint16_t* xrow = a.X + j * a.ldx;
+    f32x4 acc[PP];
+#pragma unroll
+    for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    hts_tile E[NT] = {};
+    if (HYB && kb < ke) load_entries<NT>(E, a, t0, kb, ke);
+    for (int t = kb; t < ke; t += NT) {
+        TileRegs32<PP> R[NT];
+        uint32_t type[NT];
+#pragma unroll
+        for (int s = 0; s < NT; ++s)
+            if (t + s < ke) type[s] = load_tile32<HYB, PP>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
+        if (HYB && t + NT < ke) load_entries<NT>(E, a, t0, t + NT, ke);
+#pragma unroll
+        for (int s = 0; s < NT; ++s)
+            if (t + s < ke) mma_tile32<T, PP>(R[s], type[s], acc, lane);
+    }
+
+    __shared__ f32x4 red[KS][PP][64];
+#pragma unroll
+    for (int q2 = 0; q2 < PP; ++q2) red[wave][q2][lane] = acc[q2];
+    __syncthreads();
+    for (int o = threadIdx.x; o < 256 * PP; o += 64 * KS) {
+        const int q2 = o >> 8, m = (o >> 4) & 15, rr = o & 15;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < KS; ++w) sum += red[w][q2][m + 16 * (rr >> 2)][rr & 3];
+        if (m < a.M) store_y1(a.Y, (int64_t)m * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
+    }
+}
+
+template <typename T, bool HYB>
+hipError_t launch32(const GemmArgs& a, int ksplit, int pp, hipStream_t s) {
+    // eight 32-wide tile columns per batch: the bytes of two 128-wide ones
+    if (pp == 2) {
+        const dim3 grid((unsigned)(a.N / 32)), block(64 * (ksplit >= 8 ? 8 : 4));
+        if (ksplit >= 8) gemm_decode32_kernel<T, HYB, 8, 8, 2><<<grid, block, 0, s>>>(a);
+        else gemm_decode32_kernel<T, HYB, 4, 8, 2><<<grid, block, 0, s>>>(a);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)(a.N / 16));
+    if (ksplit >= 16) gemm_decode32_kernel<T, HYB, 16, 8, 1><<<grid, dim3(1024), 0, s>>>(a);
+    else if (ksplit >= 8) gemm_decode32_kernel<T, HYB, 8, 8, 1><<<grid, dim3(512), 0, s>>>(a);
+    else gemm_decode32_kernel<T, HYB, 4, 8, 1><<<grid, dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s) {
     if (a.dtype == HTS_FP8_E4M3)   // 8-bit: the sparse instruction only (no expansion fallback)
         return a.index ? launch8<true>(a, ksplit, nt, pp, s) : launch8<false>(a, ksplit, nt, pp, s);
+    if (a.bk == 32) {              // 32-wide tiles: expansion in registers
+        (void)nt;
+        (void)sparse_path;
+        if (a.dtype == HTS_BF16) return a.index ? launch32<BF16T, true>(a, ksplit, pp, s) : launch32<BF16T, false>(a, ksplit, pp, s);
+        return a.index ? launch32<F16T, true>(a, ksplit, pp, s) : launch32<F16T, false>(a, ksplit, pp, s);
+    }
     return a.dtype == HTS_BF16 ? launch2<BF16T>(a, ksplit, nt, pp, sparse_path, s)
                                : launch2<F16T>(a, ksplit, nt, pp, sparse_path, s);
 }

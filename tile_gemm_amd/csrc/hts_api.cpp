@@ -41,8 +41,8 @@ hts_status check_desc(const hts_desc* d) {
     if (d->reserved != 0) return fail(HTS_ERR_INVALID_ARG, "descriptor reserved field must be 0");
     if (d->N <= 0 || d->K <= 0) return fail(HTS_ERR_SHAPE, "N=%lld K=%lld must be positive", (long long)d->N,
                                             (long long)d->K);
-    if (!((d->bn == 64 || d->bn == 128) && (d->bk == 64 || d->bk == 128)))
-        return fail(HTS_ERR_UNSUPPORTED, "tile %dx%d: bn and bk must each be 64 or 128", d->bn, d->bk);
+    if (!((d->bn == 32 || d->bn == 64 || d->bn == 128) && (d->bk == 32 || d->bk == 64 || d->bk == 128)))
+        return fail(HTS_ERR_UNSUPPORTED, "tile %dx%d: bn and bk must each be 32, 64 or 128", d->bn, d->bk);
     if (d->dtype == HTS_FP8_E4M3 && (d->bn != 128 || d->bk != 128))
         return fail(HTS_ERR_UNSUPPORTED, "tile %dx%d: 8-bit weights use 128x128 tiles", d->bn, d->bk);
     if (d->N % d->bn || d->K % d->bk)
@@ -85,6 +85,15 @@ int64_t decode_max_m() {
         if (x >= 0 && x <= 16) return x;
     }
     return 16;
+}
+
+// Tiles of 32 rows or 32 columns are below the tiled kernel's 64-row weight groups and 64-wide
+// slices: at M above the streaming range the product unpacks the weight into the workspace and
+// runs the dense product on it.
+bool small_tiles(const hts_desc* d) { return d->bn < 64 || d->bk < 64; }
+uint64_t unpack_workspace_bytes(const hts_desc* d, int64_t M) {
+    if (!small_tiles(d) || M <= decode_max_m()) return 0;
+    return ((uint64_t)d->N * d->K * elem_bytes(d->dtype) + 255) & ~uint64_t(255);
 }
 
 // Launch shape of the streaming kernel.  Defaults measured on MI355X (bf16, 128x128 tiles):
@@ -258,15 +267,13 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes) {
     if (st) return st;
     if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
     if (!bytes) return fail(HTS_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = 0;
+    *bytes = (size_t)unpack_workspace_bytes(d, M);
     return ok();
 }
 
 hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta, int64_t M,
                     const void* X, int64_t ldx, void* Y, int64_t ldy, int32_t y_dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     hts_status st = check_desc(d);
     if (st) return st;
     if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
@@ -276,6 +283,34 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
     if ((st = check_ld(ldx, d->K, ld_mult(d->dtype), "ldx")) || (st = check_ld(ldy, d->N, 4, "ldy"))) return st;
     if (M == 0) return ok();
     if ((st = check_ptr(X, "X")) || (st = check_ptr(Y, "Y"))) return st;
+    const uint64_t ws = unpack_workspace_bytes(d, M);
+    if (ws) {
+        if (!workspace || workspace_bytes < ws)
+            return fail(HTS_ERR_WORKSPACE, "tiles of %dx%d at M=%lld need a %llu-byte workspace (got %zu)", d->bn,
+                        d->bk, (long long)M, (unsigned long long)ws, workspace_bytes);
+        if (!aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
+        if (d->N % 64 || d->K % 64)
+            return fail(HTS_ERR_UNSUPPORTED, "the unpacked product needs N and K multiples of 64");
+        // the unpacked weight, row-major with ldw = K, then the same-library dense product on it
+        hipError_t e = hts::launch_unpack(*d, index, static_cast<const uint16_t*>(values), meta,
+                                          static_cast<uint16_t*>(workspace), d->K, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_status(e, "unpack kernel launch");
+        hts::GemmArgs a{};
+        a.dtype = d->dtype;
+        a.y_dtype = y_dtype;
+        a.M = M;
+        a.N = d->N;
+        a.K = d->K;
+        a.bn = 64;
+        a.bk = (d->K % 128 == 0) ? 128 : 64;
+        a.W = static_cast<const uint16_t*>(workspace);
+        a.ldw = d->K;
+        a.X = static_cast<const uint16_t*>(X);
+        a.ldx = ldx;
+        a.Y = Y;
+        a.ldy = ldy;
+        return run_gemm(a, static_cast<hipStream_t>(stream));
+    }
     hts::GemmArgs a{};
     a.dtype = d->dtype;
     a.y_dtype = y_dtype;

@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     p.add_argument("--no-block", action="store_true", help="skip the decoder-block leg")
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit (E4M3) leg")
+    p.add_argument("--no-tiles", action="store_true", help="skip the tile-size leg")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run three plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
@@ -127,6 +128,43 @@ def run_fp8(hts, wl, dev, time_graph, time_launches, quick):
                       "dense_same_library_us": round(t_d * 1e6, 2),
                       "dense_same_library_TFLOP/s": round(2.0 * M * L.N * L.K / t_d / 1e12, 1),
                       "speedup_vs_dense": round(t_d / t_h, 3)}
+    return out
+
+
+def run_tile_sizes(hts, wl, dev, time_graph, time_launches, quick):
+    """Tile-size ablation on the 7B up-projection (bf16, 25 % of the tiles 2:4 at every size):
+    128x128, 64x64 and 32x32 maps at M = 1, 16 (graph-timed) and 2048 (32x32 at M = 2048 runs
+    unpack + the dense product through the workspace)."""
+    import torch
+    cfg = wl.config("7b_up")
+    L = cfg.layers[0]
+    W = hts.tensor_from_bits(wl.weight_bits(cfg, L), L.dtype, dev)
+    Xall = hts.tensor_from_bits(wl.activation_bits(cfg, L, max(cfg.Ms)), L.dtype, dev)
+    out = {}
+    for t in (128, 64, 32):
+        T = (L.N // t) * (L.K // t)
+        m = wl.exact_map(T, int(round(0.25 * T)), wl.rng(cfg.cfg_id, L.layer_id, wl.TAG_MAP, (t,)))
+        pw0 = hts.pack(W, m, t, t)
+        torch.cuda.synchronize()
+        n_rot = max(2, -(-ROTATE_BYTES // pw0.packed_bytes))
+        pws = [pw0] + [hts.PackedWeight(pw0.desc, pw0.index.clone(), pw0.values.clone(), pw0.meta.clone(),
+                                        pw0.sizes, pw0.tile_map) for _ in range(n_rot - 1)]
+        row = {"packed_bytes": pw0.packed_bytes}
+        for M in (1, 16):
+            Xm = Xall[:M].contiguous()
+            Ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for _ in range(n_rot)]
+            tm = time_graph(lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n_rot]), 4 if quick else 8 * n_rot,
+                            2 if quick else 20)
+            row[f"M{M}_us"] = round(tm * 1e6, 2)
+        M = max(cfg.Ms)
+        Y = torch.empty((M, L.N), dtype=torch.bfloat16, device=dev)
+        nbytes = hts.hts_gemm_workspace(pw0.desc, M)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+        tm = time_launches(lambda i: hts.gemm(Xall, pws[i % n_rot], out=Y, workspace=ws), 5 if quick else 30)
+        row[f"M{M}_us"] = round(tm * 1e6, 1)
+        row["path_at_M2048"] = "unpack + dense product (workspace)" if nbytes else "tiled hybrid kernel"
+        out[f"{t}x{t}"] = row
+        del pws, pw0
     return out
 
 
@@ -362,6 +400,7 @@ def main():
 
     # ---------------- 8-bit E4M3 variant of the same layer ----------------
     fp8_res = None if args.no_fp8 else run_fp8(hts, wl, dev, time_graph, time_launches, args.quick)
+    tiles_res = None if args.no_tiles else run_tile_sizes(hts, wl, dev, time_graph, time_launches, args.quick)
 
     # ---------------- CPU oracle on the host cores ----------------
     cpu = None
@@ -428,6 +467,7 @@ def main():
                         "frac_hbm": round(pack_masked_bytes / t_pack_masked / 1e9 / HBM_PEAK_GBS, 4)},
         "block": block_res,
         "fp8": fp8_res,
+        "tile_sizes": tiles_res,
         "packed_bytes": packed_bytes,
         "rotation_copies": n_rot,
         "wall_s_timed_region": round(wall, 4),

@@ -149,12 +149,18 @@ hts_status hts_pack_masked(const hts_desc* d, const hts_tile* index, const void*
 hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* values,
                       const uint32_t* meta, void* W_out, int64_t ldw, void* stream);
 
-/* Host only.  Bytes of device workspace hts_gemm needs for this shape and M: 0, except for
- * tiles of 32 rows or 32 columns at M above the streaming range (M > 16), where the product
- * unpacks the weight into the workspace (N*K elements, row-major) and runs the same-library
- * dense product on it -- the tiled kernel works on 64-row weight groups and 64-wide slices.
- * Execution tiles below 128x128 are the tile-size ablation of the PATCH page (sections 2 and
- * 4): finer maps, less matrix-core efficiency. */
+/* Host only.  Bytes of device workspace for the fastest hts_gemm path at this shape and M
+ * (0 at M <= 16, the streaming range).  Two uses, in this order within the workspace:
+ *  - tiles of 32 rows or 32 columns above M = 16: the product unpacks the weight into the
+ *    workspace (N*K elements, row-major, 256-byte rounded) and runs the same-library dense
+ *    product on it -- the tiled kernel works on 64-row weight groups and 64-wide slices.
+ *    Execution tiles below 128x128 are the tile-size ablation of the PATCH page (sections 2
+ *    and 4): finer maps, less matrix-core efficiency.  This part is required.
+ *  - split products: when the tiled kernel would have at most 256 output blocks (for 128x128
+ *    tiles, ceil(N/128) * ceil(M/128) <= 256), the K range of every tile row is split over up
+ *    to 8 workgroups that write fp32 partial products (nsplit * M * N floats, 256-byte rounded),
+ *    summed in a fixed order by a second kernel.  This part is optional: with less workspace the
+ *    product runs unsplit, with the same result up to fp32 rounding order. */
 hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes);
 
 /* Device, asynchronous.  Y[M,N] = X[M,K] . mask(W)^T from the packed weight,
@@ -163,9 +169,10 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes);
  * sparse MFMA (or in-register expansion to dense MFMA when the environment
  * variable HTS_SPARSE_PATH=decompress), both into one accumulator per output
  * tile.  M == 0 is a no-op.  ldx, ldy: multiples of 8 and 4 with ldx >= K and
- * ldy >= N.  workspace: the hts_gemm_workspace() bytes, 16-byte aligned (NULL when that is 0);
- * HTS_ERR_WORKSPACE when it is missing or smaller.  Calls that share a workspace must not
- * overlap. */
+ * ldy >= N.  workspace: up to the hts_gemm_workspace() bytes, 16-byte aligned, or NULL.
+ * HTS_ERR_WORKSPACE only when the unpacked weight of 32-wide tiles does not fit; a workspace
+ * too small for the split-product parts runs the product unsplit.  Results are deterministic
+ * for a given call shape and workspace.  Calls that share a workspace must not overlap. */
 hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values,
                     const uint32_t* meta, int64_t M, const void* X, int64_t ldx,
                     void* Y, int64_t ldy, int32_t y_dtype,
@@ -173,11 +180,16 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
 
 /* Device, asynchronous.  The same-library dense product Y = X . W^T on a
  * row-major W[N,K] (ldw) with the same kernels and no tile index: the
- * reference point for speedups.  N and K multiples of 64. */
+ * reference point for speedups.  N and K multiples of 64.  workspace: optional, as the
+ * split-product part of hts_gemm's (size from hts_dense_gemm_workspace). */
 hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K,
                           const void* X, int64_t ldx, const void* W, int64_t ldw,
                           void* Y, int64_t ldy, int32_t y_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host only.  Bytes of the optional workspace of hts_dense_gemm at this shape (0 unless the
+ * product would be split, see hts_gemm_workspace). */
+hts_status hts_dense_gemm_workspace(int32_t dtype, int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /* Device, asynchronous.  H[M,N] = silu(G) * U elementwise, silu(x) = x / (1 + e^-x), fp32
  * arithmetic, one round-to-nearest-even to dtype (HTS_F16 / HTS_BF16, shared by G, U and H):

@@ -209,3 +209,30 @@ def test_small_tiles_plan_and_workspace():
         assert L.hts_gemm(by(d), A16, A16, A16, 17, A16, K, A16, N, 2, A8, N * K * 2, None) == 4
     assert hts.hts_gemm_workspace(hts.make_desc(256, 384, 128, 128, "bf16"), 2048) == 0
     assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 32, 32, "fp8"), np.zeros(64, np.uint8))) == 7
+
+
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_split_product_workspace_sizes(monkeypatch):
+    # the parts of a split product: nsplit * M * N floats when the tiled kernel would have at most
+    # 256 output blocks; nsplit = min(8, 512 // blocks), lowered until every part has >= 4 slices
+    N, K = 11008, 4096
+    d = hts.make_desc(N, K, 128, 128, "bf16")
+    for M, ns in ((1, 0), (16, 0), (17, 5), (128, 5), (129, 2), (256, 2), (257, 0), (2048, 0)):
+        assert hts.hts_gemm_workspace(d, M) == (_r256(ns * M * N * 4) if ns else 0), M
+        assert hts.hts_dense_gemm_workspace("bf16", M, N, K) == (_r256(ns * M * N * 4) if ns else 0), M
+    # 8-bit: 128-wide slices (32 per tile row here); 64x64 tiles: 64-row blocks
+    assert hts.hts_gemm_workspace(hts.make_desc(N, K, 128, 128, "fp8"), 17) == _r256(5 * 17 * N * 4)
+    assert hts.hts_gemm_workspace(hts.make_desc(4096, 4096, 64, 64, "bf16"), 17) == _r256(8 * 17 * 4096 * 4)
+    # few slices: K = 256 has 4 (bf16), too few to split
+    assert hts.hts_gemm_workspace(hts.make_desc(1024, 256, 128, 128, "bf16"), 64) == 0
+    # 32-wide tiles: the unpacked weight, then the parts of the dense product
+    d32 = hts.make_desc(N, K, 32, 32, "bf16")
+    assert hts.hts_gemm_workspace(d32, 17) == N * K * 2 + _r256(5 * 17 * N * 4)
+    # overrides: a forced count, and the two-tile-row block shapes (never split)
+    monkeypatch.setenv("HTS_PREFILL_SPLIT", "3")
+    assert hts.hts_gemm_workspace(d, 300) == _r256(3 * 300 * N * 4)
+    monkeypatch.setenv("HTS_PREFILL_TILE", "p256")
+    assert hts.hts_gemm_workspace(d, 300) == 0

@@ -62,6 +62,7 @@ _SIGS = {
                                 _VP, ctypes.c_size_t, _VP]),
     "hts_dense_gemm": (ctypes.c_int, [_I32, _I64, _I64, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _I32, _VP,
                                       ctypes.c_size_t, _VP]),
+    "hts_dense_gemm_workspace": (ctypes.c_int, [_I32, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "hts_silu_mul": (ctypes.c_int, [_I32, _I64, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _VP]),
     "hts_col_norms": (ctypes.c_int, [_I32, _I64, _I64, _VP, _I64, _VP, _VP]),
     "hts_wanda_tile_cost": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _I64, _VP, _VP, _VP]),
@@ -180,11 +181,18 @@ def hts_gemm(desc, index, values, meta, X, Y, y_dtype=None, workspace=None, stre
                           _ptr(Y), Y.stride(0), yd, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def hts_dense_gemm(X, W, Y, stream=None) -> None:
+def hts_dense_gemm_workspace(dtype, M: int, N: int, K: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().hts_dense_gemm_workspace(_dt(dtype), M, N, K, ctypes.byref(n)))
+    return n.value
+
+
+def hts_dense_gemm(X, W, Y, workspace=None, stream=None) -> None:
     M, K = X.shape
     N = W.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hts_dense_gemm(_dt(X.dtype), M, N, K, _ptr(X), X.stride(0), _ptr(W), W.stride(0), _ptr(Y),
-                                Y.stride(0), _dt(Y.dtype), None, 0, _stream(stream)))
+                                Y.stride(0), _dt(Y.dtype), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def hts_col_norms(X, out, stream=None) -> None:
@@ -293,8 +301,9 @@ def unpack(pw: PackedWeight, stream=None) -> torch.Tensor:
 
 def gemm(X: torch.Tensor, pw: PackedWeight, out_dtype=None, out: Optional[torch.Tensor] = None,
          stream=None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y[M,N] = X[M,K] . mask(W)^T from the packed weight (fp32 accumulation).  A workspace the
-    library asks for (tiles of 32 rows or columns at M > 16) is allocated here when none is given."""
+    """Y[M,N] = X[M,K] . mask(W)^T from the packed weight (fp32 accumulation).  The workspace the
+    library asks for (the unpacked weight of 32-wide tiles at M > 16, the parts of a split
+    product) is allocated here when none is given."""
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, pw.N), dtype=out_dtype or _default_out(X.dtype), device=X.device)
@@ -312,11 +321,16 @@ def _default_out(dt):
 
 
 def dense_gemm(X: torch.Tensor, W: torch.Tensor, out_dtype=None, out: Optional[torch.Tensor] = None,
-               stream=None) -> torch.Tensor:
-    """The same-library dense product Y = X . W^T (no tile index)."""
+               stream=None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The same-library dense product Y = X . W^T (no tile index); the workspace of a split
+    product is allocated here when none is given."""
     if out is None:
         out = torch.empty((X.shape[0], W.shape[0]), dtype=out_dtype or _default_out(X.dtype), device=X.device)
-    hts_dense_gemm(X, W, out, stream=stream)
+    if workspace is None:
+        nbytes = hts_dense_gemm_workspace(X.dtype, X.shape[0], W.shape[0], X.shape[1])
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    hts_dense_gemm(X, W, out, workspace=workspace, stream=stream)
     return out
 
 

@@ -337,9 +337,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % NG, wm = wave / NG;
 
-    // block id -> output block
+    // block id -> output block; blockIdx.y = part of the tile row's slices (split products)
     int nb, mb;
     block_of(blockIdx.x, NB, MB, ord, nb, mb);
+    const int nsplit = a.nsplit > 1 ? a.nsplit : 1, split = (int)blockIdx.y;
 
     Ctx<BK, HYB, BN, BM, NW> C;
     C.ldw = a.ldw;
@@ -455,36 +456,41 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
 #pragma unroll
         for (int bj = 0; bj < NBJ; ++bj) acc[b][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // slices k0 .. k1-1 of the ordered list (all of them unless the product is split)
     const int S = C.Tk * SPT, Sd = C.n_dense * SPT;
+    const int k0 = (int)((int64_t)split * S / nsplit), k1 = (int)((int64_t)(split + 1) * S / nsplit);
     const bool wvalid = C.gvalid(wn);
     const int xoff = wm * WTM * 128;
     constexpr int PER_SLICE = XJ + NG * (8 / NW);   // copy instructions per wave per slice
-    auto issue = [&](int kn) {   // called for kn = 0, 1, 2, ... in order
-        if (HYB && kn > 0 && kn % (64 * SPT) == 0) C.shift_list();
+    if (HYB)                                         // bring the block of list entry k0 / SPT first
+        for (int b = 0; b < k0 / (64 * SPT); ++b) C.shift_list();
+    auto issue = [&](int kn) {   // called for kn = k0, k0 + 1, ... in order
+        if (HYB && kn > k0 && kn % (64 * SPT) == 0) C.shift_list();
         set_x(kn);
         const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
         if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW, ES>(C, kn, stage);
         else issue_slice<BK, HYB, BN, BM, NSTAGE, false, NW, ES>(C, kn, stage);
     };
-    // prologue: slices 0 .. NSTAGE-2 in flight
+    // prologue: slices k0 .. k0+NSTAGE-2 in flight
 #pragma unroll
     for (int k = 0; k < NSTAGE - 1; ++k)
-        if (k < S) issue(k);
+        if (k0 + k < k1) issue(k0 + k);
     auto step = [&](int ks) {
         // wait until slice ks has landed: later slices (up to NSTAGE-2 of them) may stay in flight
-        wait_slice<NSTAGE, PER_SLICE>(S - 1 - ks);
+        wait_slice<NSTAGE, PER_SLICE>(k1 - 1 - ks);
         __syncthreads();                    // everyone's copies landed; stage of slice ks-1 is free
         const int kn = ks + NSTAGE - 1;
-        if (kn < S) issue(kn);
+        if (kn < k1) issue(kn);
         return smem + (ks % NSTAGE) * Lo::STAGE;
     };
-    int ks = 0;
-    for (; ks < Sd; ++ks) {
+    int ks = k0;
+    const int kd = Sd < k1 ? Sd : k1;
+    for (; ks < kd; ++ks) {
         const uint8_t* st = step(ks);
         if (wvalid) compute_dense<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
     }
     if constexpr (HYB) {
-        for (; ks < S; ++ks) {
+        for (; ks < k1; ++ks) {
             const uint8_t* st = step(ks);
             if (wvalid)
                 compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
@@ -492,8 +498,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         }
     }
 
-    // epilogue: acc[b][bj] lane (j + 16q) holds Y^T rows 4q..4q+3 of block b, column j of block bj
+    // epilogue: acc[b][bj] lane (j + 16q) holds Y^T rows 4q..4q+3 of block b, column j of block bj;
+    // a split product writes its fp32 part instead (rows of N floats)
     if (!wvalid) return;
+    void* out = a.Y;
+    int64_t ldo = a.ldy;
+    int32_t odt = a.y_dtype;
+    if (nsplit > 1) {
+        out = a.part + (int64_t)split * a.M * a.N;
+        ldo = a.N;
+        odt = HTS_F32;
+    }
     const int j = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -501,9 +516,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
 #pragma unroll
         for (int bj = 0; bj < NBJ; ++bj) {
             const int64_t m = m0 + wm * WTM + 16 * bj + j;
-            if (m < a.M) store_y4(a.Y, m * a.ldy + n, a.y_dtype, acc[b][bj]);
+            if (m < a.M) store_y4(out, m * ldo + n, odt, acc[b][bj]);
         }
     }
+}
+
+// Sum of the parts of a split product, in part order (deterministic), rounded once to y_dtype.
+// One thread per 4 consecutive outputs of a row (N is a multiple of 64).
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int nsplit, int64_t M,
+                                                        int64_t N, void* Y, int64_t ldy, int32_t y_dtype) {
+    const int64_t nq = N / 4;
+    const int64_t qi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (qi >= M * nq) return;
+    const int64_t m = qi / nq, n = 4 * (qi % nq);
+    f32x4 acc = *reinterpret_cast<const f32x4*>(part + m * N + n);
+    for (int i = 1; i < nsplit; ++i) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(part + ((int64_t)i * M + m) * N + n);
+        acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+    }
+    store_y4(Y, m * ldy + n, y_dtype, acc);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -809,7 +840,13 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
         attr_set = true;
     }
     const int NB = (int)((a.N + BN - 1) / BN), MB = (int)((a.M + BM - 1) / BM);
-    kern<<<dim3((unsigned)(NB * MB)), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
+    const int nsplit = a.nsplit > 1 ? a.nsplit : 1;
+    kern<<<dim3((unsigned)(NB * MB), (unsigned)nsplit), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit == 1) return e;
+    const int64_t quads = a.M * (a.N / 4);
+    split_sum_kernel<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s>>>(a.part, nsplit, a.M, a.N, a.Y,
+                                                                              a.ldy, a.y_dtype);
     return hipGetLastError();
 }
 

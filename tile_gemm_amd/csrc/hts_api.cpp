@@ -130,14 +130,54 @@ int decode_nt(const hts::GemmArgs& a) {
 // Block shape of the tiled kernel (HTS_PREFILL_TILE overrides): r128 = one tile row x 128 X
 // rows per workgroup, 4 waves, two workgroups per CU (default); p256 / p128 = two tile rows x
 // 256 / 128 X rows, 8 waves.
-int prefill_tile(const hts::GemmArgs& a) {
-    (void)a;
+int prefill_tile_env() {
     const char* v = getenv("HTS_PREFILL_TILE");
     if (v && *v) {
         if (!strcmp(v, "p256")) return 1;
         if (!strcmp(v, "p128")) return 2;
     }
     return 0;
+}
+int prefill_tile(const hts::GemmArgs& a) { return a.nsplit > 1 ? 0 : prefill_tile_env(); }
+
+// Split products (tiled kernel, default block shape).  A workgroup alone on its CU takes about as
+// long per 64-wide slice as each of two sharing one, so a grid of at most 256 blocks (one per CU)
+// leaves half the chip's slots empty and its run time is set by the slices per block.  Then the
+// slices of each tile row are split over nsplit workgroups -- at most 512 in all (two per CU), at
+// least 4 slices and at most 8 parts -- and a second kernel sums their fp32 parts in a fixed
+// order.  Measured on the 7B up-projection (11008 x 4096, bf16, 86 tile rows), split / unsplit:
+// M = 17 23.7 / 60.5 us (5 parts), 64 28.4 / 60.6, 128 37.2 / 61.3, 256 54.4 / 62.1 (2 parts);
+// at 258 and more blocks (M > 256 here) splitting was slower at every count tried.
+// HTS_PREFILL_SPLIT=1..16 overrides.  block_rows: weight rows per block of the launch.
+int prefill_split(int64_t M, int64_t N, int64_t K, int32_t dtype, int block_rows) {
+    if (M <= decode_max_m() || prefill_tile_env() != 0) return 1;
+    const int64_t slices = K * elem_bytes(dtype) / 128;
+    const char* v = getenv("HTS_PREFILL_SPLIT");
+    if (v && *v) {
+        const long x = strtol(v, nullptr, 10);
+        if (x >= 1 && x <= 16) return (int)(x < slices ? x : slices);
+    }
+    const int64_t blocks = ((N + block_rows - 1) / block_rows) * ((M + 127) / 128);
+    if (blocks > 256) return 1;
+    int64_t sp = 512 / blocks;
+    if (sp > 8) sp = 8;
+    while (sp > 1 && slices / sp < 4) --sp;
+    return (int)sp;
+}
+
+uint64_t split_bytes(int64_t M, int64_t N, int nsplit) {
+    if (nsplit <= 1) return 0;
+    return ((uint64_t)nsplit * M * N * 4 + 255) & ~uint64_t(255);
+}
+
+// Attach the partial-product buffer when the workspace holds it; otherwise run unsplit.
+void attach_split(hts::GemmArgs& a, int nsplit, void* ws, size_t ws_bytes) {
+    a.nsplit = 1;
+    a.part = nullptr;
+    if (nsplit > 1 && ws && ws_bytes >= split_bytes(a.M, a.N, nsplit)) {
+        a.nsplit = nsplit;
+        a.part = static_cast<float*>(ws);
+    }
 }
 
 hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
@@ -267,7 +307,10 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes) {
     if (st) return st;
     if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
     if (!bytes) return fail(HTS_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = (size_t)unpack_workspace_bytes(d, M);
+    const uint64_t ws = unpack_workspace_bytes(d, M);
+    // the unpacked weight (tiles of 32), then the parts of a split product
+    const int br = (ws || d->bn != 64) ? 128 : 64;
+    *bytes = (size_t)(ws + split_bytes(M, d->N, prefill_split(M, d->N, d->K, d->dtype, br)));
     return ok();
 }
 
@@ -309,8 +352,11 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
         a.ldx = ldx;
         a.Y = Y;
         a.ldy = ldy;
+        attach_split(a, prefill_split(M, d->N, d->K, d->dtype, 128), static_cast<uint8_t*>(workspace) + ws,
+                     workspace_bytes - ws);
         return run_gemm(a, static_cast<hipStream_t>(stream));
     }
+    if (workspace && !aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
     hts::GemmArgs a{};
     a.dtype = d->dtype;
     a.y_dtype = y_dtype;
@@ -326,14 +372,13 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
     a.ldx = ldx;
     a.Y = Y;
     a.ldy = ldy;
+    attach_split(a, prefill_split(M, d->N, d->K, d->dtype, d->bn == 64 ? 64 : 128), workspace, workspace_bytes);
     return run_gemm(a, static_cast<hipStream_t>(stream));
 }
 
 hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, const void* W,
                           int64_t ldw, void* Y, int64_t ldy, int32_t y_dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (!is_in(dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16, HTS_BF16 or HTS_FP8_E4M3", dtype);
     if (!is_out(y_dtype)) return fail(HTS_ERR_DTYPE, "y_dtype %d is not F32, F16 or BF16", y_dtype);
     if (M < 0 || N <= 0 || K <= 0)
@@ -348,6 +393,7 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const 
         return st;
     if (M == 0) return ok();
     if ((st = check_ptr(X, "X")) || (st = check_ptr(W, "W")) || (st = check_ptr(Y, "Y"))) return st;
+    if (workspace && !aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
     hts::GemmArgs a{};
     a.dtype = dtype;
     a.y_dtype = y_dtype;
@@ -362,7 +408,18 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const 
     a.ldx = ldx;
     a.Y = Y;
     a.ldy = ldy;
+    attach_split(a, prefill_split(M, N, K, dtype, 128), workspace, workspace_bytes);
     return run_gemm(a, static_cast<hipStream_t>(stream));
+}
+
+hts_status hts_dense_gemm_workspace(int32_t dtype, int64_t M, int64_t N, int64_t K, size_t* bytes) {
+    if (!is_in(dtype)) return fail(HTS_ERR_DTYPE, "dtype %d is not HTS_F16, HTS_BF16 or HTS_FP8_E4M3", dtype);
+    if (M < 0 || N <= 0 || K <= 0)
+        return fail(HTS_ERR_SHAPE, "M=%lld N=%lld K=%lld (M >= 0, N and K positive)", (long long)M, (long long)N,
+                    (long long)K);
+    if (!bytes) return fail(HTS_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = (size_t)split_bytes(M, N, prefill_split(M, N, K, dtype, 128));
+    return ok();
 }
 
 hts_status hts_silu_mul(int32_t dtype, int64_t M, int64_t N, const void* G, int64_t ldg, const void* U,

@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit (E4M3) leg")
     p.add_argument("--no-tiles", action="store_true", help="skip the tile-size leg")
     p.add_argument("--no-shard", action="store_true", help="skip the one-GPU-share (8-way N split) leg")
+    p.add_argument("--no-mid", action="store_true", help="skip the moderate-M (17..256) leg")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run three plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
@@ -169,6 +170,44 @@ def run_tile_sizes(hts, wl, dev, time_graph, time_launches, quick):
     return out
 
 
+def run_mid_m(hts, wl, dev, time_graph, quick):
+    """The 7B up-projection between the streaming range and full prefill (M = 17 .. 256): few
+    output blocks, so the tiled product is split over K (the workspace holds the parts).
+    Graph-timed with rotated weights; the same-library dense product and torch for comparison."""
+    import torch
+    cfg = wl.config("7b_up")
+    L = cfg.layers[0]
+    m = wl.tile_map(cfg, L)
+    W = hts.tensor_from_bits(wl.weight_bits(cfg, L), L.dtype, dev)
+    Xall = hts.tensor_from_bits(wl.activation_bits(cfg, L, max(cfg.Ms)), L.dtype, dev)
+    pw0 = hts.pack(W, m, L.bn, L.bk)
+    torch.cuda.synchronize()
+    n_rot = max(2, -(-ROTATE_BYTES // pw0.packed_bytes))
+    pws = [pw0] + [hts.PackedWeight(pw0.desc, pw0.index.clone(), pw0.values.clone(), pw0.meta.clone(),
+                                    pw0.sizes, pw0.tile_map) for _ in range(n_rot - 1)]
+    n_rd = max(2, -(-ROTATE_BYTES // (2 * L.N * L.K)))
+    Wd = [W] + [W.clone() for _ in range(n_rd - 1)]
+    kept = L.N * L.K - int(m.sum()) * L.bn * L.bk // 2
+    rows = []
+    for M in (17, 64, 128, 256):
+        Xm = Xall[:M].contiguous()
+        n = max(n_rot, n_rd)
+        Ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        wsh = hts.hts_gemm_workspace(pw0.desc, M)
+        wsd = hts.hts_dense_gemm_workspace(Xm.dtype, M, L.N, L.K)
+        WSh = torch.empty(wsh, dtype=torch.uint8, device=dev) if wsh else None
+        WSd = torch.empty(wsd, dtype=torch.uint8, device=dev) if wsd else None
+        per, reps = (2, 2) if quick else (n, 5)
+        t_h = time_graph(lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n], workspace=WSh), per, reps)
+        t_d = time_graph(lambda i: hts.dense_gemm(Xm, Wd[i % n_rd], out=Ys[i % n], workspace=WSd), per, reps)
+        t_t = time_graph(lambda i: torch.matmul(Xm, Wd[i % n_rd].t(), out=Ys[i % n]), per, reps)
+        rows.append({"M": M, "us": round(t_h * 1e6, 2), "TFLOP/s": round(2.0 * M * kept / t_h / 1e12, 1),
+                     "weight_GB/s": round(pw0.packed_bytes / t_h / 1e9, 1), "workspace_bytes": wsh,
+                     "dense_same_library_us": round(t_d * 1e6, 2), "torch_matmul_us": round(t_t * 1e6, 2),
+                     "speedup_vs_dense": round(t_d / t_h, 3)})
+    return rows
+
+
 def run_shard(hts, wl, dev, time_graph, time_launches, quick):
     """One GPU's share of the 7B up-projection under 8-way column-parallel sharding: tile rows
     0..10 (N = 1408, K = 4096) with their part of the map, at M = 1, 16 (graph-timed) and 2048,
@@ -197,6 +236,10 @@ def run_shard(hts, wl, dev, time_graph, time_launches, quick):
         Xm = Xall[:M].contiguous()
         n = max(n_rot, n_rd)
         Ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        wsh = hts.hts_gemm_workspace(pw0.desc, M)
+        wsd = hts.hts_dense_gemm_workspace(Xm.dtype, M, N, L.K)
+        WSh = torch.empty(wsh, dtype=torch.uint8, device=dev) if wsh else None
+        WSd = torch.empty(wsd, dtype=torch.uint8, device=dev) if wsd else None
         if M <= 16:
             per, reps = (4, 2) if quick else (8 * n_rot, 20)
             t_h = time_graph(lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n]), per, reps)
@@ -204,13 +247,14 @@ def run_shard(hts, wl, dev, time_graph, time_launches, quick):
             t_t = time_graph(lambda i: torch.matmul(Xm, Wd[i % n_rd].t(), out=Ys[i % n]), per, reps)
         else:
             reps = 5 if quick else 60
-            t_h = time_launches(lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n]), reps)
-            t_d = time_launches(lambda i: hts.dense_gemm(Xm, Wd[i % n_rd], out=Ys[i % n]), reps)
+            t_h = time_launches(lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n], workspace=WSh), reps)
+            t_d = time_launches(lambda i: hts.dense_gemm(Xm, Wd[i % n_rd], out=Ys[i % n], workspace=WSd), reps)
             t_t = time_launches(lambda i: torch.matmul(Xm, Wd[i % n_rd].t(), out=Ys[i % n]), reps)
         alg = pw0.packed_bytes + 2 * M * L.K + 2 * M * N
         flops = 2.0 * M * (N * L.K - int(m.sum()) * L.bn * L.bk // 2)    # kept weights only
         row = {"M": M, "us": round(t_h * 1e6, 2), "dense_same_library_us": round(t_d * 1e6, 2),
-               "torch_matmul_us": round(t_t * 1e6, 2), "speedup_vs_dense": round(t_d / t_h, 3)}
+               "torch_matmul_us": round(t_t * 1e6, 2), "speedup_vs_dense": round(t_d / t_h, 3),
+               "workspace_bytes": wsh}
         if M <= 16:
             row["GB/s"] = round(alg / t_h / 1e9, 1)
             row["frac_hbm"] = round(alg / t_h / (HBM_PEAK_GBS * 1e9), 4)
@@ -454,6 +498,7 @@ def main():
     fp8_res = None if args.no_fp8 else run_fp8(hts, wl, dev, time_graph, time_launches, args.quick)
     tiles_res = None if args.no_tiles else run_tile_sizes(hts, wl, dev, time_graph, time_launches, args.quick)
     shard_res = None if args.no_shard else run_shard(hts, wl, dev, time_graph, time_launches, args.quick)
+    mid_res = None if args.no_mid else run_mid_m(hts, wl, dev, time_graph, args.quick)
 
     # ---------------- CPU oracle on the host cores ----------------
     cpu = None
@@ -522,6 +567,7 @@ def main():
         "fp8": fp8_res,
         "tile_sizes": tiles_res,
         "shard": shard_res,
+        "mid_m": mid_res,
         "packed_bytes": packed_bytes,
         "rotation_copies": n_rot,
         "wall_s_timed_region": round(wall, 4),

@@ -205,3 +205,29 @@ def test_gemm_over_mask_packed_weight(M, sparse_path):
     torch.cuda.synchronize()
     assert int(malformed.item()) == 0
     _check(Y.cpu().numpy()[rows], Y_ref, f"masked M={M}")
+
+
+STREAM_ENVS = [{}, {"HTS_DECODE_PP": "2"}, {"HTS_DECODE_KSPLIT": "4"}, {"HTS_DECODE_KSPLIT": "16"},
+               {"HTS_DECODE_NT": "4"}, {"HTS_DECODE_XT_MIN_M": "1"}, {"HTS_DECODE_XT_MIN_M": "17"},
+               {"HTS_DECODE_PP": "2", "HTS_DECODE_KSPLIT": "4", "HTS_DECODE_XT_MIN_M": "1"},
+               {"HTS_DECODE_NT": "4", "HTS_DECODE_XT_MIN_M": "1"}]
+
+
+@pytest.mark.parametrize("env", STREAM_ENVS, ids=lambda e: "-".join(f"{k[11:]}{v}" for k, v in e.items()) or "default")
+@pytest.mark.parametrize("M", [1, 6, 11, 16])
+def test_streaming_launch_shapes(env, M, sparse_path, monkeypatch):
+    # every launch shape of the 16-bit streaming kernel, with X loaded in the operand layout or as
+    # whole rows through LDS, on 128x128 and 64x64 tiles (rows past M repeat row M-1)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    g = np.random.default_rng(4000 + M)
+    for bn, dtype in ((128, "bf16"), (64, "f16")):
+        N, K = 512, 1536
+        W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+        X = wl.gaussian_bits((M, K), 1.0, dtype, g)
+        m = (g.random((N // bn) * (K // bn)) < 0.5).astype(np.uint8)
+        say(f"[stream-shapes] {env} M={M} tile={bn} {sparse_path}")
+        pw = hts.pack(hts.tensor_from_bits(W, dtype, DEV), m, bn, bn)
+        Y = hts.gemm(hts.tensor_from_bits(X, dtype, DEV), pw, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check(Y.cpu().numpy(), oracle.hybrid_ref(X, W, dtype, m, bn, bn), f"{env} M={M} tile={bn}")

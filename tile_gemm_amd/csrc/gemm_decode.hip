@@ -24,6 +24,8 @@
 //   2:4 slice s   : the 8 stored values of row i for dense k in [64s+16g, +16)
 //                   (stored offset 32s + 8g) and the 16-bit code half (g & 1)
 //                   of metadata word 2s + g/2 of that row.
+#include <cstdlib>
+
 #include "gemm_common.h"
 
 namespace hts {
@@ -38,7 +40,7 @@ struct TileRegs {
 
 // Loads of tile column tk for PP consecutive 16-row panels (rows n0 .. n0 + 16 PP - 1, all in
 // one tile row: r0 + 16 PP <= bn) and the matching X chunks.
-template <typename T, int BK, bool HYB, int SP, int PP>
+template <typename T, int BK, bool HYB, int SP, int PP, bool XT>
 __device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArgs& a, const hts_tile& e, int tk,
                                               int64_t n0, int r0, int lane, const uint16_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
@@ -71,9 +73,40 @@ __device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArg
 #pragma unroll
             for (int s = 0; s < BK / 64; ++s) R.m[q][s] = mrow[16 * q * (BK / 32) + 2 * s + (g >> 1)];
     }
+    if constexpr (XT) {
+        // whole X rows: instruction v reads rows 4v .. 4v+3 of the tile column (16 chunks of 16 bytes
+        // each, full cache lines); x_fragments moves them into the operand layout
+        static_assert(BK == 128, "X rows of 128-wide tiles");
 #pragma unroll
-    for (int u = 0; u < BK / 32; ++u) R.x[u] = ld16(xrow + (int64_t)tk * BK + koff<SP>(u, g));
+        for (int v = 0; v < 4; ++v) {
+            const int64_t row = 4 * v + (lane >> 4);
+            R.x[v] = ld16(a.X + (row < a.M ? row : a.M - 1) * a.ldx + (int64_t)tk * BK + 8 * (lane & 15));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < BK / 32; ++u) R.x[u] = ld16(xrow + (int64_t)tk * BK + koff<SP>(u, g));
+    }
     return type;
+}
+
+// X chunks loaded as whole rows (lane L: row 4v + L/16, chunk L%16 of register v) into the operand
+// layout (lane i + 16g, substep u: row i, chunk koff(u, g) / 8) through the wave's own 4 KB of LDS:
+// row r at r * 256 bytes, chunk c in slot c ^ r, so the 16 rows a read instruction serves fall in
+// distinct banks.  LDS operations of one wave complete in order, so the next tile's writes cannot
+// overtake this tile's reads.
+template <int SP>
+__device__ __forceinline__ void x_fragments(u32x4 (&x)[4], uint8_t* buf, int lane) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int row = 4 * v + (lane >> 4), ch = lane & 15;
+        *reinterpret_cast<u32x4*>(buf + row * 256 + 16 * (ch ^ row)) = x[v];
+    }
+    const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = koff<SP>(u, g) / 8;
+        x[u] = *reinterpret_cast<const u32x4*>(buf + i * 256 + 16 * (c ^ i));
+    }
 }
 
 // Index records of the NT tiles of a batch starting at tile column t (clamped to the wave's last
@@ -110,7 +143,7 @@ __device__ __forceinline__ void mma_tile(const TileRegs<BK, PP>& R, uint32_t typ
     }
 }
 
-template <typename T, int BK, bool HYB, int SP, int KS, int NT, int PP>
+template <typename T, int BK, bool HYB, int SP, int KS, int NT, int PP, bool XT>
 __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -126,6 +159,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
     const int i = lane & 15;
     const int64_t j = i < a.M ? i : a.M - 1;
     const uint16_t* xrow = a.X + j * a.ldx;
+    __shared__ __attribute__((aligned(16))) uint8_t xbuf[XT ? KS : 1][XT ? 16 * 256 : 16];   // XT: per-wave X staging
     f32x4 acc[PP];
 #pragma unroll
     for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -138,11 +172,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
         uint32_t type[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP, PP>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
+            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP, PP, XT>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
         if (HYB && t + NT < ke) load_entries<NT>(E, a, t0, t + NT, ke);
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) mma_tile<T, BK, SP, PP>(R[s], type[s], acc, lane);
+            if (t + s < ke) {
+                if constexpr (XT) x_fragments<SP>(R[s].x, xbuf[wave], lane);
+                mma_tile<T, BK, SP, PP>(R[s], type[s], acc, lane);
+            }
     }
 
     __shared__ f32x4 red[KS][PP][64];
@@ -159,6 +196,32 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
     }
 }
 
+// X rows through LDS (x_fragments) from this M on (HTS_DECODE_XT_MIN_M overrides; 17 = never).
+// With few rows the operand-layout loads touch few cache lines and the LDS round trip only adds
+// latency; with many, each such load touches up to 16 half-used lines.  Measured (bf16, 128x128
+// tiles), staged / direct: 7B up (11008 x 4096) M=16 21.6 / 24.6 us, M=8 19.0 / 20.6, M=6
+// 18.6 / 19.4, M=4 18.4 / 18.8, M=2 18.4 / 17.7; 4096 x 4096 M=16 9.7 / 10.5, M=6 8.53 / 8.47,
+// M=5 8.51 / 8.23.
+int decode_xt_min_m() {
+    const char* v = getenv("HTS_DECODE_XT_MIN_M");
+    if (v && *v) {
+        const long x = strtol(v, nullptr, 10);
+        if (x >= 1 && x <= 17) return (int)x;
+    }
+    return 6;
+}
+
+template <typename T, int BK, bool HYB, int SP, int KS, int NT, int PP>
+void launch6(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    if constexpr (BK == 128) {
+        if (a.M >= decode_xt_min_m()) {
+            gemm_decode_kernel<T, BK, HYB, SP, KS, NT, PP, true><<<grid, block, 0, s>>>(a);
+            return;
+        }
+    }
+    gemm_decode_kernel<T, BK, HYB, SP, KS, NT, PP, false><<<grid, block, 0, s>>>(a);
+}
+
 template <typename T, int BK, bool HYB, int SP, int KS, int PP>
 hipError_t launch5(const GemmArgs& a, int nt, hipStream_t s) {
     const dim3 grid((unsigned)(a.N / (16 * PP))), block(64 * KS);
@@ -166,11 +229,11 @@ hipError_t launch5(const GemmArgs& a, int nt, hipStream_t s) {
     // (at most 128 registers per lane) only the 2-column batch fits without spills.
     if constexpr (KS < 16 && PP == 1) {
         if (nt >= 4) {
-            gemm_decode_kernel<T, BK, HYB, SP, KS, 4 * 128 / BK, PP><<<grid, block, 0, s>>>(a);
+            launch6<T, BK, HYB, SP, KS, 4 * 128 / BK, PP>(a, grid, block, s);
             return hipGetLastError();
         }
     }
-    gemm_decode_kernel<T, BK, HYB, SP, KS, 2 * 128 / BK, PP><<<grid, block, 0, s>>>(a);
+    launch6<T, BK, HYB, SP, KS, 2 * 128 / BK, PP>(a, grid, block, s);
     return hipGetLastError();
 }
 

@@ -138,9 +138,12 @@ def test_fp8_strided_x_and_y():
 
 @pytest.mark.parametrize("env", [{}, {"HTS_DECODE_PP": "2"}, {"HTS_DECODE_KSPLIT": "4"},
                                  {"HTS_DECODE_KSPLIT": "16"}, {"HTS_DECODE_NT": "4"},
-                                 {"HTS_DECODE_PP": "2", "HTS_DECODE_KSPLIT": "4"}])
+                                 {"HTS_DECODE_PP": "2", "HTS_DECODE_KSPLIT": "4"},
+                                 {"HTS_DECODE_XT_MIN_M": "17"},
+                                 {"HTS_DECODE_NT": "4", "HTS_DECODE_PP": "2", "HTS_DECODE_XT_MIN_M": "1"}])
 def test_fp8_streaming_launch_shapes(env, monkeypatch):
-    # every launch shape of the 8-bit streaming kernel on the 7B-shaped layer (sampled M = 16)
+    # every launch shape of the 8-bit streaming kernel, X loaded in the operand layout or as whole
+    # rows through LDS, on the 7B-shaped layer (M = 16)
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     c = wl.config("7b_up_fp8")

@@ -279,7 +279,7 @@ struct TileRegs8 {
     u32x4 x[2];       // X chunks, shared by the PP panels
 };
 
-template <bool HYB, int PP>
+template <bool HYB, int PP, bool XT>
 __device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs& a, const hts_tile& e, int tk,
                                                int64_t n0, int r0, int lane, const uint8_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
@@ -309,9 +309,36 @@ __device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs&
 #pragma unroll
         for (int q = 0; q < PP; ++q) R.m[q] = mrow[64 * q + g];
     }
-    R.x[0] = ld16(xrow + (int64_t)tk * 128 + 16 * g);
-    R.x[1] = ld16(xrow + (int64_t)tk * 128 + 64 + 16 * g);
+    if constexpr (XT) {
+        // whole X rows: instruction v reads rows 8v .. 8v+7 of the 128-byte tile column
+        const uint8_t* X8 = reinterpret_cast<const uint8_t*>(a.X);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int64_t row = 8 * v + (lane >> 3);
+            R.x[v] = ld16(X8 + (row < a.M ? row : a.M - 1) * a.ldx + (int64_t)tk * 128 + 16 * (lane & 7));
+        }
+    } else {
+        R.x[0] = ld16(xrow + (int64_t)tk * 128 + 16 * g);
+        R.x[1] = ld16(xrow + (int64_t)tk * 128 + 64 + 16 * g);
+    }
     return type;
+}
+
+// 8-bit X rows (lane L: row 8v + L/8, chunk L%8 of register v) into the operand layout (lane i + 16g:
+// chunks g and 4 + g of row i) through the wave's 2 KB of LDS: row r at r * 128 bytes, chunk c in
+// slot c ^ ((r >> 1) & 7), so the 16 rows a read serves fall in distinct banks.
+__device__ __forceinline__ void x_fragments8(u32x4 (&x)[2], uint8_t* buf, int lane) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const int row = 8 * v + (lane >> 3), ch = lane & 7;
+        *reinterpret_cast<u32x4*>(buf + row * 128 + 16 * (ch ^ ((row >> 1) & 7))) = x[v];
+    }
+    const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = 4 * h + g;
+        x[h] = *reinterpret_cast<const u32x4*>(buf + i * 128 + 16 * (c ^ ((i >> 1) & 7)));
+    }
 }
 
 template <int PP>
@@ -329,7 +356,7 @@ __device__ __forceinline__ void mma_tile8(const TileRegs8<PP>& R, uint32_t type,
     }
 }
 
-template <bool HYB, int KS, int NT, int PP>
+template <bool HYB, int KS, int NT, int PP, bool XT>
 __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -344,6 +371,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a)
     const int i = lane & 15;
     const int64_t j = i < a.M ? i : a.M - 1;
     const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.X) + j * a.ldx;
+    __shared__ __attribute__((aligned(16))) uint8_t xbuf[XT ? KS : 1][XT ? 16 * 128 : 16];   // XT: per-wave X staging
     f32x4 acc[PP];
 #pragma unroll
     for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -354,11 +382,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a)
         uint32_t type[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) type[s] = load_tile8<HYB, PP>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
+            if (t + s < ke) type[s] = load_tile8<HYB, PP, XT>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
         if (HYB && t + NT < ke) load_entries<NT>(E, a, t0, t + NT, ke);
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) mma_tile8<PP>(R[s], type[s], acc);
+            if (t + s < ke) {
+                if constexpr (XT) x_fragments8(R[s].x, xbuf[wave], lane);
+                mma_tile8<PP>(R[s], type[s], acc);
+            }
     }
 
     __shared__ f32x4 red[KS][PP][64];
@@ -374,17 +405,23 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a)
     }
 }
 
+template <bool HYB, int KS, int NT, int PP>
+void launch8x(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.M >= decode_xt_min_m()) gemm_decode8_kernel<HYB, KS, NT, PP, true><<<grid, block, 0, s>>>(a);
+    else gemm_decode8_kernel<HYB, KS, NT, PP, false><<<grid, block, 0, s>>>(a);
+}
+
 template <bool HYB, int KS, int PP>
 hipError_t launch8_nt(const GemmArgs& a, int nt, hipStream_t s) {
     const dim3 grid((unsigned)(a.N / (16 * PP))), block(64 * KS);
     // nt counts 16-bit 128x128 tile columns; an 8-bit tile column is half the bytes
     if constexpr (KS < 16 && PP == 1) {
         if (nt >= 4) {
-            gemm_decode8_kernel<HYB, KS, 8, PP><<<grid, block, 0, s>>>(a);
+            launch8x<HYB, KS, 8, PP>(a, grid, block, s);
             return hipGetLastError();
         }
     }
-    gemm_decode8_kernel<HYB, KS, 4, PP><<<grid, block, 0, s>>>(a);
+    launch8x<HYB, KS, 4, PP>(a, grid, block, s);
     return hipGetLastError();
 }
 

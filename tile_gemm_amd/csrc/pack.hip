@@ -2,10 +2,10 @@
 //
 // One workgroup per tile (page "PATCH: Learnable Tile-level Hybrid Sparsity for
 // LLMs", section 2: the dense / 2:4 decision is made per tile).  Each thread
-// handles 32 consecutive weights of one tile row: four 16-byte loads, and either
-// a raw copy (dense tile) or eight 2-of-4 selections producing 16 kept values
-// and one 32-bit metadata word (2:4 tile).  The pass is bound by HBM bandwidth:
-// it reads W once and writes the packed bytes once.
+// handles one 16-byte chunk of a tile row per step: a raw copy (dense tile) or
+// two (four for 8-bit weights) 2-of-4 selections producing the kept values and
+// their codes (2:4 tile).  The pass is bound by HBM bandwidth: it reads W once
+// and writes the packed bytes once.
 #include "device_common.h"
 #include "hts_internal.h"
 
@@ -13,6 +13,7 @@ namespace hts {
 namespace {
 
 constexpr int kPackThreads = 256;
+constexpr int kInFlight = 4;   // 16-byte chunks a pack thread loads before it uses any
 
 // Score of one weight: |w| as binary32, times the column scale when given
 // (a single IEEE multiply: nothing to contract).
@@ -44,6 +45,11 @@ __device__ __forceinline__ void pick_two(const float s[4], uint32_t& i0, uint32_
 // PATCH-Tile variant freezes 2:4 patterns from a one-shot method): the score of a weight is 1
 // where the mask byte is nonzero, else 0, under the same rank rule, so a group marking exactly
 // two weights keeps those two.  Groups marking another number are counted into *malformed.
+//
+// Work split: a thread takes one 16-byte chunk of a tile row per step (8 weights = two groups),
+// consecutive lanes on consecutive chunks, so every load and store of a wave covers whole cache
+// lines.  A 2:4 chunk becomes 8 stored bytes and one metadata byte: the codes of its two groups
+// (group g's nibble is bits 4(g%8).. of word g/8 of the row, so groups 2c and 2c+1 are byte c).
 template <typename T, bool MASKED>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     const hts_tile* __restrict__ index, int64_t Tk, int bn, int bk,
@@ -54,72 +60,72 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     uint32_t bad = 0;
     const hts_tile e = index[t];
     const int64_t tn = t / Tk, tk = t % Tk;
-    const int wpr = bk / 32;                       // 32-weight chunks per tile row
-    const int items = bn * wpr;
-    for (int it = threadIdx.x; it < items; it += kPackThreads) {
-        const int r = it / wpr, w = it % wpr;
-        const int64_t k0 = tk * bk + 32 * w;
-        const uint16_t* src = W + (tn * bn + r) * ldw + k0;
-        u32x4 q[4];
+    const int cpr = bk / 8;                        // 16-byte chunks per tile row
+    const int items = bn * cpr;
+    uint8_t* mbytes = reinterpret_cast<uint8_t*>(meta + e.meta_off);
+    // kInFlight chunks per thread are loaded before any is used (guarded: small tiles have fewer
+    // chunks than kInFlight x 256)
+    for (int base = threadIdx.x; base < items; base += kInFlight * kPackThreads) {
+        u32x4 qs[kInFlight];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) q[c] = ld16(src + 8 * c);
-        if (e.type == HTS_TILE_DENSE) {
-            uint16_t* dst = values + e.val_off + (int64_t)r * bk + 32 * w;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) st16(dst + 8 * c, q[c]);
-            continue;
-        }
-        uint32_t kept[8];   // 16 kept 16-bit values, two per word
-        uint32_t word = 0;
-        u32x4 mk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};   // 32 mask bytes of the chunk
-        if (MASKED) {
-            const uint8_t* msrc = mask + (tn * bn + r) * ldm + k0;
-            mk[0] = *reinterpret_cast<const u32x4*>(msrc);
-            mk[1] = *reinterpret_cast<const u32x4*>(msrc + 16);
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads;
+            if (it < items) qs[j] = ld16(W + (tn * bn + it / cpr) * ldw + tk * bk + 8 * (it % cpr));
         }
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            // group g = weights 4g..4g+3 of this chunk = dwords 2g, 2g+1
-            const uint32_t d0 = q[g / 2][(2 * g) % 4], d1 = q[g / 2][(2 * g + 1) % 4];
-            const uint32_t b[4] = {d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16};
-            float s[4];
-            if (MASKED) {
-                const uint32_t mw = mk[g / 4][g % 4];            // mask bytes of weights 4g..4g+3
-                int marked = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool on = ((mw >> (8 * i)) & 0xFFu) != 0u;
-                    s[i] = on ? 1.0f : 0.0f;
-                    marked += on;
-                }
-                bad += marked != 2;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[i] = score<T>(b[i], cs, k0 + 4 * g + i);
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads;
+            if (it >= items) break;
+            const int r = it / cpr, c = it % cpr;
+            const int64_t k0 = tk * bk + 8 * c;
+            const u32x4 q = qs[j];
+            if (e.type == HTS_TILE_DENSE) {
+                st16(values + e.val_off + (int64_t)r * bk + 8 * c, q);
+                continue;
             }
-            uint32_t i0, i1;
-            pick_two(s, i0, i1);
-            uint32_t v0 = b[0], v1 = b[1];
-            v0 = (i0 == 1u) ? b[1] : v0;
-            v0 = (i0 == 2u) ? b[2] : v0;
-            v1 = (i1 == 2u) ? b[2] : v1;
-            v1 = (i1 == 3u) ? b[3] : v1;
-            kept[g] = v0 | (v1 << 16);
-            word |= (i0 | (i1 << 2)) << (4 * g);
+            uint2 mk = {0u, 0u};   // mask bytes of the chunk's 8 weights
+            if (MASKED) mk = *reinterpret_cast<const uint2*>(mask + (tn * bn + r) * ldm + k0);
+            uint32_t kept[2];      // kept pair of each group, two 16-bit values per word
+            uint32_t code = 0;
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const uint32_t d0 = q[2 * g], d1 = q[2 * g + 1];
+                const uint32_t b[4] = {d0 & 0xFFFFu, d0 >> 16, d1 & 0xFFFFu, d1 >> 16};
+                float s[4];
+                if (MASKED) {
+                    const uint32_t mw = g ? mk.y : mk.x;      // mask bytes of the group's four weights
+                    int marked = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool on = ((mw >> (8 * i)) & 0xFFu) != 0u;
+                        s[i] = on ? 1.0f : 0.0f;
+                        marked += on;
+                    }
+                    bad += marked != 2;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[i] = score<T>(b[i], cs, k0 + 4 * g + i);
+                }
+                uint32_t i0, i1;
+                pick_two(s, i0, i1);
+                uint32_t v0 = b[0], v1 = b[1];
+                v0 = (i0 == 1u) ? b[1] : v0;
+                v0 = (i0 == 2u) ? b[2] : v0;
+                v1 = (i1 == 2u) ? b[2] : v1;
+                v1 = (i1 == 3u) ? b[3] : v1;
+                kept[g] = v0 | (v1 << 16);
+                code |= (i0 | (i1 << 2)) << (4 * g);
+            }
+            *reinterpret_cast<uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 4 * c) = uint2{kept[0], kept[1]};
+            mbytes[(int64_t)r * (bk / 8) + c] = (uint8_t)code;
         }
-        uint16_t* dst = values + e.val_off + (int64_t)r * (bk / 2) + 16 * w;
-        u32x4 o0 = {kept[0], kept[1], kept[2], kept[3]};
-        u32x4 o1 = {kept[4], kept[5], kept[6], kept[7]};
-        st16(dst, o0);
-        st16(dst + 8, o1);
-        meta[e.meta_off + (int64_t)r * wpr + w] = word;
     }
     if (MASKED && malformed && bad) atomicAdd(malformed, bad);
 }
 
-// The same pass for 8-bit E4M3 weights: a thread takes 32 consecutive bytes of a tile row (two
-// 16-byte loads); a 2:4 chunk becomes 16 kept bytes (one 16-byte store) and the same 32-bit code
-// word as above.  The score is |w| decoded exactly (times the column scale when given).
+// The same pass for 8-bit E4M3 weights: a 16-byte chunk is 16 weights (four groups); a 2:4 chunk
+// becomes 8 kept bytes and 16 bits of codes (metadata bytes 2c, 2c+1 of the row).  The score is
+// |w| decoded exactly (times the column scale when given).
 template <bool MASKED>
 __global__ __launch_bounds__(kPackThreads) void pack8_kernel(
     const hts_tile* __restrict__ index, int64_t Tk, int bn, int bk,
@@ -130,69 +136,74 @@ __global__ __launch_bounds__(kPackThreads) void pack8_kernel(
     uint32_t bad = 0;
     const hts_tile e = index[t];
     const int64_t tn = t / Tk, tk = t % Tk;
-    const int wpr = bk / 32;
-    const int items = bn * wpr;
-    for (int it = threadIdx.x; it < items; it += kPackThreads) {
-        const int r = it / wpr, w = it % wpr;
-        const int64_t k0 = tk * bk + 32 * w;
-        const uint8_t* src = W + (tn * bn + r) * ldw + k0;
-        const u32x4 q0 = ld16(src), q1 = ld16(src + 16);
-        if (e.type == HTS_TILE_DENSE) {
-            uint8_t* dst = values + e.val_off + (int64_t)r * bk + 32 * w;
-            st16(dst, q0);
-            st16(dst + 16, q1);
-            continue;
+    const int cpr = bk / 16;
+    const int items = bn * cpr;
+    uint16_t* mhalves = reinterpret_cast<uint16_t*>(meta + e.meta_off);
+    for (int base = threadIdx.x; base < items; base += kInFlight * kPackThreads) {
+        u32x4 qs[kInFlight];
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads;
+            if (it < items) qs[j] = ld16(W + (tn * bn + it / cpr) * ldw + tk * bk + 16 * (it % cpr));
         }
-        const uint32_t d[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};   // group g = d[g]
-        u32x4 mk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-        if (MASKED) {
-            const uint8_t* msrc = mask + (tn * bn + r) * ldm + k0;
-            mk[0] = *reinterpret_cast<const u32x4*>(msrc);
-            mk[1] = *reinterpret_cast<const u32x4*>(msrc + 16);
-        }
-        uint32_t kept[8];   // kept pair of group g: low byte = lower index
-        uint32_t word = 0;
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const uint32_t b[4] = {d[g] & 0xFFu, (d[g] >> 8) & 0xFFu, (d[g] >> 16) & 0xFFu, d[g] >> 24};
-            float sc[4];
-            if (MASKED) {
-                const uint32_t mw = mk[g / 4][g % 4];
-                int marked = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool on = ((mw >> (8 * i)) & 0xFFu) != 0u;
-                    sc[i] = on ? 1.0f : 0.0f;
-                    marked += on;
-                }
-                bad += marked != 2;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float a = fabsf(widen_e4m3(b[i]));
-                    sc[i] = cs ? a * cs[k0 + 4 * g + i] : a;
-                }
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads;
+            if (it >= items) break;
+            const int r = it / cpr, c = it % cpr;
+            const int64_t k0 = tk * bk + 16 * c;
+            const u32x4 q = qs[j];
+            if (e.type == HTS_TILE_DENSE) {
+                st16(values + e.val_off + (int64_t)r * bk + 16 * c, q);
+                continue;
             }
-            uint32_t i0, i1;
-            pick_two(sc, i0, i1);
-            uint32_t v0 = b[0], v1 = b[1];
-            v0 = (i0 == 1u) ? b[1] : v0;
-            v0 = (i0 == 2u) ? b[2] : v0;
-            v1 = (i1 == 2u) ? b[2] : v1;
-            v1 = (i1 == 3u) ? b[3] : v1;
-            kept[g] = v0 | (v1 << 8);
-            word |= (i0 | (i1 << 2)) << (4 * g);
+            u32x4 mk = {0u, 0u, 0u, 0u};
+            if (MASKED) mk = *reinterpret_cast<const u32x4*>(mask + (tn * bn + r) * ldm + k0);
+            uint32_t kept[4];   // kept pair of group g: low byte = lower index
+            uint32_t code = 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t d = q[g];
+                const uint32_t b[4] = {d & 0xFFu, (d >> 8) & 0xFFu, (d >> 16) & 0xFFu, d >> 24};
+                float sc[4];
+                if (MASKED) {
+                    const uint32_t mw = mk[g];
+                    int marked = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool on = ((mw >> (8 * i)) & 0xFFu) != 0u;
+                        sc[i] = on ? 1.0f : 0.0f;
+                        marked += on;
+                    }
+                    bad += marked != 2;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float a = fabsf(widen_e4m3(b[i]));
+                        sc[i] = cs ? a * cs[k0 + 4 * g + i] : a;
+                    }
+                }
+                uint32_t i0, i1;
+                pick_two(sc, i0, i1);
+                uint32_t v0 = b[0], v1 = b[1];
+                v0 = (i0 == 1u) ? b[1] : v0;
+                v0 = (i0 == 2u) ? b[2] : v0;
+                v1 = (i1 == 2u) ? b[2] : v1;
+                v1 = (i1 == 3u) ? b[3] : v1;
+                kept[g] = v0 | (v1 << 8);
+                code |= (i0 | (i1 << 2)) << (4 * g);
+            }
+            *reinterpret_cast<uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 8 * c) =
+                uint2{kept[0] | (kept[1] << 16), kept[2] | (kept[3] << 16)};
+            mhalves[(int64_t)r * (bk / 16) + c] = (uint16_t)code;
         }
-        uint8_t* dst = values + e.val_off + (int64_t)r * (bk / 2) + 16 * w;
-        st16(dst, u32x4{kept[0] | (kept[1] << 16), kept[2] | (kept[3] << 16), kept[4] | (kept[5] << 16),
-                        kept[6] | (kept[7] << 16)});
-        meta[e.meta_off + (int64_t)r * wpr + w] = word;
     }
     if (MASKED && malformed && bad) atomicAdd(malformed, bad);
 }
 
 __global__ void zero_counter(uint32_t* c) { *c = 0u; }
 
+// Inverse passes, one 16-byte output chunk per thread and step (as the packs above).
 __global__ __launch_bounds__(kPackThreads) void unpack_kernel(
     const hts_tile* __restrict__ index, int64_t Tk, int bn, int bk,
     const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
@@ -200,25 +211,29 @@ __global__ __launch_bounds__(kPackThreads) void unpack_kernel(
     const int64_t t = blockIdx.x;
     const hts_tile e = index[t];
     const int64_t tn = t / Tk, tk = t % Tk;
-    const int wpr = bk / 32;
-    const int items = bn * wpr;
-    for (int it = threadIdx.x; it < items; it += kPackThreads) {
-        const int r = it / wpr, w = it % wpr;
-        uint16_t* dst = W + (tn * bn + r) * ldw + tk * bk + 32 * w;
-        if (e.type == HTS_TILE_DENSE) {
-            const uint16_t* src = values + e.val_off + (int64_t)r * bk + 32 * w;
+    const int cpr = bk / 8;
+    const int items = bn * cpr;
+    const uint8_t* mbytes = reinterpret_cast<const uint8_t*>(meta + e.meta_off);
+    const bool dense = e.type == HTS_TILE_DENSE;
+    for (int base = threadIdx.x; base < items; base += kInFlight * kPackThreads) {
+        u32x4 q[kInFlight];        // dense: the chunk; 2:4: stored values in .x, .y and the code byte in .z
 #pragma unroll
-            for (int c = 0; c < 4; ++c) st16(dst + 8 * c, ld16(src + 8 * c));
-            continue;
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            if (it >= items) break;
+            if (dense) {
+                q[j] = ld16(values + e.val_off + (int64_t)r * bk + 8 * c);
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 4 * c);
+                q[j] = u32x4{v.x, v.y, mbytes[(int64_t)r * (bk / 8) + c], 0u};
+            }
         }
-        const uint16_t* src = values + e.val_off + (int64_t)r * (bk / 2) + 16 * w;
-        const u32x4 a = ld16(src), b = ld16(src + 8);
-        const uint32_t word = meta[e.meta_off + (int64_t)r * wpr + w];
-        const uint32_t kv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {   // output chunk c = groups 2c, 2c+1
-            uint2 v = {kv[2 * c], kv[2 * c + 1]};
-            st16(dst + 8 * c, expand_two_groups(v, (word >> (8 * c)) & 0xFFu));
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            if (it >= items) break;
+            uint16_t* dst = W + (tn * bn + r) * ldw + tk * bk + 8 * c;
+            st16(dst, dense ? q[j] : expand_two_groups(uint2{q[j][0], q[j][1]}, q[j][2]));
         }
     }
 }
@@ -230,28 +245,41 @@ __global__ __launch_bounds__(kPackThreads) void unpack8_kernel(
     const int64_t t = blockIdx.x;
     const hts_tile e = index[t];
     const int64_t tn = t / Tk, tk = t % Tk;
-    const int wpr = bk / 32;
-    const int items = bn * wpr;
-    for (int it = threadIdx.x; it < items; it += kPackThreads) {
-        const int r = it / wpr, w = it % wpr;
-        uint8_t* dst = W + (tn * bn + r) * ldw + tk * bk + 32 * w;
-        if (e.type == HTS_TILE_DENSE) {
-            const uint8_t* src = values + e.val_off + (int64_t)r * bk + 32 * w;
-            st16(dst, ld16(src));
-            st16(dst + 16, ld16(src + 16));
-            continue;
-        }
-        const u32x4 kv = ld16(values + e.val_off + (int64_t)r * (bk / 2) + 16 * w);
-        const uint32_t word = meta[e.meta_off + (int64_t)r * wpr + w];
-        uint32_t out[8];
+    const int cpr = bk / 16;
+    const int items = bn * cpr;
+    const uint16_t* mhalves = reinterpret_cast<const uint16_t*>(meta + e.meta_off);
+    const bool dense = e.type == HTS_TILE_DENSE;
+    for (int base = threadIdx.x; base < items; base += kInFlight * kPackThreads) {
+        u32x4 q[kInFlight];        // dense: the chunk; 2:4: kept bytes in .x, .y and the codes in .z
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {   // group g: kept bytes 2g, 2g+1 of the chunk
-            const uint32_t pair = (kv[g / 2] >> (16 * (g & 1))) & 0xFFFFu;
-            const uint32_t code = (word >> (4 * g)) & 0xFu, i0 = code & 3u, i1 = code >> 2;
-            out[g] = ((pair & 0xFFu) << (8 * i0)) | ((pair >> 8) << (8 * i1));
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            if (it >= items) break;
+            if (dense) {
+                q[j] = ld16(values + e.val_off + (int64_t)r * bk + 16 * c);
+            } else {
+                const uint2 kv = *reinterpret_cast<const uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 8 * c);
+                q[j] = u32x4{kv.x, kv.y, mhalves[(int64_t)r * (bk / 16) + c], 0u};
+            }
         }
-        st16(dst, u32x4{out[0], out[1], out[2], out[3]});
-        st16(dst + 16, u32x4{out[4], out[5], out[6], out[7]});
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            if (it >= items) break;
+            uint8_t* dst = W + (tn * bn + r) * ldw + tk * bk + 16 * c;
+            if (dense) {
+                st16(dst, q[j]);
+                continue;
+            }
+            uint32_t out[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {   // group g: kept bytes 2g, 2g+1 of the chunk's 8
+                const uint32_t pair = ((g < 2 ? q[j][0] : q[j][1]) >> (16 * (g & 1))) & 0xFFFFu;
+                const uint32_t code = (q[j][2] >> (4 * g)) & 0xFu, i0 = code & 3u, i1 = code >> 2;
+                out[g] = ((pair & 0xFFu) << (8 * i0)) | ((pair >> 8) << (8 * i1));
+            }
+            st16(dst, u32x4{out[0], out[1], out[2], out[3]});
+        }
     }
 }
 

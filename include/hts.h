@@ -93,12 +93,16 @@ typedef struct {
 } hts_sizes;
 
 /* Packed format (bit-exact contract of hts_pack / hts_unpack):
- *   dense tile : bn*bk values, row-major inside the tile, raw bits of W.
- *   2:4 tile   : per tile row r and group g of four weights (k = 4g..4g+3
- *                from the tile start) the two kept weights, lower index first,
- *                at values[val_off + r*(bk/2) + 2g + {0,1}] (raw bits); and the
- *                4-bit code i0 | (i1 << 2) (i0 < i1 the kept positions in the
- *                group) at bits 4*(g%8)..+3 of meta[meta_off + r*(bk/32) + g/8].
+ *   dense tile : the bn x bk weights (raw bits of W) as rows of bk values.
+ *   2:4 tile   : rows of bk/2 values: for tile row r and group g of four weights (k = 4g..4g+3
+ *                from the tile start) the two kept weights, lower index first, at row position
+ *                2g + {0,1} (raw bits); and the 4-bit code i0 | (i1 << 2) (i0 < i1 the kept
+ *                positions in the group) at bits 4*(g%8)..+3 of meta[meta_off + r*(bk/32) + g/8].
+ *   Storage order of the rows of a tile (from values[val_off]): 16-row panels, one after another;
+ *   each row cut into 16-byte chunks (8 values of 16 bits, 16 of 8 bits); inside a panel the
+ *   chunks column by column, the panel's 16 rows consecutive in each: chunk c of row r is at
+ *   ((r / 16) * 16 * row_length + (c * 16 + r % 16) * chunk_length) values.  The four chunks of
+ *   16 consecutive rows that feed one matrix-core instruction are then one contiguous kilobyte.
  *   Kept pair: the two largest scores of the group, the lower index first among
  *   equal scores.  Score = |w| as binary32, or the binary32 product |w| * c[k]
  *   when a column scale c is given (the Wanda rule: weight magnitude times the

@@ -205,6 +205,32 @@ def plan(tile_map: np.ndarray, N: int, K: int, bn: int, bk: int, elem_bytes: int
     return index, sizes
 
 
+# Storage order inside a tile (a format choice of this library, not of the pages): a tile's rows
+# (dense: all bk weights; 2:4: the bk/2 kept weights) are cut into 16-row panels -- the whole tile
+# when bn is not a multiple of 16 -- and into 16-byte chunks along the row.  Inside a panel the
+# chunks are stored column by column, the panel's rows consecutive within a chunk column: chunk c
+# of panel row r is at (c * panel_rows + r) chunks from the panel start.  A matrix-core operand
+# (one chunk of each of 16 consecutive rows, for four consecutive chunk columns) is then one
+# contiguous kilobyte.
+
+def panel_rows(bn: int) -> int:
+    return 16 if bn % 16 == 0 else bn
+
+
+def panel_order(block: np.ndarray, elem_bytes: int) -> np.ndarray:
+    """The elements of a row-major [rows, w] block of one tile, flattened in storage order."""
+    rows, w = block.shape
+    ph, ch = panel_rows(rows), 16 // elem_bytes
+    assert w % ch == 0
+    return block.reshape(rows // ph, ph, w // ch, ch).transpose(0, 2, 1, 3).ravel()
+
+
+def panel_unorder(flat: np.ndarray, rows: int, w: int, elem_bytes: int) -> np.ndarray:
+    """Inverse of panel_order: the row-major [rows, w] block."""
+    ph, ch = panel_rows(rows), 16 // elem_bytes
+    return np.asarray(flat).reshape(rows // ph, w // ch, ph, ch).transpose(0, 2, 1, 3).reshape(rows, w)
+
+
 def pack(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int, bk: int,
          col_scale: np.ndarray | None = None, scores: np.ndarray | None = None):
     """(values, meta uint32, index uint32[T,4]) of W under the tile map (values in the storage
@@ -214,6 +240,7 @@ def pack(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int, bk: int,
     (see pack_masked)."""
     N, K = W_bits.shape
     st = storage_type(dtype)
+    eb = np.dtype(st).itemsize
     index, sizes = plan(tile_map, N, K, bn, bk)
     tmap = index[:, 2]
     tiles = as_tiles(np.asarray(W_bits, dtype=st), bn, bk)
@@ -225,14 +252,15 @@ def pack(W_bits: np.ndarray, dtype: str, tile_map: np.ndarray, bn: int, bk: int,
     G = bk // 4
     for t in range(tiles.shape[0]):
         if tmap[t] == TILE_DENSE:
-            values.append(tiles[t].ravel())
+            values.append(panel_order(tiles[t], eb))
             continue
         keep = sparse_tile_keep(stiles[t]).reshape(bn, G, 4)
         i0, i1 = kept_positions(keep)                       # [bn, G]
         groups = tiles[t].reshape(bn, G, 4)
         v0 = np.take_along_axis(groups, i0[..., None], axis=-1)[..., 0]
         v1 = np.take_along_axis(groups, i1[..., None], axis=-1)[..., 0]
-        values.append(np.stack([v0, v1], axis=-1).ravel())  # row r: (g, lower/higher)
+        kept = np.stack([v0, v1], axis=-1).reshape(bn, bk // 2)   # row r: (g, lower/higher)
+        values.append(panel_order(kept, eb))
         nib = (i0 | (i1 << 2)).astype(np.uint32).reshape(bn, G // 8, 8)
         shifts = (4 * np.arange(8)).astype(np.uint32)
         words = np.bitwise_or.reduce(nib << shifts, axis=-1)  # [bn, bk/32]
@@ -300,13 +328,14 @@ def unpack(values: np.ndarray, meta: np.ndarray, index: np.ndarray, N: int, K: i
     assert index.shape == (T, 4)
     G = bk // 4
     values = np.asarray(values)
+    eb = values.dtype.itemsize
     tiles = np.zeros((T, bn, bk), dtype=values.dtype)
     for t in range(T):
         val_off, meta_off, typ, _ = (int(x) for x in index[t])
         if typ == TILE_DENSE:
-            tiles[t] = values[val_off: val_off + bn * bk].reshape(bn, bk)
+            tiles[t] = panel_unorder(values[val_off: val_off + bn * bk], bn, bk, eb)
             continue
-        pairs = values[val_off: val_off + bn * bk // 2].reshape(bn, G, 2)
+        pairs = panel_unorder(values[val_off: val_off + bn * bk // 2], bn, bk // 2, eb).reshape(bn, G, 2)
         words = meta[meta_off: meta_off + bn * bk // 32].reshape(bn, G // 8).astype(np.uint32)
         nib = (words[..., None] >> (4 * np.arange(8)).astype(np.uint32)) & np.uint32(0xF)
         nib = nib.reshape(bn, G)

@@ -231,8 +231,6 @@ def test_split_product_workspace_sizes(monkeypatch):
     # 32-wide tiles: the unpacked weight, then the parts of the dense product
     d32 = hts.make_desc(N, K, 32, 32, "bf16")
     assert hts.hts_gemm_workspace(d32, 17) == N * K * 2 + _r256(5 * 17 * N * 4)
-    # overrides: a forced count, and the two-tile-row block shapes (never split)
+    # override: a forced count
     monkeypatch.setenv("HTS_PREFILL_SPLIT", "3")
     assert hts.hts_gemm_workspace(d, 300) == _r256(3 * 300 * N * 4)
-    monkeypatch.setenv("HTS_PREFILL_TILE", "p256")
-    assert hts.hts_gemm_workspace(d, 300) == 0

@@ -79,10 +79,27 @@ def brute_pair(scores):
     return best
 
 
+def brute_place(rows, elem_bytes):
+    """Storage order of one tile's rows (equal-length lists), element by element: 16-row panels
+    (the whole tile when its row count is not a multiple of 16), 16-byte chunks along a row,
+    chunk columns one after another with the panel's rows consecutive inside each."""
+    n, w = len(rows), len(rows[0])
+    ph = 16 if n % 16 == 0 else n
+    ch = 16 // elem_bytes
+    out = [None] * (n * w)
+    for r in range(n):
+        for j in range(w):
+            panel, rr = divmod(r, ph)
+            cc, e = divmod(j, ch)
+            out[panel * ph * w + (cc * ph + rr) * ch + e] = rows[r][j]
+    return out
+
+
 def brute_mask_and_pack(Wb, dtype, tmap, bn, bk, c=None):
     """Pure-Python masking and packing, element by element."""
     N, K = Wb.shape
     Tk = K // bk
+    eb = 1 if dtype == "fp8" else 2
     Wm = [[int(Wb[n, k]) for k in range(K)] for n in range(N)]
     values, meta, index = [], [], []
     voff = moff = 0
@@ -91,19 +108,20 @@ def brute_mask_and_pack(Wb, dtype, tmap, bn, bk, c=None):
             t = tn * Tk + tk
             index.append((voff, moff, int(tmap[t]), 0))
             if tmap[t] == 0:
-                for r in range(bn):
-                    for cc in range(bk):
-                        values.append(int(Wb[tn * bn + r, tk * bk + cc]))
+                values += brute_place([[int(Wb[tn * bn + r, tk * bk + cc]) for cc in range(bk)]
+                                       for r in range(bn)], eb)
                 voff += bn * bk
                 continue
+            kept_rows = []
             for r in range(bn):
                 n = tn * bn + r
                 word, nword = 0, 0
+                kept = []
                 for g in range(bk // 4):
                     ks = [tk * bk + 4 * g + i for i in range(4)]
                     sc = [brute_score(Wb[n, k], dtype, None if c is None else c[k]) for k in ks]
                     i0, i1 = brute_pair(sc)
-                    values += [int(Wb[n, ks[i0]]), int(Wb[n, ks[i1]])]
+                    kept += [int(Wb[n, ks[i0]]), int(Wb[n, ks[i1]])]
                     for i in range(4):
                         if i not in (i0, i1):
                             Wm[n][ks[i]] = 0
@@ -111,6 +129,8 @@ def brute_mask_and_pack(Wb, dtype, tmap, bn, bk, c=None):
                     if g % 8 == 7:
                         meta.append(word)
                         word, nword = 0, nword + 1
+                kept_rows.append(kept)
+            values += brute_place(kept_rows, eb)
             voff += bn * bk // 2
             moff += bn * bk // 32
     st = np.uint8 if dtype == "fp8" else np.uint16
@@ -408,7 +428,8 @@ def test_golden_pack_from_mask(dtype):
     assert bad == 0
     assert [f"{int(w):08X}" for w in meta] == gold["meta_hex"]
     assert np.array_equal(vals[:32], _bits(gold["values_tile0"], dtype))
-    assert np.array_equal(vals[32:], W[:, 32:].ravel())
+    # the dense tile: chunks of 8 values, chunk column by chunk column, the two rows consecutive
+    assert np.array_equal(vals[32:], np.concatenate([W[r, 32 + 8 * c: 40 + 8 * c] for c in range(4) for r in range(2)]))
 
 
 def _random_pair_mask(N, K, g):

@@ -45,29 +45,32 @@ __device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArg
                                               int64_t n0, int r0, int lane, const uint16_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
-    const uint16_t* base;
-    int64_t rstride;
     uint32_t moff = 0;
     if (HYB) {
         type = e.type;
         moff = e.meta_off;
-        rstride = type == HTS_TILE_DENSE ? BK : BK / 2;
-        base = a.values + e.val_off + (int64_t)(r0 + i) * rstride;
-    } else {
-        rstride = a.ldw;
-        base = a.W + (n0 + i) * a.ldw + (int64_t)tk * BK;
     }
-    if (type == HTS_TILE_DENSE) {
+    if (!HYB) {        // row-major W: lane i reads row i
+        const uint16_t* base = a.W + (n0 + i) * a.ldw + (int64_t)tk * BK;
 #pragma unroll
         for (int q = 0; q < PP; ++q)
 #pragma unroll
-            for (int u = 0; u < BK / 32; ++u) R.a[q][u] = ld16(base + 16 * q * rstride + koff<SP>(u, g));
+            for (int u = 0; u < BK / 32; ++u) R.a[q][u] = ld16(base + 16 * q * a.ldw + koff<SP>(u, g));
+    } else if (type == HTS_TILE_DENSE) {
+        // packed tile: 16-row panels of BK-element rows, chunk c of panel row i at (16 c + i) chunks
+        // from the panel start -- the four chunks of a substep are one contiguous kilobyte
+        const uint16_t* panel = a.values + e.val_off + (int64_t)r0 * BK;
+#pragma unroll
+        for (int q = 0; q < PP; ++q)
+#pragma unroll
+            for (int u = 0; u < BK / 32; ++u) R.a[q][u] = ld16(panel + 16 * q * BK + (16 * (koff<SP>(u, g) / 8) + i) * 8);
     } else {
         const uint32_t* mrow = a.meta + moff + (int64_t)(r0 + i) * (BK / 32);
+        const uint16_t* panel = a.values + e.val_off + (int64_t)r0 * (BK / 2);   // stored rows: BK/2 values
 #pragma unroll
         for (int q = 0; q < PP; ++q)
 #pragma unroll
-            for (int s = 0; s < BK / 64; ++s) R.a[q][s] = ld16(base + 16 * q * rstride + 32 * s + 8 * g);
+            for (int s = 0; s < BK / 64; ++s) R.a[q][s] = ld16(panel + 16 * q * (BK / 2) + (16 * (4 * s + g) + i) * 8);
 #pragma unroll
         for (int q = 0; q < PP; ++q)
 #pragma unroll
@@ -284,28 +287,32 @@ __device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs&
                                                int64_t n0, int r0, int lane, const uint8_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
-    const uint8_t* base;
-    int64_t rstride;
     uint32_t moff = 0;
     if (HYB) {
         type = e.type;
         moff = e.meta_off;
-        rstride = type == HTS_TILE_DENSE ? 128 : 64;
-        base = reinterpret_cast<const uint8_t*>(a.values) + e.val_off + (int64_t)(r0 + i) * rstride;
-    } else {
-        rstride = a.ldw;
-        base = reinterpret_cast<const uint8_t*>(a.W) + (n0 + i) * a.ldw + (int64_t)tk * 128;
     }
-    if (type == HTS_TILE_DENSE) {
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.values) + e.val_off;
+    if (!HYB) {        // row-major W: lane i reads row i
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.W) + (n0 + i) * a.ldw + (int64_t)tk * 128;
 #pragma unroll
         for (int q = 0; q < PP; ++q) {
-            R.a[q][0] = ld16(base + 16 * q * rstride + 16 * g);
-            R.a[q][1] = ld16(base + 16 * q * rstride + 64 + 16 * g);
+            R.a[q][0] = ld16(base + 16 * q * a.ldw + 16 * g);
+            R.a[q][1] = ld16(base + 16 * q * a.ldw + 64 + 16 * g);
+        }
+    } else if (type == HTS_TILE_DENSE) {
+        // packed tile: 16-row panels of 128-byte rows, chunk c of panel row i at (16 c + i) * 16 bytes
+        const uint8_t* panel = vb + (int64_t)r0 * 128;
+#pragma unroll
+        for (int q = 0; q < PP; ++q) {
+            R.a[q][0] = ld16(panel + 16 * q * 128 + (16 * g + i) * 16);
+            R.a[q][1] = ld16(panel + 16 * q * 128 + (16 * (4 + g) + i) * 16);
         }
     } else {
         const uint32_t* mrow = a.meta + moff + (int64_t)(r0 + i) * 4;
+        const uint8_t* panel = vb + (int64_t)r0 * 64;   // stored rows: 64 bytes
 #pragma unroll
-        for (int q = 0; q < PP; ++q) R.a[q][0] = ld16(base + 16 * q * rstride + 16 * g);
+        for (int q = 0; q < PP; ++q) R.a[q][0] = ld16(panel + 16 * q * 64 + (16 * g + i) * 16);
 #pragma unroll
         for (int q = 0; q < PP; ++q) R.m[q] = mrow[64 * q + g];
     }
@@ -454,26 +461,27 @@ __device__ __forceinline__ uint32_t load_tile32(TileRegs32<PP>& R, const GemmArg
                                                 int64_t n0, int r0, int lane, const uint16_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
-    const uint16_t* base;
-    int64_t rstride;
     uint32_t moff = 0;
     if (HYB) {
         type = e.type;
         moff = e.meta_off;
-        rstride = type == HTS_TILE_DENSE ? 32 : 16;
-        base = a.values + e.val_off + (int64_t)(r0 + i) * rstride;
-    } else {
-        rstride = a.ldw;
-        base = a.W + (n0 + i) * a.ldw + (int64_t)tk * 32;
     }
-    if (type == HTS_TILE_DENSE) {
+    if (!HYB) {        // row-major W: lane i reads row i
+        const uint16_t* base = a.W + (n0 + i) * a.ldw + (int64_t)tk * 32;
 #pragma unroll
-        for (int q = 0; q < PP; ++q) R.a[q] = ld16(base + 16 * q * rstride + 8 * g);
+        for (int q = 0; q < PP; ++q) R.a[q] = ld16(base + 16 * q * a.ldw + 8 * g);
+    } else if (type == HTS_TILE_DENSE) {
+        // packed tile: 16-row panels of 32-value rows (4 chunks), chunk c of panel row i at 16 c + i
+        const uint16_t* panel = a.values + e.val_off + (int64_t)r0 * 32;
+#pragma unroll
+        for (int q = 0; q < PP; ++q) R.a[q] = ld16(panel + 16 * q * 32 + (16 * g + i) * 8);
     } else {
+        // stored rows of 16 values (2 chunks): the 4 values of group pair g are half g % 2 of chunk g / 2
         const uint32_t* mrow = a.meta + moff + (r0 + i);
+        const uint16_t* panel = a.values + e.val_off + (int64_t)r0 * 16;
 #pragma unroll
         for (int q = 0; q < PP; ++q) {
-            const uint2 v = *reinterpret_cast<const uint2*>(base + 16 * q * rstride + 4 * g);
+            const uint2 v = *reinterpret_cast<const uint2*>(panel + 16 * q * 16 + (16 * (g >> 1) + i) * 8 + 4 * (g & 1));
             R.a[q] = u32x4{v.x, v.y, 0u, 0u};
             R.m[q] = mrow[16 * q];
         }

@@ -186,7 +186,8 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
         }
         const uint32_t r = 64 * gi;             // a block is one tile row: groups at rows 0, 64
         if (DENSE) {
-            const uint32_t so = ES * (voff - C.vbase + r * BK) + 128 * s;
+            // packed tile: slice s is chunk columns 8s .. 8s+7 of every row, 2048 bytes per 8 columns
+            const uint32_t so = ES * (voff - C.vbase + r * BK) + 2048 * s;
 #pragma unroll
             for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
         } else {
@@ -194,7 +195,7 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
             // codes, then the same two again into the sink).  With 4 waves wave w does jobs w and
             // 4 + w, with 8 waves job w.
             if (NW == 4 || C.wave < 4)
-                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 64 * s);
+                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
             if (NW == 4 || C.wave >= 4)
                 buf4(C.mr,
                      C.meta_to_sink ? (uint32_t)Lo::SINK
@@ -219,13 +220,16 @@ __device__ __forceinline__ void load_x(u32x8 (&Bx)[NBJ], const uint8_t* xs, int 
 
 // Weight fragments of row block b (16 rows) of a wave whose rows start at group g0: groups are
 // 8 KiB apart in LDS, a dense group holds 64 rows x 128 B, a 2:4 group 64 rows x 64 B (+ codes).
-template <typename T, int SP, int NBI, int NBJ>
+// PANEL (packed weights): each 16-row block is the stored order of its slice -- chunk c of row i at
+// (16 c + i) * 16, so a fragment read (16 rows of one chunk) is 256 contiguous bytes; otherwise
+// (row-major W) row i at i * 128 with XOR-swizzled chunks, as for X.
+template <typename T, int SP, int NBI, int NBJ, bool PANEL>
 __device__ __forceinline__ void compute_dense(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws, int lane) {
     const int i = lane & 15, g = lane >> 4;
     const int c0 = (SP == SPARSE_SMFMAC) ? g : 2 * g;
     const int c1 = (SP == SPARSE_SMFMAC) ? 4 + g : 2 * g + 1;
-    const int a0 = i * 128 + 16 * (c0 ^ ((i >> 1) & 7));
-    const int a1 = i * 128 + 16 * (c1 ^ ((i >> 1) & 7));
+    const int a0 = PANEL ? 16 * (16 * c0 + i) : i * 128 + 16 * (c0 ^ ((i >> 1) & 7));
+    const int a1 = PANEL ? 16 * (16 * c1 + i) : i * 128 + 16 * (c1 ^ ((i >> 1) & 7));
     u32x8 Bx[NBJ];
     load_x<SP, NBJ>(Bx, xs, lane);
     if constexpr (NBI == 4) {
@@ -265,7 +269,7 @@ template <typename T, int SP, int NBI, int NBJ>
 __device__ __forceinline__ void compute_sparse(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws,
                                                const uint32_t* ms, int lane) {
     const int i = lane & 15, g = lane >> 4;
-    const int s0 = i * 64 + 16 * (g ^ ((i >> 2) & 3));
+    const int s0 = 16 * (16 * g + i);    // stored order: chunk g of row i of the 16-row block
     u32x8 Bx[NBJ];
     load_x<SP, NBJ>(Bx, xs, lane);
 #pragma unroll
@@ -373,11 +377,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     C.xso = 0;
     for (int v = 0; v < 8 / NW; ++v) {
         const int row = 8 * (wave + NW * v) + (lane >> 3), col = (lane & 7) ^ ((row >> 1) & 7);
-        C.dvo[v] = HYB ? (uint32_t)(ES * row * BK + 16 * col) : (uint32_t)(ES * (int64_t)row * a.ldw + 16 * col);
+        // packed tile: a slice of a 16-row panel is one contiguous 2 KiB (its 8 chunk columns, the 16
+        // rows consecutive in each), so job j copies kilobyte j % 2 of panel j / 2 straight -- the LDS
+        // image is the stored order.  A row-major W: lane = (row, swizzled chunk) as for X.
+        const int job = wave + NW * v;
+        C.dvo[v] = HYB ? (uint32_t)((job >> 1) * 16 * BK * ES + 1024 * (job & 1) + 16 * lane)
+                       : (uint32_t)(ES * (int64_t)row * a.ldw + 16 * col);
     }
     {
-        const int row = 16 * (wave & 3) + (lane >> 2), col = (lane & 3) ^ ((row >> 2) & 3);
-        C.svo = (uint32_t)(ES * row * (BK / 2) + 16 * col);
+        // stored rows of BK/2 values: a slice of a 16-row panel is one contiguous kilobyte (job = panel)
+        C.svo = (uint32_t)((wave & 3) * 16 * (BK / 2) * ES + 16 * lane);
         // codes jobs of 256 bytes: 64 rows x (KSL / 32) words per slice; job j covers words
         // 64 j .. 64 j + 63 of that row-major block
         constexpr int WPR = KSL / 32, NCJ = MGB / 256;
@@ -487,7 +496,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     const int kd = Sd < k1 ? Sd : k1;
     for (; ks < kd; ++ks) {
         const uint8_t* st = step(ks);
-        if (wvalid) compute_dense<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
+        if (wvalid) compute_dense<T, SP, 4, NBJ, HYB>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
     }
     if constexpr (HYB) {
         for (; ks < k1; ++ks) {
@@ -537,274 +546,6 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
     store_y4(Y, m * ldy + n, y_dtype, acc);
 }
 
-// ---------------------------------------------------------------------------------------
-// Two tile rows per workgroup.  A 2*bn (weight rows) x BM (X rows) block moves fewer bytes
-// per flop from L2 than one tile row, and the copies from L2 are what bound the product at
-// large M.  The tile columns of the pair are ordered by their pair of tile types --
-// (dense, dense), (dense, 2:4), (2:4, dense), (2:4, 2:4) -- giving four runs; in each run
-// every wave (a wave works on one tile row) runs one instruction kind with no branch on the
-// tile type inside the K loop.
-// ---------------------------------------------------------------------------------------
-// Weight-stationary fragment order for the pair kernel: a wave holds the fragments of all its
-// NBI row blocks for one substep and streams the X fragments column block by column block,
-// keeping the live registers to NBI weight fragments plus one X fragment.
-template <typename T, int SP, int NBI, int NBJ>
-__device__ __forceinline__ void compute_dense_ws(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws, int lane) {
-    const int i = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int c = (SP == SPARSE_SMFMAC) ? (u ? 4 + g : g) : (2 * g + u);
-        const int off = i * 128 + 16 * (c ^ ((i >> 1) & 7));
-        u32x4 A[NBI];
-#pragma unroll
-        for (int b = 0; b < NBI; ++b) A[b] = ld16(ws + b * 2048 + off);
-#pragma unroll
-        for (int bj = 0; bj < NBJ; ++bj) {
-            const u32x4 B = ld16(xs + bj * 2048 + off);
-#pragma unroll
-            for (int b = 0; b < NBI; ++b) acc[b][bj] = mfma_dense<T>(A[b], B, acc[b][bj]);
-        }
-    }
-}
-
-template <typename T, int SP, int NBI, int NBJ>
-__device__ __forceinline__ void compute_sparse_ws(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws,
-                                                  const uint32_t* ms, int lane) {
-    const int i = lane & 15, g = lane >> 4;
-    const int s0 = i * 64 + 16 * (g ^ ((i >> 2) & 3));
-    if (SP == SPARSE_SMFMAC) {
-        const int x0 = i * 128 + 16 * (g ^ ((i >> 1) & 7));
-        const int x1 = i * 128 + 16 * ((4 + g) ^ ((i >> 1) & 7));
-        u32x4 A[NBI];
-        uint32_t idx[NBI];
-#pragma unroll
-        for (int b = 0; b < NBI; ++b) {
-            const int h = b / 4, bb = b % 4;
-            A[b] = ld16(ws + h * kGroupBytes + bb * 1024 + s0);
-            idx[b] = ms[h * (kMetaGroupBytes / 4) + 2 * (16 * bb + i) + (g >> 1)] >> (16 * (g & 1));
-        }
-#pragma unroll
-        for (int bj = 0; bj < NBJ; ++bj) {
-            const u32x8 B = cat8(ld16(xs + bj * 2048 + x0), ld16(xs + bj * 2048 + x1));
-#pragma unroll
-            for (int b = 0; b < NBI; ++b) acc[b][bj] = mfma_sparse<T, 0>(A[b], B, idx[b], acc[b][bj]);
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int xo = i * 128 + 16 * ((2 * g + u) ^ ((i >> 1) & 7));
-            u32x4 A[NBI];
-#pragma unroll
-            for (int b = 0; b < NBI; ++b) {
-                const int h = b / 4, bb = b % 4;
-                const uint2 v = *reinterpret_cast<const uint2*>(ws + h * kGroupBytes + bb * 1024 + s0 + 8 * u);
-                const uint32_t code =
-                    (ms[h * (kMetaGroupBytes / 4) + 2 * (16 * bb + i) + (g >> 1)] >> (16 * (g & 1) + 8 * u)) & 0xFFu;
-                A[b] = expand_two_groups(v, code);
-            }
-#pragma unroll
-            for (int bj = 0; bj < NBJ; ++bj) {
-                const u32x4 B = ld16(xs + bj * 2048 + xo);
-#pragma unroll
-                for (int b = 0; b < NBI; ++b) acc[b][bj] = mfma_dense<T>(A[b], B, acc[b][bj]);
-            }
-        }
-    }
-}
-
-template <int BNT, int BM, int NSTAGE>
-struct Layout2 {
-    static constexpr int NG = 2 * BNT / 64;                  // 64-row groups of the pair
-    static constexpr int WOFF = BM * 128;
-    static constexpr int MOFF = WOFF + NG * kGroupBytes;
-    static constexpr int STAGE = MOFF + NG * kMetaGroupBytes;
-    static constexpr int SINK = NSTAGE * STAGE;              // target of the padding copies
-    static constexpr int LIST = SINK + 1024;                 // {valA, metaA, valB, metaB} per position
-    static constexpr int LCOL = LIST + kMaxTileCols * 16;    // tile column of each position
-    static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // per-wave run counts while ordering
-    static constexpr int TOTAL = WCNT + 4 * 16 * 4;
-};
-
-template <typename T, int BK, bool HYB, int SP, int BNT, int BM, int NSTAGE, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_pair_kernel(const GemmArgs a, int NB, int MB, int ord) {
-    using Lo = Layout2<BNT, BM, NSTAGE>;
-    constexpr int NG = Lo::NG, GPR = BNT / 64, WM = NW / 2, WTM = BM / WM, NBJ = WTM / 16, NBI = BNT / 16;
-    constexpr int SPT = BK / kKS, XJ = BM / (8 * NW), WJ = 8 * NG / NW;
-    static_assert(XJ >= 1 && WJ >= 1 && NBJ >= 1, "block shape");
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave & 1, wm = wave >> 1;      // tile row of the pair, X-row block
-
-    // block id -> output block
-    int nb, mb;
-    block_of(blockIdx.x, NB, MB, ord, nb, mb);
-
-    const int64_t n0 = (int64_t)nb * 2 * BNT, m0 = (int64_t)mb * BM;
-    const bool validB = n0 + BNT < a.N;
-    const int Tk = (int)(a.K / BK);
-    uint4* list = reinterpret_cast<uint4*>(smem + Lo::LIST);
-    uint16_t* lcol = reinterpret_cast<uint16_t*>(smem + Lo::LCOL);
-    int* wcnt = reinterpret_cast<int*>(smem + Lo::WCNT);
-    const uint32_t sink = Lo::SINK;
-
-    // order the tile columns by their pair of types (runs 0..3), tile column order inside a run
-    int rend[4] = {Tk, Tk, Tk, Tk};
-    if (HYB) {
-        const int64_t tnA = n0 / BNT, tnB = tnA + 1;
-        const int t = tid;                          // one tile column per thread (Tk <= 256)
-        const bool have = t < Tk;
-        hts_tile eA = {0u, 0u, 0u, 0u}, eB = {0u, 0u, 0u, 0u};
-        if (have) {
-            eA = a.index[tnA * Tk + t];
-            if (validB) eB = a.index[tnB * Tk + t];
-        }
-        const int combo = 2 * (int)eA.type + (int)eB.type;
-        int below = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint64_t b = __ballot(have && combo == c);
-            if (combo == c)
-                below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
-            if (lane == 0) wcnt[c * NW + wave] = __popcll(b);
-        }
-        __syncthreads();
-        int start = 0, mine = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            int cnt = 0, pre = 0;
-            for (int w = 0; w < NW; ++w) {
-                const int x = wcnt[c * NW + w];
-                cnt += x;
-                if (w < wave) pre += x;
-            }
-            if (combo == c) mine = start + pre + below;
-            start += cnt;
-            rend[c] = start;
-        }
-        if (have) {
-            list[mine] = uint4{eA.val_off, eA.meta_off, eB.val_off, eB.meta_off};
-            lcol[mine] = (uint16_t)t;
-        }
-        __syncthreads();
-    }
-
-    // per-lane sources of this wave's copy jobs, fixed for the K loop (8 waves: wave w does job w
-    // of every 64-row group, plus XJ jobs of the X slice)
-    static_assert(NW == 8 && WJ == NG, "one job per group per wave");
-    const uint16_t* xsrc[XJ];
-#pragma unroll
-    for (int v = 0; v < XJ; ++v) {
-        const int row = 8 * (wave + NW * v) + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        const int64_t m = m0 + row;
-        xsrc[v] = a.X + (m < a.M ? m : a.M - 1) * a.ldx + 8 * c;   // rows past M only feed unstored outputs
-    }
-    const int q = wave;
-    const int drow = 8 * q + (lane >> 3), dcol = (lane & 7) ^ ((drow >> 1) & 7);
-    const int d_off = drow * BK + 8 * dcol;                                    // dense group job
-    const int srow = 16 * (q & 3) + (lane >> 2), scol = (lane & 3) ^ ((srow >> 2) & 3);
-    const int s_off = srow * (BK / 2) + 8 * scol;                              // 2:4 values job (q < 4)
-    const int wi = 64 * (q & 1) + lane;
-    const int m_off = (wi >> 1) * (BK / 32) + (wi & 1);                        // 2:4 codes job (q >= 4)
-    const int64_t rm_off = (int64_t)drow * a.ldw + 8 * dcol;                   // row-major weight job
-
-    // issue the copies of slice ks into a stage (fixed count per wave: XJ + NG)
-    auto issue = [&](int ks, uint32_t stage) {
-        const int p = ks / SPT, s = ks % SPT;
-        uint4 e = {0u, 0u, 0u, 0u};
-        int tk = p;
-        if (HYB) {                          // LDS reads before any copy of this slice
-            e = list[p];
-            e.x = __builtin_amdgcn_readfirstlane(e.x);
-            e.y = __builtin_amdgcn_readfirstlane(e.y);
-            e.z = __builtin_amdgcn_readfirstlane(e.z);
-            e.w = __builtin_amdgcn_readfirstlane(e.w);
-            tk = __builtin_amdgcn_readfirstlane((int)lcol[p]);
-        }
-        const int c = (p >= rend[0]) + (p >= rend[1]) + (p >= rend[2]);
-        const int64_t k0 = (int64_t)tk * BK + s * kKS;
-#pragma unroll
-        for (int v = 0; v < XJ; ++v) dma16(xsrc[v] + k0, stage + 1024 * (wave + NW * v));
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int rs = gi / GPR, r = 64 * (gi % GPR);
-            const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
-            if (rs == 1 && !validB) {
-                dma16(xsrc[0], sink);
-                continue;
-            }
-            if (!HYB) {
-                dma16(a.W + (n0 + 64 * gi) * a.ldw + k0 + rm_off, ws + 1024 * q);
-                continue;
-            }
-            const bool dense = ((rs ? c & 1 : c >> 1) == 0);
-            const uint32_t voff = rs ? e.z : e.x, moff = rs ? e.w : e.y;
-            if (dense) {
-                dma16(a.values + voff + r * BK + s * kKS + d_off, ws + 1024 * q);
-            } else if (q < 4) {
-                dma16(a.values + voff + r * (BK / 2) + s * (kKS / 2) + s_off, ws + 1024 * q);
-            } else {                        // jobs 4, 5: codes; 6, 7: the same into the sink
-                dma4(a.meta + moff + r * (BK / 32) + 2 * s + m_off,
-                     q < 6 ? stage + Lo::MOFF + gi * kMetaGroupBytes + 256 * (q & 1) : sink);
-            }
-        }
-    };
-
-    f32x4 acc[NBI][NBJ];
-#pragma unroll
-    for (int b = 0; b < NBI; ++b)
-#pragma unroll
-        for (int bj = 0; bj < NBJ; ++bj) acc[b][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int S = Tk * SPT;
-    constexpr int PER_SLICE = XJ + WJ;
-#pragma unroll
-    for (int k = 0; k < NSTAGE - 1; ++k)
-        if (k < S) issue(k, k * Lo::STAGE);
-    auto step = [&](int ks) -> const uint8_t* {
-        wait_slice<NSTAGE, PER_SLICE>(S - 1 - ks);
-        __syncthreads();
-        const int kn = ks + NSTAGE - 1;
-        if (kn < S) issue(kn, (kn % NSTAGE) * Lo::STAGE);
-        return smem + (ks % NSTAGE) * Lo::STAGE;
-    };
-    const bool wvalid = wn == 0 || validB;
-    const int xoff = wm * WTM * 128;
-    const int woff = Lo::WOFF + wn * GPR * kGroupBytes, moff = Lo::MOFF + wn * GPR * kMetaGroupBytes;
-    int ks = 0;
-    for (int c = 0; c < 4; ++c) {
-        const int kend = rend[c] * SPT;
-        const bool mydense = ((wn ? c & 1 : c >> 1) == 0);
-        if (!wvalid) {
-            for (; ks < kend; ++ks) step(ks);
-        } else if (mydense) {
-            for (; ks < kend; ++ks) {
-                const uint8_t* st = step(ks);
-                compute_dense_ws<T, SP, NBI, NBJ>(acc, st + xoff, st + woff, lane);
-            }
-        } else {
-            for (; ks < kend; ++ks) {
-                const uint8_t* st = step(ks);
-                compute_sparse_ws<T, SP, NBI, NBJ>(acc, st + xoff, st + woff,
-                                                   reinterpret_cast<const uint32_t*>(st + moff), lane);
-            }
-        }
-    }
-
-    // epilogue: acc[b][bj] lane (j + 16q) holds Y^T rows 4q..4q+3 of block b, column j of block bj
-    if (!wvalid) return;
-    const int j = lane & 15, qd = lane >> 4;
-#pragma unroll
-    for (int b = 0; b < NBI; ++b) {
-        const int64_t n = n0 + wn * BNT + 16 * b + 4 * qd;
-#pragma unroll
-        for (int bj = 0; bj < NBJ; ++bj) {
-            const int64_t m = m0 + wm * WTM + 16 * bj + j;
-            if (m < a.M) store_y4(a.Y, m * a.ldy + n, a.y_dtype, acc[b][bj]);
-        }
-    }
-}
-
 // Block order of the tiled kernels (HTS_PREFILL_ORDER overrides; see block_of).
 int prefill_order() {
     const char* e = getenv("HTS_PREFILL_ORDER");
@@ -812,21 +553,6 @@ int prefill_order() {
     const int g = (v >> 1) & 31;
     if (v < 0 || v > 127 || g == 0) return 1 | (kGroupN << 1);   // groups of at least one N-block
     return v;
-}
-
-template <typename T, int BK, bool HYB, int SP, int BNT, int BM, int NSTAGE, int NW>
-hipError_t launch_pair(const GemmArgs& a, hipStream_t s) {
-    using Lo = Layout2<BNT, BM, NSTAGE>;
-    auto kern = gemm_pair_kernel<T, BK, HYB, SP, BNT, BM, NSTAGE, NW>;
-    static bool attr_set = false;   // per instantiation; raising the dynamic-LDS limit is idempotent
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Lo::TOTAL);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const int NB = (int)((a.N + 2 * BNT - 1) / (2 * BNT)), MB = (int)((a.M + BM - 1) / BM);
-    kern<<<dim3((unsigned)(NB * MB)), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
-    return hipGetLastError();
 }
 
 template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW = 4>
@@ -851,56 +577,40 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 }
 
 template <typename T, int BK, bool HYB, int SP>
-hipError_t launch4(const GemmArgs& a, int tile, hipStream_t s) {
-    // tile 0: one tile row x 128 X rows, 4 waves, 2 stages (two workgroups per CU)
-    //      1: two tile rows x 256 X rows, 8 waves, 2 stages;  2: two tile rows x 128 X rows
-    // (8-bit elements: the single-tile-row block only)
+hipError_t launch4(const GemmArgs& a, hipStream_t s) {
+    // one tile row x 128 X rows per workgroup, 4 waves, 2 stages (two workgroups per CU)
     if constexpr (Elem<T>::bytes == 1) {
-        (void)tile;
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     } else {
-    const int bn = HYB ? a.bn : 128;
-    if (bn == 64) {
-        switch (tile) {
-            case 1: return launch_pair<T, BK, HYB, SP, 64, 256, 2, 8>(a, s);
-            case 2: return launch_pair<T, BK, HYB, SP, 64, 128, 2, 8>(a, s);
-            default: return launch_tile<T, BK, HYB, SP, 64, 128, 2>(a, s);
-        }
-    }
-    switch (tile) {
-        case 1: return launch_pair<T, BK, HYB, SP, 128, 256, 2, 8>(a, s);
-        case 2: return launch_pair<T, BK, HYB, SP, 128, 128, 2, 8>(a, s);
-        default: return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
-    }
+        if (HYB && a.bn == 64) return launch_tile<T, BK, HYB, SP, 64, 128, 2>(a, s);
+        return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     }
 }
 
 template <typename T, int BK, bool HYB>
-hipError_t launch3(const GemmArgs& a, int sp, int tile, hipStream_t s) {
+hipError_t launch3(const GemmArgs& a, int sp, hipStream_t s) {
     if constexpr (Elem<T>::bytes == 1) {
         (void)sp;
-        return launch4<T, BK, HYB, SPARSE_SMFMAC>(a, tile, s);   // 8-bit: no expansion path
+        return launch4<T, BK, HYB, SPARSE_SMFMAC>(a, s);   // 8-bit: no expansion path
     } else {
-        return sp == SPARSE_SMFMAC ? launch4<T, BK, HYB, SPARSE_SMFMAC>(a, tile, s)
-                                   : launch4<T, BK, HYB, SPARSE_DECOMPRESS>(a, tile, s);
+        return sp == SPARSE_SMFMAC ? launch4<T, BK, HYB, SPARSE_SMFMAC>(a, s)
+                                   : launch4<T, BK, HYB, SPARSE_DECOMPRESS>(a, s);
     }
 }
 
 template <typename T>
-hipError_t launch2(const GemmArgs& a, int sp, int tile, hipStream_t s) {
+hipError_t launch2(const GemmArgs& a, int sp, hipStream_t s) {
     const bool hyb = a.index != nullptr;
-    if (a.bk == 128)
-        return hyb ? launch3<T, 128, true>(a, sp, tile, s) : launch3<T, 128, false>(a, sp, tile, s);
-    return hyb ? launch3<T, 64, true>(a, sp, tile, s) : launch3<T, 64, false>(a, sp, tile, s);
+    if (a.bk == 128) return hyb ? launch3<T, 128, true>(a, sp, s) : launch3<T, 128, false>(a, sp, s);
+    return hyb ? launch3<T, 64, true>(a, sp, s) : launch3<T, 64, false>(a, sp, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, int tile, hipStream_t s) {
+hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s) {
     if (a.dtype == HTS_FP8_E4M3)   // 128x128 tiles only
-        return a.index ? launch3<FP8T, 128, true>(a, sparse_path, tile, s) : launch3<FP8T, 128, false>(a, sparse_path, tile, s);
-    return a.dtype == HTS_BF16 ? launch2<BF16T>(a, sparse_path, tile, s)
-                               : launch2<F16T>(a, sparse_path, tile, s);
+        return a.index ? launch3<FP8T, 128, true>(a, sparse_path, s) : launch3<FP8T, 128, false>(a, sparse_path, s);
+    return a.dtype == HTS_BF16 ? launch2<BF16T>(a, sparse_path, s) : launch2<F16T>(a, sparse_path, s);
 }
 
 }  // namespace hts

@@ -127,18 +127,7 @@ int decode_nt(const hts::GemmArgs& a) {
     return 2;
 }
 
-// Block shape of the tiled kernel (HTS_PREFILL_TILE overrides): r128 = one tile row x 128 X
-// rows per workgroup, 4 waves, two workgroups per CU (default); p256 / p128 = two tile rows x
-// 256 / 128 X rows, 8 waves.
-int prefill_tile_env() {
-    const char* v = getenv("HTS_PREFILL_TILE");
-    if (v && *v) {
-        if (!strcmp(v, "p256")) return 1;
-        if (!strcmp(v, "p128")) return 2;
-    }
-    return 0;
-}
-int prefill_tile(const hts::GemmArgs& a) { return a.nsplit > 1 ? 0 : prefill_tile_env(); }
+
 
 // Split products (tiled kernel, default block shape).  A workgroup alone on its CU takes about as
 // long per 64-wide slice as each of two sharing one, so a grid of at most 256 blocks (one per CU)
@@ -150,7 +139,7 @@ int prefill_tile(const hts::GemmArgs& a) { return a.nsplit > 1 ? 0 : prefill_til
 // at 258 and more blocks (M > 256 here) splitting was slower at every count tried.
 // HTS_PREFILL_SPLIT=1..16 overrides.  block_rows: weight rows per block of the launch.
 int prefill_split(int64_t M, int64_t N, int64_t K, int32_t dtype, int block_rows) {
-    if (M <= decode_max_m() || prefill_tile_env() != 0) return 1;
+    if (M <= decode_max_m()) return 1;
     const int64_t slices = K * elem_bytes(dtype) / 128;
     const char* v = getenv("HTS_PREFILL_SPLIT");
     if (v && *v) {
@@ -185,7 +174,6 @@ hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
     if (a.M <= decode_max_m()) {
         e = hts::launch_gemm_decode(a, decode_ksplit(a), decode_nt(a), decode_pp(a), sparse_path(), s);
     } else {
-        const int tile = prefill_tile(a);
         // the tiled kernel addresses X rows (and rows of a row-major W) by 32-bit byte offsets
         // from its block's first row
         if (a.ldx > (int64_t(1) << 24) || (!a.index && a.ldw > (int64_t(1) << 24)))
@@ -193,7 +181,7 @@ hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
         if (a.index && a.K / a.bk > hts::kMaxTileColsPerRow)
             return fail(HTS_ERR_UNSUPPORTED, "K/bk=%lld tile columns exceed the %d of one tile row the tiled kernel holds",
                         (long long)(a.K / a.bk), hts::kMaxTileColsPerRow);
-        e = hts::launch_gemm_prefill(a, sparse_path(), tile, s);
+        e = hts::launch_gemm_prefill(a, sparse_path(), s);
     }
     return hip_status(e, "product kernel launch");
 }

@@ -43,9 +43,9 @@ hipError_t launch_unpack(const hts_desc& d, const hts_tile* index, const uint16_
 // ksplit: waves per workgroup (4, 8 or 16); nt: 128-wide tile columns per batch of loads (2 or 4);
 // pp: 16-row panels per workgroup (1 or 2; 2 requires N % 32 == 0)
 hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s);
-// Tiled kernel (block shapes: see prefill_tile); with a.nsplit > 1 it also launches the
+// Tiled kernel (one tile row x 128 X rows per workgroup); with a.nsplit > 1 it also launches the
 // fixed-order sum of the partial products into Y.
-hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, int tile, hipStream_t s);
+hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s);
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the
 // tiled kernel holds the index records of one tile row in LDS.
 constexpr int kMaxTileColsPerRow = 256;

@@ -15,6 +15,23 @@ namespace {
 constexpr int kPackThreads = 256;
 constexpr int kInFlight = 4;   // 16-byte chunks a pack thread loads before it uses any
 
+// Storage order inside a tile: rows cut into 16-row panels (tiles have 32, 64 or 128 rows) and
+// 16-byte chunks; in a panel the chunks are stored column by column, the panel's rows consecutive
+// within a chunk column, so one matrix-core operand (a chunk of 16 consecutive rows, for four
+// consecutive chunk columns) is one contiguous kilobyte.  Offset, in elements, of chunk c of row
+// r of a stored block with w elements per row and ce elements per chunk:
+__device__ __forceinline__ int64_t stored_chunk(int r, int c, int w, int ce) {
+    return (int64_t)(r >> 4) * 16 * w + ((int64_t)c * 16 + (r & 15)) * ce;
+}
+
+// Work item -> (row, chunk) of a tile: 8 consecutive rows fastest, then the chunks of the row,
+// then the next 8 rows -- a wave reads whole 128-byte lines of W and writes whole 128-byte runs.
+__device__ __forceinline__ void item_rc(int it, int cpr, int& r, int& c) {
+    const int rest = it >> 3;
+    c = rest % cpr;
+    r = 8 * (rest / cpr) + (it & 7);
+}
+
 // Score of one weight: |w| as binary32, times the column scale when given
 // (a single IEEE multiply: nothing to contract).
 template <typename T>
@@ -70,17 +87,20 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
             const int it = base + j * kPackThreads;
-            if (it < items) qs[j] = ld16(W + (tn * bn + it / cpr) * ldw + tk * bk + 8 * (it % cpr));
+            int r, c;
+            item_rc(it, cpr, r, c);
+            if (it < items) qs[j] = ld16(W + (tn * bn + r) * ldw + tk * bk + 8 * c);
         }
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
             const int it = base + j * kPackThreads;
             if (it >= items) break;
-            const int r = it / cpr, c = it % cpr;
+            int r, c;
+            item_rc(it, cpr, r, c);
             const int64_t k0 = tk * bk + 8 * c;
             const u32x4 q = qs[j];
             if (e.type == HTS_TILE_DENSE) {
-                st16(values + e.val_off + (int64_t)r * bk + 8 * c, q);
+                st16(values + e.val_off + stored_chunk(r, c, bk, 8), q);
                 continue;
             }
             uint2 mk = {0u, 0u};   // mask bytes of the chunk's 8 weights
@@ -116,7 +136,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
                 kept[g] = v0 | (v1 << 16);
                 code |= (i0 | (i1 << 2)) << (4 * g);
             }
-            *reinterpret_cast<uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 4 * c) = uint2{kept[0], kept[1]};
+            // the 4 kept values are half (c % 2) of stored chunk c / 2
+            *reinterpret_cast<uint2*>(values + e.val_off + stored_chunk(r, c >> 1, bk / 2, 8) + 4 * (c & 1)) =
+                uint2{kept[0], kept[1]};
             mbytes[(int64_t)r * (bk / 8) + c] = (uint8_t)code;
         }
     }
@@ -144,17 +166,20 @@ __global__ __launch_bounds__(kPackThreads) void pack8_kernel(
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
             const int it = base + j * kPackThreads;
-            if (it < items) qs[j] = ld16(W + (tn * bn + it / cpr) * ldw + tk * bk + 16 * (it % cpr));
+            int r, c;
+            item_rc(it, cpr, r, c);
+            if (it < items) qs[j] = ld16(W + (tn * bn + r) * ldw + tk * bk + 16 * c);
         }
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
             const int it = base + j * kPackThreads;
             if (it >= items) break;
-            const int r = it / cpr, c = it % cpr;
+            int r, c;
+            item_rc(it, cpr, r, c);
             const int64_t k0 = tk * bk + 16 * c;
             const u32x4 q = qs[j];
             if (e.type == HTS_TILE_DENSE) {
-                st16(values + e.val_off + (int64_t)r * bk + 16 * c, q);
+                st16(values + e.val_off + stored_chunk(r, c, bk, 16), q);
                 continue;
             }
             u32x4 mk = {0u, 0u, 0u, 0u};
@@ -193,7 +218,7 @@ __global__ __launch_bounds__(kPackThreads) void pack8_kernel(
                 kept[g] = v0 | (v1 << 8);
                 code |= (i0 | (i1 << 2)) << (4 * g);
             }
-            *reinterpret_cast<uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 8 * c) =
+            *reinterpret_cast<uint2*>(values + e.val_off + stored_chunk(r, c >> 1, bk / 2, 16) + 8 * (c & 1)) =
                 uint2{kept[0] | (kept[1] << 16), kept[2] | (kept[3] << 16)};
             mhalves[(int64_t)r * (bk / 16) + c] = (uint16_t)code;
         }
@@ -219,19 +244,24 @@ __global__ __launch_bounds__(kPackThreads) void unpack_kernel(
         u32x4 q[kInFlight];        // dense: the chunk; 2:4: stored values in .x, .y and the code byte in .z
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
-            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            const int it = base + j * kPackThreads;
             if (it >= items) break;
+            int r, c;
+            item_rc(it, cpr, r, c);
             if (dense) {
-                q[j] = ld16(values + e.val_off + (int64_t)r * bk + 8 * c);
+                q[j] = ld16(values + e.val_off + stored_chunk(r, c, bk, 8));
             } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 4 * c);
+                const uint2 v = *reinterpret_cast<const uint2*>(values + e.val_off + stored_chunk(r, c >> 1, bk / 2, 8) +
+                                                                4 * (c & 1));
                 q[j] = u32x4{v.x, v.y, mbytes[(int64_t)r * (bk / 8) + c], 0u};
             }
         }
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
-            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            const int it = base + j * kPackThreads;
             if (it >= items) break;
+            int r, c;
+            item_rc(it, cpr, r, c);
             uint16_t* dst = W + (tn * bn + r) * ldw + tk * bk + 8 * c;
             st16(dst, dense ? q[j] : expand_two_groups(uint2{q[j][0], q[j][1]}, q[j][2]));
         }
@@ -253,19 +283,24 @@ __global__ __launch_bounds__(kPackThreads) void unpack8_kernel(
         u32x4 q[kInFlight];        // dense: the chunk; 2:4: kept bytes in .x, .y and the codes in .z
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
-            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            const int it = base + j * kPackThreads;
             if (it >= items) break;
+            int r, c;
+            item_rc(it, cpr, r, c);
             if (dense) {
-                q[j] = ld16(values + e.val_off + (int64_t)r * bk + 16 * c);
+                q[j] = ld16(values + e.val_off + stored_chunk(r, c, bk, 16));
             } else {
-                const uint2 kv = *reinterpret_cast<const uint2*>(values + e.val_off + (int64_t)r * (bk / 2) + 8 * c);
+                const uint2 kv = *reinterpret_cast<const uint2*>(values + e.val_off + stored_chunk(r, c >> 1, bk / 2, 16) +
+                                                                 8 * (c & 1));
                 q[j] = u32x4{kv.x, kv.y, mhalves[(int64_t)r * (bk / 16) + c], 0u};
             }
         }
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
-            const int it = base + j * kPackThreads, r = it / cpr, c = it % cpr;
+            const int it = base + j * kPackThreads;
             if (it >= items) break;
+            int r, c;
+            item_rc(it, cpr, r, c);
             uint8_t* dst = W + (tn * bn + r) * ldw + tk * bk + 16 * c;
             if (dense) {
                 st16(dst, q[j]);

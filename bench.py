@@ -359,6 +359,11 @@ def main():
                                     pw0.sizes, pw0.tile_map) for _ in range(n_rot - 1)]
     n_rot_d = max(2, -(-ROTATE_BYTES // dense_bytes))
     Ws = [W] + [W.clone() for _ in range(n_rot_d - 1)]
+    # the same weight packed with an all-dense map: the hybrid path's own dense reference (same
+    # kernels and storage order; the row-major dense product reads W row by row)
+    pd0 = hts.pack(W, np.zeros_like(tmap), L.bn, L.bk)
+    pds = [pd0] + [hts.PackedWeight(pd0.desc, pd0.index.clone(), pd0.values.clone(), pd0.meta.clone(),
+                                    pd0.sizes, pd0.tile_map) for _ in range(n_rot_d - 1)]
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -418,9 +423,11 @@ def main():
         hyb = lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n_rot])
         den = lambda i: hts.dense_gemm(Xm, Ws[i % n_rot_d], out=Yd[i % n_rot_d])
         mm = lambda i: torch.matmul(Xm, Ws[i % n_rot_d].t(), out=Yd[i % n_rot_d])
+        dpk = lambda i: hts.gemm(Xm, pds[i % n_rot_d], out=Yd[i % n_rot_d])
         per = 4 if args.quick else 8 * max(n_rot, n_rot_d)
         t_h = time_graph(hyb, per, 2 if args.quick else 25)
         t_d = time_graph(den, per, 2 if args.quick else 25)
+        t_dp = time_graph(dpk, per, 2 if args.quick else 25)
         t_t = time_graph(mm, per, 2 if args.quick else 25)
         alg_bytes = packed_bytes + 2 * M * L.K + 2 * M * L.N
         den_bytes = dense_bytes + 2 * M * L.K + 2 * M * L.N
@@ -432,6 +439,8 @@ def main():
             "dense_same_library_us": round(t_d * 1e6, 3),
             "dense_same_library_GB/s": round(den_bytes / t_d / 1e9, 1),
             "speedup_vs_dense": round(t_d / t_h, 3),
+            "dense_packed_us": round(t_dp * 1e6, 3),
+            "speedup_vs_dense_packed": round(t_dp / t_h, 3),
             "torch_matmul_us": round(t_t * 1e6, 3),
         })
 
@@ -460,6 +469,8 @@ def main():
     Ydd = [torch.empty((M, L.N), dtype=tdt, device=dev) for _ in range(2)]
     n_pf = 10 if args.quick else 50
     t_dense = time_launches(lambda i: hts.dense_gemm(Xm, Ws[i % n_rot_d], out=Ydd[i % 2]), n_pf)
+    # (not in profiling runs: it launches the timed step's kernel on another map)
+    t_dense_packed = None if args.quick else time_launches(lambda i: hts.gemm(Xm, pds[i % n_rot_d], out=Ydd[i % 2]), n_pf)
     t_torch = time_launches(lambda i: torch.matmul(Xm, Ws[i % n_rot_d].t(), out=Ydd[i % 2]), n_pf)
 
     # ---------------- pack / unpack ----------------
@@ -529,6 +540,8 @@ def main():
         "dense_same_library_us": round(t_dense * 1e6, 2),
         "dense_same_library_TFLOP/s": round(dense_flops / t_dense / 1e12, 2),
         "speedup_vs_dense": round(t_dense / t_step, 3),
+        "dense_packed_us": None if t_dense_packed is None else round(t_dense_packed * 1e6, 2),
+        "speedup_vs_dense_packed": None if t_dense_packed is None else round(t_dense_packed / t_step, 3),
         "torch_matmul_us": round(t_torch * 1e6, 2),
         "torch_matmul_TFLOP/s": round(dense_flops / t_torch / 1e12, 2),
     }

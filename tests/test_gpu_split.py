@@ -6,7 +6,8 @@ The checks cover:
 - ragged M, and parts that cross the dense / 2:4 boundary of the ordered tile list;
 - parts that start past the first 64 list entries (86 tile columns of the 7B down-projection);
 - 8-bit weights, 64x64 tiles, the dense product, and the unpack path of 32-wide tiles;
-- a workspace too small for the parts, which runs the product unsplit.
+- a workspace too small for the parts, which runs the product unsplit;
+- every chunk size of the dense-first ordered tile list (HTS_PREFILL_CHUNK).
 
 Results must be within 5e-3 * max|Y_ref| of the oracle and identical from call to call.
 """
@@ -177,3 +178,37 @@ def test_split_small_tiles_workspace():
     Y_ref = oracle.hybrid_ref(X, W, "bf16", m, 32, 32)
     _check(Y.cpu().numpy(), Y_ref, "32x32 split")
     _check(Yu.cpu().numpy(), Y_ref, "32x32 unsplit")
+
+
+@pytest.mark.parametrize("chunk", ["4", "8", "16", "32", "64"])
+@pytest.mark.parametrize("M", [100, 300])
+def test_chunked_list_orders(chunk, M, monkeypatch):
+    # the ordered list is dense-first inside chunks of tile columns; every chunk size gives the
+    # same product within tolerance, split parts starting or ending inside a chunk (M=100: 3
+    # blocks, 8 parts) or unsplit (M=300, forced), with a last chunk that is only partly filled
+    # (K/bk = 44 tile columns)
+    monkeypatch.setenv("HTS_PREFILL_CHUNK", chunk)
+    if M == 300:
+        monkeypatch.setenv("HTS_PREFILL_SPLIT", "1")
+    N, K = 384, 44 * 128
+    W, m, g = _layer(N, K, "bf16", 0.5, zlib.crc32(f"chunk{chunk}-{M}".encode()))
+    X = wl.gaussian_bits((M, K), 1.0, "bf16", g)
+    say(f"[chunk] chunk={chunk} M={M}")
+    pw = hts.pack(hts.tensor_from_bits(W, "bf16", DEV), m, 128, 128)
+    Y = hts.gemm(hts.tensor_from_bits(X, "bf16", DEV), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), oracle.hybrid_ref(X, W, "bf16", m, 128, 128), f"chunk={chunk} M={M}")
+
+
+@pytest.mark.parametrize("chunk", ["4", "8", "64"])
+def test_chunked_list_64_tiles(chunk, monkeypatch):
+    # bk = 64: one 64-wide slice per tile column, the default chunk is 8 tile columns
+    monkeypatch.setenv("HTS_PREFILL_CHUNK", chunk)
+    N, K, M = 256, 70 * 64, 200
+    W, m, g = _layer(N, K, "f16", 0.4, 1300 + int(chunk), bn=64, bk=64)
+    X = wl.gaussian_bits((M, K), 1.0, "f16", g)
+    say(f"[chunk-64] chunk={chunk}")
+    pw = hts.pack(hts.tensor_from_bits(W, "f16", DEV), m, 64, 64)
+    Y = hts.gemm(hts.tensor_from_bits(X, "f16", DEV), pw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), oracle.hybrid_ref(X, W, "f16", m, 64, 64), f"64x64 chunk={chunk}")

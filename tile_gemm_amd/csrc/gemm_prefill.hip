@@ -74,7 +74,7 @@ struct Layout {
     static constexpr int SINK = NSTAGE * STAGE;              // target of the padding copies
     static constexpr int LIST = SINK + 1024;                 // ordered tile list: {val_off, meta_off}
     static constexpr int LCOL = LIST + kMaxTileCols * 8;     // ... and the tile column of each entry
-    static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // per-wave counts while ordering
+    static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // dense tiles of each chunk (bytes)
     static constexpr int TOTAL = WCNT + 64;
 };
 
@@ -117,7 +117,8 @@ struct Ctx {
     int64_t N, n0;
     int r0;                     // first row of the block inside its tile (0 when BN == bn)
     int wave, lane;
-    int n_dense;                // dense tiles of the list (they come first)
+    int lch;                    // log2 of the tile columns per chunk of the list
+    uint32_t lnd;               // lane c: dense tiles of chunk c (they come first in the chunk)
     const uint2* list;          // {val_off, meta_off} of the tile row's tiles in list order
     // the ordered list in registers, 64 entries per register (K / bk <= 256).  It is read in order,
     // and after each block of 64 entries the registers move down by one (shift_list), so entry p
@@ -331,7 +332,7 @@ __device__ __forceinline__ void wait_slice(int later) {
 }
 
 template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord) {
+__global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
     constexpr int ES = Elem<T>::bytes, KSL = slice_k<ES>(), MGB = meta_group_bytes<ES>();
     using Lo = Layout<BN, BM, NSTAGE, MGB>;
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -396,11 +397,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         C.mvo = (uint32_t)(4 * ((wi / WPR) * (BK / 32) + (wi % WPR)));
         C.meta_to_sink = cj >= NCJ;
     }
-    // ordered tile list of the tile row (dense first), tile columns kept for the X copies
+    // ordered tile list of the tile row, tile columns kept for the X copies.  The row is cut
+    // into chunks of 2^lch tile columns (inside one wave: lch <= 6), each ordered dense first.
+    // Tile rows then walk K chunk by chunk, so workgroups of different tile rows that run
+    // together stay within a chunk of each other and find each other's X slices in L2.
     uint2* list = reinterpret_cast<uint2*>(smem + Lo::LIST);
     uint16_t* lcol = reinterpret_cast<uint16_t*>(smem + Lo::LCOL);
-    int* wcount = reinterpret_cast<int*>(smem + Lo::WCNT);
+    uint8_t* cnd = reinterpret_cast<uint8_t*>(smem + Lo::WCNT);   // dense tiles per chunk (<= 64 chunks)
     C.list = list;
+    C.lch = lch;
     if (HYB) {
         const int tn = (int)(C.n0 / a.bn);
         const int t = tid;                         // one tile column per thread (Tk <= 256)
@@ -409,28 +414,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         if (have) e = a.index[(int64_t)tn * C.Tk + t];
         const bool isd = have && e.type == HTS_TILE_DENSE, iss = have && !isd;
         const uint64_t bd = __ballot(isd), bs = __ballot(iss);
-        const int below_d = __builtin_amdgcn_mbcnt_hi((uint32_t)(bd >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bd, 0));
-        const int below_s = __builtin_amdgcn_mbcnt_hi((uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0));
-        if (lane == 0) {
-            wcount[wave] = __popcll(bd);
-            wcount[NW + wave] = __popcll(bs);
-        }
-        __syncthreads();
-        int nd = 0, pd = 0, ps = 0;
-        for (int w = 0; w < NW; ++w) {
-            nd += wcount[w];
-            if (w < wave) {
-                pd += wcount[w];
-                ps += wcount[NW + w];
-            }
-        }
+        const int ch = 1 << lch, cl = lane & ~(ch - 1);             // first lane of this chunk
+        const uint64_t cm = (lch == 6 ? ~0ull : ((1ull << ch) - 1)) << cl;
+        const uint64_t lt = (1ull << lane) - 1;                      // lanes below this one
+        const int nd_c = __popcll(bd & cm);
+        const int below_d = __popcll(bd & cm & lt), below_s = __popcll(bs & cm & lt);
         if (have) {
-            const int pos = isd ? pd + below_d : nd + ps + below_s;
+            const int pos = (t & ~(ch - 1)) + (isd ? below_d : nd_c + below_s);
             list[pos] = uint2{e.val_off, e.meta_off};
             lcol[pos] = (uint16_t)t;
+            if (lane == cl) cnd[t >> lch] = (uint8_t)nd_c;
         }
-        C.n_dense = nd;
         __syncthreads();
+        const int nch = (C.Tk + ch - 1) >> lch;
+        C.lnd = lane < nch ? (uint32_t)cnd[lane] : 0u;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const int q = 64 * w + lane;
@@ -440,7 +437,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
             C.lc[w] = in ? (uint32_t)lcol[q] : 0u;
         }
     } else {
-        C.n_dense = C.Tk;
+        C.lnd = 0u;
 #pragma unroll
         for (int w = 0; w < 4; ++w) C.lv[w] = C.lm[w] = C.lc[w] = 0u;
     }
@@ -466,7 +463,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         for (int bj = 0; bj < NBJ; ++bj) acc[b][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // slices k0 .. k1-1 of the ordered list (all of them unless the product is split)
-    const int S = C.Tk * SPT, Sd = C.n_dense * SPT;
+    const int S = C.Tk * SPT, lcs = lch + (SPT == 2 ? 1 : 0);   // slices per chunk: 2^lcs
+    // slice kn is dense when it lies in the dense run at the start of its chunk
+    auto dense_slice = [&](int kn) {
+        return !HYB || (kn & ((1 << lcs) - 1)) < SPT * (int)__builtin_amdgcn_readlane((int)C.lnd, kn >> lcs);
+    };
     const int k0 = (int)((int64_t)split * S / nsplit), k1 = (int)((int64_t)(split + 1) * S / nsplit);
     const bool wvalid = C.gvalid(wn);
     const int xoff = wm * WTM * 128;
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         if (HYB && kn > k0 && kn % (64 * SPT) == 0) C.shift_list();
         set_x(kn);
         const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
-        if (!HYB || kn < Sd) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW, ES>(C, kn, stage);
+        if (dense_slice(kn)) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW, ES>(C, kn, stage);
         else issue_slice<BK, HYB, BN, BM, NSTAGE, false, NW, ES>(C, kn, stage);
     };
     // prologue: slices k0 .. k0+NSTAGE-2 in flight
@@ -493,17 +494,28 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         return smem + (ks % NSTAGE) * Lo::STAGE;
     };
     int ks = k0;
-    const int kd = Sd < k1 ? Sd : k1;
-    for (; ks < kd; ++ks) {
-        const uint8_t* st = step(ks);
-        if (wvalid) compute_dense<T, SP, 4, NBJ, HYB>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
-    }
-    if constexpr (HYB) {
+    if constexpr (!HYB) {
         for (; ks < k1; ++ks) {
             const uint8_t* st = step(ks);
-            if (wvalid)
-                compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
-                                           reinterpret_cast<const uint32_t*>(st + Lo::MOFF + wn * MGB), lane);
+            if (wvalid) compute_dense<T, SP, 4, NBJ, false>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
+        }
+    } else {
+        // chunk by chunk: its dense run, then its 2:4 run (a split part may start or end inside)
+        while (ks < k1) {
+            const int c = ks >> lcs, cs = c << lcs;
+            const int ce = (cs + (1 << lcs)) < k1 ? cs + (1 << lcs) : k1;
+            int de = cs + SPT * (int)__builtin_amdgcn_readlane((int)C.lnd, c);
+            de = de < ce ? de : ce;
+            for (; ks < de; ++ks) {
+                const uint8_t* st = step(ks);
+                if (wvalid) compute_dense<T, SP, 4, NBJ, true>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
+            }
+            for (; ks < ce; ++ks) {
+                const uint8_t* st = step(ks);
+                if (wvalid)
+                    compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
+                                               reinterpret_cast<const uint32_t*>(st + Lo::MOFF + wn * MGB), lane);
+            }
         }
     }
 
@@ -555,6 +567,16 @@ int prefill_order() {
     return v;
 }
 
+// Tile columns per chunk of the ordered list, as log2: chunks of 512 K by default
+// (HTS_PREFILL_CHUNK = 4, 8, 16, 32 or 64 tile columns overrides).
+int prefill_chunk_log2(int bk) {
+    const char* e = getenv("HTS_PREFILL_CHUNK");
+    const int v = (e && *e) ? atoi(e) : 512 / bk;
+    for (int l = 2; l <= 6; ++l)
+        if (v == (1 << l)) return l;
+    return bk == 64 ? 3 : 2;
+}
+
 template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW = 4>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     using Lo = Layout<BN, BM, NSTAGE, meta_group_bytes<Elem<T>::bytes>()>;
@@ -567,7 +589,8 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     }
     const int NB = (int)((a.N + BN - 1) / BN), MB = (int)((a.M + BM - 1) / BM);
     const int nsplit = a.nsplit > 1 ? a.nsplit : 1;
-    kern<<<dim3((unsigned)(NB * MB), (unsigned)nsplit), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order());
+    kern<<<dim3((unsigned)(NB * MB), (unsigned)nsplit), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order(),
+                                                                                   prefill_chunk_log2(BK));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     const int64_t quads = a.M * (a.N / 4);

@@ -171,8 +171,9 @@ def run_tile_sizes(hts, wl, dev, time_graph, time_launches, quick):
 
 
 def run_mid_m(hts, wl, dev, time_graph, quick):
-    """The 7B up-projection between the streaming range and full prefill (M = 17 .. 256): few
-    output blocks, so the tiled product is split over K (the workspace holds the parts).
+    """The 7B up-projection between decode and full prefill (M = 17 .. 256).  Up to M = 32 the
+    streaming kernel feeds each weight fragment to two groups of 16 X rows; above, the tiled
+    product has few output blocks and is split over K (the workspace holds the parts).
     Graph-timed with rotated weights; the same-library dense product and torch for comparison."""
     import torch
     cfg = wl.config("7b_up")
@@ -189,7 +190,7 @@ def run_mid_m(hts, wl, dev, time_graph, quick):
     Wd = [W] + [W.clone() for _ in range(n_rd - 1)]
     kept = L.N * L.K - int(m.sum()) * L.bn * L.bk // 2
     rows = []
-    for M in (17, 64, 128, 256):
+    for M in (17, 32, 64, 128, 256):
         Xm = Xall[:M].contiguous()
         n = max(n_rot, n_rd)
         Ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for _ in range(n)]

@@ -154,8 +154,9 @@ hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* valu
                       const uint32_t* meta, void* W_out, int64_t ldw, void* stream);
 
 /* Host only.  Bytes of device workspace for the fastest hts_gemm path at this shape and M
- * (0 at M <= 16, the streaming range).  Two uses, in this order within the workspace:
- *  - tiles of 32 rows or 32 columns above M = 16: the product unpacks the weight into the
+ * (0 in the streaming range: M <= 32 for 16-bit data on 128-wide tiles, else M <= 16; the
+ * environment variable HTS_DECODE_MAX_M lowers it).  Two uses, in this order within the workspace:
+ *  - tiles of 32 rows or 32 columns above the streaming range: the product unpacks the weight into the
  *    workspace (N*K elements, row-major, 256-byte rounded) and runs the same-library dense
  *    product on it -- the tiled kernel works on 64-row weight groups and 64-wide slices.
  *    Execution tiles below 128x128 are the tile-size ablation of the PATCH page (sections 2
@@ -169,7 +170,9 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes);
 
 /* Device, asynchronous.  Y[M,N] = X[M,K] . mask(W)^T from the packed weight,
  * fp32 accumulation, Y written as y_dtype (HTS_F32, HTS_F16 or HTS_BF16; 16-bit
- * outputs rounded to nearest even).  Dense tiles use dense MFMA, 2:4 tiles
+ * outputs rounded to nearest even).  In the streaming range (see hts_gemm_workspace) one
+ * kernel streams the weight from HBM once; above it a tiled kernel stages weight and X
+ * slices through LDS.  Dense tiles use dense MFMA, 2:4 tiles
  * sparse MFMA (or in-register expansion to dense MFMA when the environment
  * variable HTS_SPARSE_PATH=decompress), both into one accumulator per output
  * tile.  M == 0 is a no-op.  ldx, ldy: multiples of 8 and 4 with ldx >= K and

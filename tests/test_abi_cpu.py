@@ -201,12 +201,14 @@ def test_small_tiles_plan_and_workspace():
         o_idx, o_sz = oracle.plan(m, N, K, bn, bk)
         assert np.array_equal(idx, o_idx) and sz["values_bytes"] == o_sz["values_bytes"]
         assert sz["meta_bytes"] == o_sz["meta_bytes"]
-        assert hts.hts_gemm_workspace(d, 16) == 0
-        assert hts.hts_gemm_workspace(d, 17) == N * K * 2
+        # the streaming kernel covers M <= 32 on 128-wide tiles (two X row groups), else M <= 16
+        top = 32 if bk == 128 else 16
+        assert hts.hts_gemm_workspace(d, top) == 0
+        assert hts.hts_gemm_workspace(d, top + 1) == N * K * 2
         # missing or short workspace: HTS_ERR_WORKSPACE, misaligned: HTS_ERR_ALIGN, before any launch
-        assert L.hts_gemm(by(d), A16, A16, A16, 17, A16, K, A16, N, 2, None, 0, None) == 6
-        assert L.hts_gemm(by(d), A16, A16, A16, 17, A16, K, A16, N, 2, A16, N * K, None) == 6
-        assert L.hts_gemm(by(d), A16, A16, A16, 17, A16, K, A16, N, 2, A8, N * K * 2, None) == 4
+        assert L.hts_gemm(by(d), A16, A16, A16, top + 1, A16, K, A16, N, 2, None, 0, None) == 6
+        assert L.hts_gemm(by(d), A16, A16, A16, top + 1, A16, K, A16, N, 2, A16, N * K, None) == 6
+        assert L.hts_gemm(by(d), A16, A16, A16, top + 1, A16, K, A16, N, 2, A8, N * K * 2, None) == 4
     assert hts.hts_gemm_workspace(hts.make_desc(256, 384, 128, 128, "bf16"), 2048) == 0
     assert _err(lambda: hts.hts_pack_plan(hts.make_desc(256, 256, 32, 32, "fp8"), np.zeros(64, np.uint8))) == 7
 
@@ -220,7 +222,8 @@ def test_split_product_workspace_sizes(monkeypatch):
     # 256 output blocks; nsplit = min(8, 512 // blocks), lowered until every part has >= 4 slices
     N, K = 11008, 4096
     d = hts.make_desc(N, K, 128, 128, "bf16")
-    for M, ns in ((1, 0), (16, 0), (17, 5), (128, 5), (129, 2), (256, 2), (257, 0), (2048, 0)):
+    # (M <= 32 runs on the streaming kernel: 16-bit data on 128-wide tiles)
+    for M, ns in ((1, 0), (16, 0), (17, 0), (32, 0), (33, 5), (128, 5), (129, 2), (256, 2), (257, 0), (2048, 0)):
         assert hts.hts_gemm_workspace(d, M) == (_r256(ns * M * N * 4) if ns else 0), M
         assert hts.hts_dense_gemm_workspace("bf16", M, N, K) == (_r256(ns * M * N * 4) if ns else 0), M
     # 8-bit: 128-wide slices (32 per tile row here); 64x64 tiles: 64-row blocks
@@ -230,7 +233,12 @@ def test_split_product_workspace_sizes(monkeypatch):
     assert hts.hts_gemm_workspace(hts.make_desc(1024, 256, 128, 128, "bf16"), 64) == 0
     # 32-wide tiles: the unpacked weight, then the parts of the dense product
     d32 = hts.make_desc(N, K, 32, 32, "bf16")
-    assert hts.hts_gemm_workspace(d32, 17) == N * K * 2 + _r256(5 * 17 * N * 4)
+    assert hts.hts_gemm_workspace(d32, 17) == N * K * 2          # the unpacked product streams at M <= 32
+    assert hts.hts_gemm_workspace(d32, 33) == N * K * 2 + _r256(5 * 33 * N * 4)
+    # HTS_DECODE_MAX_M lowers the streaming range: M = 17 is then split
+    monkeypatch.setenv("HTS_DECODE_MAX_M", "16")
+    assert hts.hts_gemm_workspace(d, 17) == _r256(5 * 17 * N * 4)
+    monkeypatch.delenv("HTS_DECODE_MAX_M")
     # override: a forced count
     monkeypatch.setenv("HTS_PREFILL_SPLIT", "3")
     assert hts.hts_gemm_workspace(d, 300) == _r256(3 * 300 * N * 4)

@@ -231,3 +231,44 @@ def test_streaming_launch_shapes(env, M, sparse_path, monkeypatch):
         Y = hts.gemm(hts.tensor_from_bits(X, dtype, DEV), pw, out_dtype=torch.float32)
         torch.cuda.synchronize()
         _check(Y.cpu().numpy(), oracle.hybrid_ref(X, W, dtype, m, bn, bn), f"{env} M={M} tile={bn}")
+
+
+TWO_GROUP_ENVS = [{}, {"HTS_DECODE_NT": "2"}, {"HTS_DECODE_PP": "2"}, {"HTS_DECODE_KSPLIT": "4"},
+                  {"HTS_DECODE_PP": "2", "HTS_DECODE_KSPLIT": "4", "HTS_DECODE_NT": "2"},
+                  {"HTS_DECODE_KSPLIT": "16", "HTS_DECODE_NT": "4"}]
+
+
+@pytest.mark.parametrize("env", TWO_GROUP_ENVS, ids=lambda e: "-".join(f"{k[11:]}{v}" for k, v in e.items()) or "default")
+@pytest.mark.parametrize("M", [17, 20, 31, 32])
+def test_streaming_two_row_groups(env, M, sparse_path, monkeypatch):
+    # 17 <= M <= 32 on 128-wide tiles: the streaming kernel feeds each weight fragment to two
+    # groups of 16 X rows (rows past M repeat row M-1 and are never stored); every launch shape,
+    # 128- and 32-row tiles, f32 and 16-bit outputs, strided X and Y, and the dense product
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    g = np.random.default_rng(4100 + M)
+    for bn, dtype in ((128, "bf16"), (32, "f16")):
+        N, K = 512, 1536
+        W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+        X = wl.gaussian_bits((M, K), 1.0, dtype, g)
+        m = (g.random((N // bn) * (K // 128)) < 0.5).astype(np.uint8)
+        say(f"[stream-2g] {env} M={M} tile={bn}x128 {sparse_path}")
+        desc = hts.make_desc(N, K, bn, 128, torch.bfloat16 if dtype == "bf16" else torch.float16)
+        assert hts.hts_gemm_workspace(desc, M) == 0          # no workspace: the streaming kernel
+        pw = hts.pack(hts.tensor_from_bits(W, dtype, DEV), m, bn, 128)
+        Y_ref = oracle.hybrid_ref(X, W, dtype, m, bn, 128)
+        Xs = torch.zeros((M, K + 64), dtype=torch.bfloat16 if dtype == "bf16" else torch.float16, device=DEV)
+        Xs[:, :K] = hts.tensor_from_bits(X, dtype, DEV)
+        Yf = hts.gemm(Xs[:, :K], pw, out_dtype=torch.float32)
+        Ys = torch.full((M, N + 32), float("nan"), dtype=Xs.dtype, device=DEV)
+        hts.gemm(Xs[:, :K], pw, out=Ys[:, :N])
+        Yf2 = hts.gemm(Xs[:, :K], pw, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check(Yf.cpu().numpy(), Y_ref, f"{env} M={M} tile={bn} f32")
+        _check(Ys[:, :N].float().cpu().numpy(), Y_ref, f"{env} M={M} tile={bn} 16-bit")
+        assert torch.isnan(Ys[:, N:]).all(), "columns past N of a strided Y were written"
+        assert torch.equal(Yf, Yf2)
+        if bn == 128:
+            Yd = hts.dense_gemm(Xs[:, :K], hts.tensor_from_bits(W, dtype, DEV), out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            _check(Yd.cpu().numpy(), oracle.gemm_ref(X, W, dtype), f"dense {env} M={M}")

@@ -41,7 +41,7 @@ def _layer(N, K, dtype, p, seed, bn=128, bk=128, w_sigma=None):
 
 
 @pytest.mark.parametrize("split", ["auto", "2", "3", "5", "7", "16"])
-@pytest.mark.parametrize("M", [17, 100, 130])
+@pytest.mark.parametrize("M", [33, 100, 130])
 def test_split_forced_counts(split, M, monkeypatch):
     if split != "auto":
         monkeypatch.setenv("HTS_PREFILL_SPLIT", split)
@@ -78,9 +78,9 @@ def test_split_list_boundaries(kind, monkeypatch):
         _check(Y.float().cpu().numpy(), oracle.hybrid_ref(X, W, "f16", m, 128, 128), f"{kind} out={od}")
 
 
-@pytest.mark.parametrize("M", [17, 128, 256])
+@pytest.mark.parametrize("M", [33, 128, 256])
 def test_split_7b_down_projection(M):
-    # 4096 x 11008: 86 tile columns, 172 slices; at M <= 256 the 32-64 blocks split 8 ways and
+    # 4096 x 11008: 86 tile columns, 172 slices; at 32 < M <= 256 the 32-64 blocks split 8 ways and
     # later parts start past list entry 64
     c = wl.config("7b_block")
     L = next(x for x in c.layers if x.name == "down")
@@ -97,7 +97,7 @@ def test_split_7b_down_projection(M):
            f"down M={M}")
 
 
-@pytest.mark.parametrize("M", [17, 64, 200])
+@pytest.mark.parametrize("M", [33, 64, 200])
 def test_split_7b_up_projection(M):
     c = wl.config("7b_up")
     L = c.layers[0]

@@ -302,7 +302,7 @@ def unpack(pw: PackedWeight, stream=None) -> torch.Tensor:
 def gemm(X: torch.Tensor, pw: PackedWeight, out_dtype=None, out: Optional[torch.Tensor] = None,
          stream=None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y[M,N] = X[M,K] . mask(W)^T from the packed weight (fp32 accumulation).  The workspace the
-    library asks for (the unpacked weight of 32-wide tiles at M > 16, the parts of a split
+    library asks for (the unpacked weight of 32-wide tiles above the streaming range, the parts of a split
     product) is allocated here when none is given."""
     M = X.shape[0]
     if out is None:

@@ -1,4 +1,5 @@
-// Hybrid tile-sparse product for small M (M <= 16): the HBM-streaming path.
+// Hybrid tile-sparse product for small M (M <= 16; M <= 32 for 16-bit data on 128-wide tiles,
+// where each weight fragment feeds two groups of 16 X rows): the HBM-streaming path.
 //
 // At decode-sized M the weight bytes are almost all of the traffic, so every
 // weight byte is read once, straight from HBM into registers, with no LDS
@@ -31,18 +32,19 @@
 namespace hts {
 namespace {
 
-template <int BK, int PP>
+template <int BK, int PP, int MG = 1>
 struct TileRegs {
     u32x4 a[PP][BK / 32];      // per panel: dense: BK/32 chunks; 2:4: BK/64 chunks
     uint32_t m[PP][BK / 64];   // per panel: 2:4 metadata words, one per slice
-    u32x4 x[BK / 32];          // X chunks, shared by the PP panels
+    u32x4 x[MG][BK / 32];      // X chunks of MG groups of 16 rows, shared by the PP panels
 };
 
 // Loads of tile column tk for PP consecutive 16-row panels (rows n0 .. n0 + 16 PP - 1, all in
 // one tile row: r0 + 16 PP <= bn) and the matching X chunks.
-template <typename T, int BK, bool HYB, int SP, int PP, bool XT>
-__device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArgs& a, const hts_tile& e, int tk,
+template <typename T, int BK, bool HYB, int SP, int PP, bool XT, int MG>
+__device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP, MG>& R, const GemmArgs& a, const hts_tile& e, int tk,
                                               int64_t n0, int r0, int lane, const uint16_t* xrow) {
+    static_assert(MG == 1 || XT, "two X row groups are loaded as whole rows");
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
     uint32_t moff = 0;
@@ -77,17 +79,19 @@ __device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP>& R, const GemmArg
             for (int s = 0; s < BK / 64; ++s) R.m[q][s] = mrow[16 * q * (BK / 32) + 2 * s + (g >> 1)];
     }
     if constexpr (XT) {
-        // whole X rows: instruction v reads rows 4v .. 4v+3 of the tile column (16 chunks of 16 bytes
-        // each, full cache lines); x_fragments moves them into the operand layout
+        // whole X rows: instruction v of group h reads rows 16h + 4v .. +3 of the tile column (16
+        // chunks of 16 bytes each, full cache lines); x_fragments moves them into the operand layout
         static_assert(BK == 128, "X rows of 128-wide tiles");
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t row = 4 * v + (lane >> 4);
-            R.x[v] = ld16(a.X + (row < a.M ? row : a.M - 1) * a.ldx + (int64_t)tk * BK + 8 * (lane & 15));
-        }
+        for (int h = 0; h < MG; ++h)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = 16 * h + 4 * v + (lane >> 4);
+                R.x[h][v] = ld16(a.X + (row < a.M ? row : a.M - 1) * a.ldx + (int64_t)tk * BK + 8 * (lane & 15));
+            }
     } else {
 #pragma unroll
-        for (int u = 0; u < BK / 32; ++u) R.x[u] = ld16(xrow + (int64_t)tk * BK + koff<SP>(u, g));
+        for (int u = 0; u < BK / 32; ++u) R.x[0][u] = ld16(xrow + (int64_t)tk * BK + koff<SP>(u, g));
     }
     return type;
 }
@@ -120,14 +124,16 @@ __device__ __forceinline__ void load_entries(hts_tile (&E)[NT], const GemmArgs& 
     for (int s = 0; s < NT; ++s) E[s] = a.index[t0 + (t + s < ke ? t + s : ke - 1)];
 }
 
-template <typename T, int BK, int SP, int PP>
-__device__ __forceinline__ void mma_tile(const TileRegs<BK, PP>& R, uint32_t type, f32x4 (&acc)[PP], int lane) {
+template <typename T, int BK, int SP, int PP, int MG>
+__device__ __forceinline__ void mma_tile(const TileRegs<BK, PP, MG>& R, uint32_t type, f32x4 (&acc)[MG][PP], int lane) {
     const int g = lane >> 4;
     if (type == HTS_TILE_DENSE) {
 #pragma unroll
         for (int q = 0; q < PP; ++q)
 #pragma unroll
-            for (int u = 0; u < BK / 32; ++u) acc[q] = mfma_dense<T>(R.a[q][u], R.x[u], acc[q]);
+            for (int u = 0; u < BK / 32; ++u)
+#pragma unroll
+                for (int h = 0; h < MG; ++h) acc[h][q] = mfma_dense<T>(R.a[q][u], R.x[h][u], acc[h][q]);
     } else {
 #pragma unroll
         for (int q = 0; q < PP; ++q)
@@ -135,18 +141,24 @@ __device__ __forceinline__ void mma_tile(const TileRegs<BK, PP>& R, uint32_t typ
             for (int s = 0; s < BK / 64; ++s) {
                 const uint32_t code = R.m[q][s] >> (16 * (g & 1));
                 if (SP == SPARSE_SMFMAC) {
-                    acc[q] = mfma_sparse<T, 0>(R.a[q][s], cat8(R.x[2 * s], R.x[2 * s + 1]), code, acc[q]);
+#pragma unroll
+                    for (int h = 0; h < MG; ++h)
+                        acc[h][q] = mfma_sparse<T, 0>(R.a[q][s], cat8(R.x[h][2 * s], R.x[h][2 * s + 1]), code, acc[h][q]);
                 } else {
                     const u32x4 v = R.a[q][s];
-                    acc[q] = mfma_dense<T>(expand_two_groups(uint2{v[0], v[1]}, code & 0xFFu), R.x[2 * s], acc[q]);
-                    acc[q] = mfma_dense<T>(expand_two_groups(uint2{v[2], v[3]}, (code >> 8) & 0xFFu),
-                                           R.x[2 * s + 1], acc[q]);
+                    const u32x4 e0 = expand_two_groups(uint2{v[0], v[1]}, code & 0xFFu);
+                    const u32x4 e1 = expand_two_groups(uint2{v[2], v[3]}, (code >> 8) & 0xFFu);
+#pragma unroll
+                    for (int h = 0; h < MG; ++h) {
+                        acc[h][q] = mfma_dense<T>(e0, R.x[h][2 * s], acc[h][q]);
+                        acc[h][q] = mfma_dense<T>(e1, R.x[h][2 * s + 1], acc[h][q]);
+                    }
                 }
             }
     }
 }
 
-template <typename T, int BK, bool HYB, int SP, int KS, int NT, int PP, bool XT>
+template <typename T, int BK, bool HYB, int SP, int KS, int NT, int PP, bool XT, int MG = 1>
 __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -162,40 +174,52 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
     const int i = lane & 15;
     const int64_t j = i < a.M ? i : a.M - 1;
     const uint16_t* xrow = a.X + j * a.ldx;
-    __shared__ __attribute__((aligned(16))) uint8_t xbuf[XT ? KS : 1][XT ? 16 * 256 : 16];   // XT: per-wave X staging
-    f32x4 acc[PP];
+    // per-wave LDS: X staging (XT: 4 KB per group of 16 rows), then the wave's partial sums
+    constexpr int XB = XT ? MG * 16 * 256 : 0, RB = MG * PP * 64 * 16, WB = XB > RB ? XB : RB;
+    __shared__ __attribute__((aligned(16))) uint8_t wbuf[KS][WB];
+    f32x4 acc[MG][PP];
 #pragma unroll
-    for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < MG; ++h)
+#pragma unroll
+        for (int q2 = 0; q2 < PP; ++q2) acc[h][q2] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the index records of a batch are read one batch ahead, so their latency hides under the
     // weight loads of the batch before instead of preceding them
     hts_tile E[NT] = {};
     if (HYB && kb < ke) load_entries<NT>(E, a, t0, kb, ke);
     for (int t = kb; t < ke; t += NT) {
-        TileRegs<BK, PP> R[NT];
+        TileRegs<BK, PP, MG> R[NT];
         uint32_t type[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP, PP, XT>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
+            if (t + s < ke) type[s] = load_tile<T, BK, HYB, SP, PP, XT, MG>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
         if (HYB && t + NT < ke) load_entries<NT>(E, a, t0, t + NT, ke);
 #pragma unroll
         for (int s = 0; s < NT; ++s)
             if (t + s < ke) {
-                if constexpr (XT) x_fragments<SP>(R[s].x, xbuf[wave], lane);
-                mma_tile<T, BK, SP, PP>(R[s], type[s], acc, lane);
+                if constexpr (XT)
+#pragma unroll
+                    for (int h = 0; h < MG; ++h) x_fragments<SP>(R[s].x[h], wbuf[wave] + h * 16 * 256, lane);
+                mma_tile<T, BK, SP, PP, MG>(R[s], type[s], acc, lane);
             }
     }
 
-    __shared__ f32x4 red[KS][PP][64];
+    // the partial sums go to the wave's own LDS (its X staging is done: one wave's LDS operations
+    // complete in order), then the KS partials of each output are added in wave order
+    f32x4* red = reinterpret_cast<f32x4*>(wbuf[wave]);
 #pragma unroll
-    for (int q2 = 0; q2 < PP; ++q2) red[wave][q2][lane] = acc[q2];
+    for (int h = 0; h < MG; ++h)
+#pragma unroll
+        for (int q2 = 0; q2 < PP; ++q2) red[(h * PP + q2) * 64 + lane] = acc[h][q2];
     __syncthreads();
-    for (int o = threadIdx.x; o < 256 * PP; o += 64 * KS) {
-        // output (row rr of panel q2, column m of Y^T): lane m + 16*(rr/4), component rr%4
-        const int q2 = o >> 8, m = (o >> 4) & 15, rr = o & 15;
+    for (int o = threadIdx.x; o < 256 * PP * MG; o += 64 * KS) {
+        // output (row rr of panel q2, column 16h + m of Y^T): lane m + 16*(rr/4), component rr%4
+        const int h = o / (256 * PP), q2 = (o >> 8) % PP, m = (o >> 4) & 15, rr = o & 15;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < KS; ++w) sum += red[w][q2][m + 16 * (rr >> 2)][rr & 3];
-        if (m < a.M) store_y1(a.Y, (int64_t)m * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
+        for (int w = 0; w < KS; ++w)
+            sum += reinterpret_cast<const f32x4*>(wbuf[w])[(h * PP + q2) * 64 + m + 16 * (rr >> 2)][rr & 3];
+        const int64_t row = 16 * h + m;
+        if (row < a.M) store_y1(a.Y, row * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
     }
 }
 
@@ -216,7 +240,11 @@ int decode_xt_min_m() {
 
 template <typename T, int BK, bool HYB, int SP, int KS, int NT, int PP>
 void launch6(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-    if constexpr (BK == 128) {
+    if constexpr (BK == 128 && NT <= 2 && KS <= 8) {
+        if (a.M > 16) {             // two groups of 16 X rows per weight fragment (M <= 32)
+            gemm_decode_kernel<T, BK, HYB, SP, KS, NT, PP, true, 2><<<grid, block, 0, s>>>(a);
+            return;
+        }
         if (a.M >= decode_xt_min_m()) {
             gemm_decode_kernel<T, BK, HYB, SP, KS, NT, PP, true><<<grid, block, 0, s>>>(a);
             return;
@@ -231,8 +259,14 @@ hipError_t launch5(const GemmArgs& a, int nt, hipStream_t s) {
     // nt counts 128-wide tile columns; a 64-wide tile is half as many bytes.  With 16 waves
     // (at most 128 registers per lane) only the 2-column batch fits without spills.
     if constexpr (KS < 16 && PP == 1) {
-        if (nt >= 4) {
+        if (nt >= 4 && a.M <= 16) {
             launch6<T, BK, HYB, SP, KS, 4 * 128 / BK, PP>(a, grid, block, s);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (BK == 128) {
+        if (nt == 1) {
+            launch6<T, BK, HYB, SP, KS, 1, PP>(a, grid, block, s);
             return hipGetLastError();
         }
     }
@@ -248,7 +282,7 @@ hipError_t launch4(const GemmArgs& a, int ksplit, int nt, int pp, hipStream_t s)
         if (ksplit >= 8) return launch5<T, BK, HYB, SP, 8, 2>(a, nt, s);
         return launch5<T, BK, HYB, SP, 4, 2>(a, nt, s);
     }
-    if (ksplit >= 16) return launch5<T, BK, HYB, SP, 16, 1>(a, nt, s);
+    if (ksplit >= 16 && a.M <= 16) return launch5<T, BK, HYB, SP, 16, 1>(a, nt, s);
     if (ksplit >= 8) return launch5<T, BK, HYB, SP, 8, 1>(a, nt, s);
     return launch5<T, BK, HYB, SP, 4, 1>(a, nt, s);
 }
@@ -568,6 +602,8 @@ hipError_t launch32(const GemmArgs& a, int ksplit, int pp, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s) {
+    // M = 17 .. 32 runs two groups of X rows per weight fragment: 16-bit data, 128-wide tiles
+    if (a.M < 1 || a.M > 32 || (a.M > 16 && (a.dtype == HTS_FP8_E4M3 || a.bk != 128))) return hipErrorInvalidValue;
     if (a.dtype == HTS_FP8_E4M3)   // 8-bit: the sparse instruction only (no expansion fallback)
         return a.index ? launch8<true>(a, ksplit, nt, pp, s) : launch8<false>(a, ksplit, nt, pp, s);
     if (a.bk == 32) {              // 32-wide tiles: expansion in registers

@@ -77,14 +77,16 @@ int sparse_path() {
     return hts::SPARSE_SMFMAC;
 }
 
-// Largest M served by the streaming kernel (HTS_DECODE_MAX_M, 0..16; default 16).
-int64_t decode_max_m() {
+// Largest M served by the streaming kernel: 32 for 16-bit data on 128-wide tiles (two groups of
+// 16 X rows per weight fragment), else 16.  HTS_DECODE_MAX_M (0..32) lowers it.
+int64_t streaming_max_m(int32_t dtype, int bk) {
+    const int64_t lim = (dtype != HTS_FP8_E4M3 && bk == 128) ? 32 : 16;
     const char* v = getenv("HTS_DECODE_MAX_M");
     if (v && *v) {
         long x = strtol(v, nullptr, 10);
-        if (x >= 0 && x <= 16) return x;
+        if (x >= 0 && x <= 32) return x < lim ? x : lim;
     }
-    return 16;
+    return lim;
 }
 
 // Tiles of 32 rows or 32 columns are below the tiled kernel's 64-row weight groups and 64-wide
@@ -92,7 +94,7 @@ int64_t decode_max_m() {
 // runs the dense product on it.
 bool small_tiles(const hts_desc* d) { return d->bn < 64 || d->bk < 64; }
 uint64_t unpack_workspace_bytes(const hts_desc* d, int64_t M) {
-    if (!small_tiles(d) || M <= decode_max_m()) return 0;
+    if (!small_tiles(d) || M <= streaming_max_m(d->dtype, d->bk)) return 0;
     return ((uint64_t)d->N * d->K * elem_bytes(d->dtype) + 255) & ~uint64_t(255);
 }
 
@@ -102,8 +104,9 @@ uint64_t unpack_workspace_bytes(const hts_desc* d, int64_t M) {
 //     (K = 4096, 11008 rows: 17.2 us at pp = 1 against 20.2 at pp = 2);
 //   waves per workgroup: 4 when pp = 2 still leaves >= 400 workgroups, else 8 (8-bit weights at
 //     M < 8: 4 -- 7B up, M=1: 10.8 us against 13.6 at 8);
-//   tile columns per batch of loads: 2.
-// HTS_DECODE_PP=1|2, HTS_DECODE_KSPLIT=4|8|16 and HTS_DECODE_NT=2|4 override.
+//   tile columns per batch of loads: 2 (1 at M > 16, where two groups of X rows double the X
+//     registers and a batch of two would leave one wave per SIMD).
+// HTS_DECODE_PP=1|2, HTS_DECODE_KSPLIT=4|8|16 and HTS_DECODE_NT=1|2|4 override.
 int decode_pp(const hts::GemmArgs& a) {
     if (a.N % 32) return 1;                  // every accepted shape has 32 | N; kept as a guard
     const char* v = getenv("HTS_DECODE_PP");
@@ -122,9 +125,8 @@ int decode_ksplit(const hts::GemmArgs& a) {
 
 int decode_nt(const hts::GemmArgs& a) {
     const char* v = getenv("HTS_DECODE_NT");
-    if (v && (!strcmp(v, "2") || !strcmp(v, "4"))) return atoi(v);
-    (void)a;
-    return 2;
+    if (v && (!strcmp(v, "1") || !strcmp(v, "2") || !strcmp(v, "4"))) return atoi(v);
+    return a.M > 16 ? 1 : 2;
 }
 
 
@@ -138,8 +140,8 @@ int decode_nt(const hts::GemmArgs& a) {
 // M = 17 23.7 / 60.5 us (5 parts), 64 28.4 / 60.6, 128 37.2 / 61.3, 256 54.4 / 62.1 (2 parts);
 // at 258 and more blocks (M > 256 here) splitting was slower at every count tried.
 // HTS_PREFILL_SPLIT=1..16 overrides.  block_rows: weight rows per block of the launch.
-int prefill_split(int64_t M, int64_t N, int64_t K, int32_t dtype, int block_rows) {
-    if (M <= decode_max_m()) return 1;
+int prefill_split(int64_t M, int64_t N, int64_t K, int32_t dtype, int bk, int block_rows) {
+    if (M <= streaming_max_m(dtype, bk)) return 1;
     const int64_t slices = K * elem_bytes(dtype) / 128;
     const char* v = getenv("HTS_PREFILL_SPLIT");
     if (v && *v) {
@@ -171,13 +173,14 @@ void attach_split(hts::GemmArgs& a, int nsplit, void* ws, size_t ws_bytes) {
 
 hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
     hipError_t e;
-    if (a.M <= decode_max_m()) {
+    if (a.M <= streaming_max_m(a.dtype, a.bk)) {
         e = hts::launch_gemm_decode(a, decode_ksplit(a), decode_nt(a), decode_pp(a), sparse_path(), s);
     } else {
         // the tiled kernel addresses X rows (and rows of a row-major W) by 32-bit byte offsets
         // from its block's first row
         if (a.ldx > (int64_t(1) << 24) || (!a.index && a.ldw > (int64_t(1) << 24)))
-            return fail(HTS_ERR_UNSUPPORTED, "leading dimension above 2^24 elements at M > %lld", (long long)decode_max_m());
+            return fail(HTS_ERR_UNSUPPORTED, "leading dimension above 2^24 elements at M > %lld",
+                        (long long)streaming_max_m(a.dtype, a.bk));
         if (a.index && a.K / a.bk > hts::kMaxTileColsPerRow)
             return fail(HTS_ERR_UNSUPPORTED, "K/bk=%lld tile columns exceed the %d of one tile row the tiled kernel holds",
                         (long long)(a.K / a.bk), hts::kMaxTileColsPerRow);
@@ -298,7 +301,8 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes) {
     const uint64_t ws = unpack_workspace_bytes(d, M);
     // the unpacked weight (tiles of 32), then the parts of a split product
     const int br = (ws || d->bn != 64) ? 128 : 64;
-    *bytes = (size_t)(ws + split_bytes(M, d->N, prefill_split(M, d->N, d->K, d->dtype, br)));
+    const int bk = ws ? ((d->K % 128 == 0) ? 128 : 64) : d->bk;   // the unpacked product's slices
+    *bytes = (size_t)(ws + split_bytes(M, d->N, prefill_split(M, d->N, d->K, d->dtype, bk, br)));
     return ok();
 }
 
@@ -340,7 +344,7 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
         a.ldx = ldx;
         a.Y = Y;
         a.ldy = ldy;
-        attach_split(a, prefill_split(M, d->N, d->K, d->dtype, 128), static_cast<uint8_t*>(workspace) + ws,
+        attach_split(a, prefill_split(M, d->N, d->K, d->dtype, a.bk, 128), static_cast<uint8_t*>(workspace) + ws,
                      workspace_bytes - ws);
         return run_gemm(a, static_cast<hipStream_t>(stream));
     }
@@ -360,7 +364,7 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
     a.ldx = ldx;
     a.Y = Y;
     a.ldy = ldy;
-    attach_split(a, prefill_split(M, d->N, d->K, d->dtype, d->bn == 64 ? 64 : 128), workspace, workspace_bytes);
+    attach_split(a, prefill_split(M, d->N, d->K, d->dtype, d->bk, d->bn == 64 ? 64 : 128), workspace, workspace_bytes);
     return run_gemm(a, static_cast<hipStream_t>(stream));
 }
 
@@ -396,7 +400,7 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const 
     a.ldx = ldx;
     a.Y = Y;
     a.ldy = ldy;
-    attach_split(a, prefill_split(M, N, K, dtype, 128), workspace, workspace_bytes);
+    attach_split(a, prefill_split(M, N, K, dtype, a.bk, 128), workspace, workspace_bytes);
     return run_gemm(a, static_cast<hipStream_t>(stream));
 }
 
@@ -406,7 +410,7 @@ hts_status hts_dense_gemm_workspace(int32_t dtype, int64_t M, int64_t N, int64_t
         return fail(HTS_ERR_SHAPE, "M=%lld N=%lld K=%lld (M >= 0, N and K positive)", (long long)M, (long long)N,
                     (long long)K);
     if (!bytes) return fail(HTS_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = (size_t)split_bytes(M, N, prefill_split(M, N, K, dtype, 128));
+    *bytes = (size_t)split_bytes(M, N, prefill_split(M, N, K, dtype, (K % 128 == 0) ? 128 : 64, 128));
     return ok();
 }
 

@@ -198,7 +198,7 @@ def run_mid_m(hts, wl, dev, time_graph, quick):
         wsd = hts.hts_dense_gemm_workspace(Xm.dtype, M, L.N, L.K)
         WSh = torch.empty(wsh, dtype=torch.uint8, device=dev) if wsh else None
         WSd = torch.empty(wsd, dtype=torch.uint8, device=dev) if wsd else None
-        per, reps = (2, 2) if quick else (n, 5)
+        per, reps = (2, 2) if quick else (8 * n, 5)     # 8 launches per weight copy: graph launch cost amortized
         t_h = time_graph(lambda i: hts.gemm(Xm, pws[i % n_rot], out=Ys[i % n], workspace=WSh), per, reps)
         t_d = time_graph(lambda i: hts.dense_gemm(Xm, Wd[i % n_rd], out=Ys[i % n], workspace=WSd), per, reps)
         t_t = time_graph(lambda i: torch.matmul(Xm, Wd[i % n_rd].t(), out=Ys[i % n]), per, reps)

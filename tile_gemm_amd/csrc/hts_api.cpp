@@ -102,8 +102,8 @@ uint64_t unpack_workspace_bytes(const hts_desc* d, int64_t M) {
 //   panels per workgroup pp: 2 (each X fragment feeds two 16-row panels) when K >= 4608 --
 //     K = 5120: M=16 36.9 -> 29.4 us (13824 rows), 20.1 -> 16.4 us (5120 rows) -- else 1
 //     (K = 4096, 11008 rows: 17.2 us at pp = 1 against 20.2 at pp = 2);
-//   waves per workgroup: 4 when pp = 2 still leaves >= 400 workgroups, else 8 (8-bit weights at
-//     M < 8: 4 -- 7B up, M=1: 10.8 us against 13.6 at 8);
+//   waves per workgroup: 4 when pp = 2 still leaves >= 400 workgroups, else 8 (8-bit packed
+//     weights: 4 -- 7B up, M=1: 10.3 us against 12.3 at 8);
 //   tile columns per batch of loads: 2 (1 at M > 16, where two groups of X rows double the X
 //     registers and a batch of two would leave one wave per SIMD).
 // HTS_DECODE_PP=1|2, HTS_DECODE_KSPLIT=4|8|16 and HTS_DECODE_NT=1|2|4 override.
@@ -118,8 +118,9 @@ int decode_pp(const hts::GemmArgs& a) {
 int decode_ksplit(const hts::GemmArgs& a) {
     const char* v = getenv("HTS_DECODE_KSPLIT");
     if (v && (!strcmp(v, "4") || !strcmp(v, "8") || !strcmp(v, "16"))) return atoi(v);
-    // 8-bit tiles are half the bytes: at the smallest M fewer, longer waves stream better
-    if (a.dtype == HTS_FP8_E4M3 && a.M < 8) return 4;
+    // 8-bit tiles are half the bytes: fewer, longer waves stream better -- for the packed weight
+    // at every M (7B up: M=8 12.2 -> 10.8 us, M=16 12.6 -> 11.7), for a row-major one below M = 8
+    if (a.dtype == HTS_FP8_E4M3 && (a.index || a.M < 8)) return 4;
     return (decode_pp(a) == 2 && a.N / 32 >= 400) ? 4 : 8;
 }
 

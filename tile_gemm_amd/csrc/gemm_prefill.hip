@@ -117,9 +117,7 @@ struct Ctx {
     int64_t N, n0;
     int r0;                     // first row of the block inside its tile (0 when BN == bn)
     int wave, lane;
-    int lch;                    // log2 of the tile columns per chunk of the list
     uint32_t lnd;               // lane c: dense tiles of chunk c (they come first in the chunk)
-    const uint2* list;          // {val_off, meta_off} of the tile row's tiles in list order
     // the ordered list in registers, 64 entries per register (K / bk <= 256).  It is read in order,
     // and after each block of 64 entries the registers move down by one (shift_list), so entry p
     // is always lane p % 64 of the first register: one lane read, no register select.
@@ -404,8 +402,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
     uint2* list = reinterpret_cast<uint2*>(smem + Lo::LIST);
     uint16_t* lcol = reinterpret_cast<uint16_t*>(smem + Lo::LCOL);
     uint8_t* cnd = reinterpret_cast<uint8_t*>(smem + Lo::WCNT);   // dense tiles per chunk (<= 64 chunks)
-    C.list = list;
-    C.lch = lch;
     if (HYB) {
         const int tn = (int)(C.n0 / a.bn);
         const int t = tid;                         // one tile column per thread (Tk <= 256)

@@ -296,10 +296,13 @@ def run_block(hts, wl, dev, time_graph, quick):
         packed = {L.name: hts.pack(Ws[L.name], mp[L.name].cpu().numpy(), L.bn, L.bk) for L in cfg.layers}
         bufs = block.buffers(M, packed, X.dtype, dev)
         t = time_graph(lambda i: block.forward(X, packed, bufs), 1, reps)
+        # the up product writing silu(gate) * up itself (the dense block has no such variant)
+        t_f = time_graph(lambda i: block.forward(X, packed, bufs, fused=True), 1, reps)
         flops = block.kept_flops(M, packed)
         ns = {L.name: int(mp[L.name].sum().item()) for L in cfg.layers}
         out[kind] = {"us": round(t * 1e6, 1), "TFLOP/s": round(flops / t / 1e12, 1),
                      "speedup_vs_dense": round(t_dense / t, 3),
+                     "fused_gate_us": round(t_f * 1e6, 1), "fused_gate_speedup_vs_dense": round(t_dense / t_f, 3),
                      "sparse_tiles": ns, "overall_sparsity": round(0.5 * sum(ns.values()) / T, 4)}
         del packed, bufs
     out["dense_same_library_us"] = round(t_dense * 1e6, 1)

@@ -198,6 +198,20 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K,
  * product would be split, see hts_gemm_workspace). */
 hts_status hts_dense_gemm_workspace(int32_t dtype, int64_t M, int64_t N, int64_t K, size_t* bytes);
 
+/* Device, asynchronous.  The hybrid product with the gated-MLP step in its output stage:
+ * Y[M,N] = silu(G) * (X[M,K] . mask(W)^T), silu(x) = x / (1 + e^-x), with G[M,N] (ldg) in
+ * y_dtype.  The up projection of a decoder block whose linear layers are hybrid tile-sparse
+ * writes silu(gate) * up in one pass instead of writing up and running hts_silu_mul (the pages
+ * prune the linear layers of LLaMA models; this step is the architecture's, not the method's).
+ * The product is hts_gemm's (same kernels, tiles, workspace and determinism); the output stage
+ * multiplies the fp32 sum by silu(g) in fp32 and rounds once to y_dtype.  G: 16-byte aligned,
+ * ldg >= N and a multiple of 4; G may be Y (each element is read, then written, by one
+ * thread).  Errors as hts_gemm's, and HTS_ERR_INVALID_ARG when G is NULL with M > 0. */
+hts_status hts_gemm_silu_mul(const hts_desc* d, const hts_tile* index, const void* values,
+                             const uint32_t* meta, int64_t M, const void* X, int64_t ldx,
+                             const void* G, int64_t ldg, void* Y, int64_t ldy, int32_t y_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device, asynchronous.  H[M,N] = silu(G) * U elementwise, silu(x) = x / (1 + e^-x), fp32
  * arithmetic, one round-to-nearest-even to dtype (HTS_F16 / HTS_BF16, shared by G, U and H):
  * the gated-MLP step between the gate / up projections and the down projection of a decoder

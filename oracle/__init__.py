@@ -10,11 +10,11 @@ from .hybrid import (TILE_DENSE, TILE_SPARSE24, VALID_NIBBLES, widen_f32, widen_
                      sparse_tile_keep, masked_weights, plan, pack, unpack, gemm_ref, hybrid_ref,
                      within_tolerance, column_norms, wanda_tile_cost, wanda_tile_map, density,
                      mask_scores, malformed_groups, pack_masked, masked_weights_from_mask, wanda_global_maps,
-                     silu_mul_ref, storage_type, e4m3_value)
+                     silu_mul_ref, gated_ref, storage_type, e4m3_value)
 
 __all__ = ["TILE_DENSE", "TILE_SPARSE24", "VALID_NIBBLES", "widen_f32", "widen_f64", "check_grid",
            "as_tiles", "from_tiles", "selection_scores", "keep_two_of_four", "kept_positions",
            "sparse_tile_keep", "masked_weights", "plan", "pack", "unpack", "gemm_ref", "hybrid_ref",
            "within_tolerance", "column_norms", "wanda_tile_cost", "wanda_tile_map", "density",
            "mask_scores", "malformed_groups", "pack_masked", "masked_weights_from_mask", "wanda_global_maps",
-           "silu_mul_ref", "storage_type", "e4m3_value"]
+           "silu_mul_ref", "gated_ref", "storage_type", "e4m3_value"]

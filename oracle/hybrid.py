@@ -439,6 +439,14 @@ def silu_mul_ref(G_bits: np.ndarray, U_bits: np.ndarray, dtype: str) -> np.ndarr
     return g / (1.0 + np.exp(-g)) * u
 
 
+def gated_ref(G_bits: np.ndarray, Y: np.ndarray, dtype: str) -> np.ndarray:
+    """silu(G) * Y in float64, G exactly widened from its 16-bit patterns (or taken as float32 when
+    dtype is "f32"), Y a float64 product: the gated-MLP step applied to an unrounded product, as
+    when it is done in the product's output stage.  With Y the widened 16-bit U it is silu_mul_ref."""
+    g = np.asarray(G_bits, np.float32).astype(np.float64) if dtype == "f32" else widen_f64(G_bits, dtype)
+    return g / (1.0 + np.exp(-g)) * np.asarray(Y, np.float64)
+
+
 def wanda_global_maps(costs, n_sparse: int):
     """Global allocation over several layers (PATCH page, section 4, ablations: a sparsity
     target shared by the whole model beats one per layer): the n_sparse tiles of lowest cost

@@ -96,6 +96,24 @@ def test_plan_rejects_bad_arguments():
 A16, A8 = 0x10000, 0x10008
 
 
+def test_gated_gemm_rejects_bad_arguments_before_any_launch():
+    # hts_gemm_silu_mul: hts_gemm's checks, plus G (non-NULL, 16-byte aligned) and ldg (>= N, a
+    # multiple of 4); M == 0 is a no-op even without G
+    L = hts.lib()
+    d = hts.make_desc(256, 256, 64, 64, "f16")
+
+    def gated(G=A16, ldg=256, M=4, yd=2, index=A16):
+        return L.hts_gemm_silu_mul(ctypes.byref(d), index, A16, A16, M, A16, 256, G, ldg, A16, 256, yd, None, 0, None)
+
+    assert gated(G=None) == 1
+    assert gated(G=A8) == 4
+    assert gated(ldg=255) == 3
+    assert gated(ldg=258) == 4
+    assert gated(index=None) == 1
+    assert gated(yd=7) == 2
+    assert gated(G=None, M=0) == 0
+
+
 def test_gemm_rejects_bad_arguments_before_any_launch():
     L = hts.lib()
     d = hts.make_desc(256, 256, 64, 64, "f16")

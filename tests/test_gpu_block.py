@@ -78,23 +78,47 @@ def test_block_step_parity(hybrid):
     assert np.all(np.abs(got - h_ref) <= 2.0 ** -8 * np.abs(h_ref) + 2.0 ** -24)
 
 
-def test_block_step_in_a_graph():
+def test_block_step_fused_gate_parity():
+    # the up product writes silu(gate) * up in its output stage: h against the oracle's gated step
+    # on the unrounded up product, and the down projection against h
+    c = wl.config("7b_block")
+    M = 300
+    say(f"[block-fused] M={M}")
+    W = _weights(c, M, True)
+    X = activations(c.cfg_id, "q")[:M]
+    Xt = hts.tensor_from_bits(np.ascontiguousarray(X), "bf16", DEV)
+    bufs = block.buffers(M, W, Xt.dtype, DEV)
+    block.forward(Xt, W, bufs, fused=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    bits = {k: hts.bits_from_tensor(v) for k, v in bufs.items()}
+    up_ref = oracle.gemm_ref(X[rows], _masked(c, "up"), "bf16")
+    h_ref = oracle.gated_ref(bits["gate"][rows], up_ref, "bf16")
+    ok, rel = oracle.within_tolerance(oracle.widen_f64(bits["h"][rows], "bf16"), h_ref, TOL)
+    assert ok, f"h: {rel:.3e}"
+    d_ref = oracle.gemm_ref(bits["h"][rows], _masked(c, "down"), "bf16")
+    ok, rel = oracle.within_tolerance(oracle.widen_f64(bits["down"][rows], "bf16"), d_ref, TOL)
+    assert ok, f"down: {rel:.3e}"
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_block_step_in_a_graph(fused):
     # captured once, replayed with eager work in between: every replay equals the eager step
     c = wl.config("7b_block")
     M = 128
     W = _weights(c, M, True)
     X = hts.tensor_from_bits(np.ascontiguousarray(activations(c.cfg_id, "q")[:M]), "bf16", DEV)
     bufs = block.buffers(M, W, X.dtype, DEV)
-    eager = block.forward(X, W, bufs).clone()
+    eager = block.forward(X, W, bufs, fused).clone()
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        block.forward(X, W, bufs)
+        block.forward(X, W, bufs, fused)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        block.forward(X, W, bufs)
+        block.forward(X, W, bufs, fused)
     for rep in range(3):
         for v in bufs.values():
             v.fill_(0)

@@ -553,6 +553,19 @@ def test_silu_mul_closed_forms():
                        rtol=1e-15, atol=0)
 
 
+def test_gated_ref_reduces_to_silu_mul():
+    # the gated output stage on an unrounded product: with the product equal to a 16-bit U it is the
+    # elementwise step exactly; a product of 1.0 gives the tabulated logistic values; fp32 G (y_dtype
+    # f32) is taken as is
+    g = np.random.default_rng(61)
+    G = wl.gaussian_bits((64, 48), 2.0, "bf16", g)
+    U = wl.gaussian_bits((64, 48), 1.0, "bf16", g)
+    assert np.array_equal(oracle.gated_ref(G, oracle.widen_f64(U, "bf16"), "bf16"), oracle.silu_mul_ref(G, U, "bf16"))
+    one = np.ones(3)
+    assert np.allclose(oracle.gated_ref(np.array([1.0, 2.0, -1.0], np.float32), one, "f32"),
+                       [0.7310585786300049, 2 * 0.8807970779778823, -0.2689414213699951], rtol=1e-15, atol=0)
+
+
 # ---------------------------------------------------------------------------
 # the 8-bit (OCP E4M3) variant
 # ---------------------------------------------------------------------------

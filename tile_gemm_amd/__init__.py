@@ -60,6 +60,8 @@ _SIGS = {
     "hts_gemm_workspace": (ctypes.c_int, [ctypes.POINTER(hts_desc), _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "hts_gemm": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _I32,
                                 _VP, ctypes.c_size_t, _VP]),
+    "hts_gemm_silu_mul": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _VP,
+                                         _I64, _I32, _VP, ctypes.c_size_t, _VP]),
     "hts_dense_gemm": (ctypes.c_int, [_I32, _I64, _I64, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _I32, _VP,
                                       ctypes.c_size_t, _VP]),
     "hts_dense_gemm_workspace": (ctypes.c_int, [_I32, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
@@ -179,6 +181,15 @@ def hts_gemm(desc, index, values, meta, X, Y, y_dtype=None, workspace=None, stre
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hts_gemm(ctypes.byref(desc), _ptr(index), _ptr(values), _ptr(meta), M, _ptr(X), X.stride(0),
                           _ptr(Y), Y.stride(0), yd, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hts_gemm_silu_mul(desc, index, values, meta, X, G, Y, y_dtype=None, workspace=None, stream=None) -> None:
+    M = X.shape[0]
+    yd = _dt(Y.dtype) if y_dtype is None else y_dtype
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hts_gemm_silu_mul(ctypes.byref(desc), _ptr(index), _ptr(values), _ptr(meta), M, _ptr(X),
+                                   X.stride(0), _ptr(G), G.stride(0), _ptr(Y), Y.stride(0), yd, _ptr(workspace),
+                                   ws_bytes, _stream(stream)))
 
 
 def hts_dense_gemm_workspace(dtype, M: int, N: int, K: int) -> int:
@@ -312,6 +323,25 @@ def gemm(X: torch.Tensor, pw: PackedWeight, out_dtype=None, out: Optional[torch.
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
     hts_gemm(pw.desc, pw.index, pw.values, pw.meta, X, out, workspace=workspace, stream=stream)
+    return out
+
+
+def gemm_silu_mul(X: torch.Tensor, pw: PackedWeight, G: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  stream=None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = silu(G) * (X . mask(W)^T): the product with the gated-MLP step in its output stage.  G
+    and Y share a type (the output type); G may be Y."""
+    M = X.shape[0]
+    if G.shape != (M, pw.N):
+        raise ValueError(f"G has shape {tuple(G.shape)}, expected {(M, pw.N)}")
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=G.dtype, device=X.device)
+    if out.dtype != G.dtype:
+        raise ValueError("G and the output must share a type")
+    if workspace is None:
+        nbytes = hts_gemm_workspace(pw.desc, M)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    hts_gemm_silu_mul(pw.desc, pw.index, pw.values, pw.meta, X, G, out, workspace=workspace, stream=stream)
     return out
 
 

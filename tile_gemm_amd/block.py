@@ -20,7 +20,7 @@ from typing import Dict
 
 import torch
 
-from . import PackedWeight, dense_gemm, gemm, silu_mul
+from . import PackedWeight, dense_gemm, gemm, gemm_silu_mul, silu_mul
 
 PROJECTIONS = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -40,12 +40,19 @@ def _linear(x: torch.Tensor, w, out: torch.Tensor) -> torch.Tensor:
     return dense_gemm(x, w, out=out)
 
 
-def forward(X: torch.Tensor, weights: Dict[str, object], bufs: Dict[str, torch.Tensor]) -> torch.Tensor:
-    """One block step on M = X.shape[0] tokens; returns the down-projection output."""
-    for name in ("q", "k", "v", "gate", "up"):
+def forward(X: torch.Tensor, weights: Dict[str, object], bufs: Dict[str, torch.Tensor],
+            fused: bool = False) -> torch.Tensor:
+    """One block step on M = X.shape[0] tokens; returns the down-projection output.  fused (packed
+    up weight only): the up product writes silu(gate) * up itself (hts_gemm_silu_mul) instead of
+    writing up for a separate elementwise pass."""
+    fuse = fused and isinstance(weights["up"], PackedWeight)
+    for name in ("q", "k", "v", "gate") + (() if fuse else ("up",)):
         _linear(X, weights[name], bufs[name])
     _linear(bufs["q"], weights["o"], bufs["o"])          # attention output stand-in: A = q
-    silu_mul(bufs["gate"], bufs["up"], out=bufs["h"])
+    if fuse:
+        gemm_silu_mul(X, weights["up"], bufs["gate"], out=bufs["h"])
+    else:
+        silu_mul(bufs["gate"], bufs["up"], out=bufs["h"])
     return _linear(bufs["h"], weights["down"], bufs["down"])
 
 

@@ -31,6 +31,32 @@ __device__ __forceinline__ void store_y1(void* Y, int64_t off, int32_t y_dtype, 
     }
 }
 
+// Gated output: silu(g) * v with silu(x) = x / (1 + e^-x), g = G[off] in the output type (fp32
+// arithmetic, one rounding when the result is stored).
+__device__ __forceinline__ float gate_value(const void* G, int64_t off, int32_t dt) {
+    if (dt == HTS_F32) return reinterpret_cast<const float*>(G)[off];
+    const uint32_t b = reinterpret_cast<const uint16_t*>(G)[off];
+    return dt == HTS_BF16 ? widen<BF16T>(b) : widen<F16T>(b);
+}
+__device__ __forceinline__ float silu_times(float g, float v) { return g / (1.0f + expf(-g)) * v; }
+// Four consecutive gate values G[off .. off+3] in one load (off is a multiple of 4 and G is
+// 16-byte aligned: 8 bytes for 16-bit types, 16 for fp32).
+__device__ __forceinline__ f32x4 load_gate4(const void* G, int64_t off, int32_t dt) {
+    if (dt == HTS_F32) return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(G) + off);
+    const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(G) + off);
+    const uint32_t h[4] = {b.x & 0xFFFFu, b.x >> 16, b.y & 0xFFFFu, b.y >> 16};
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = dt == HTS_BF16 ? widen<BF16T>(h[e]) : widen<F16T>(h[e]);
+    return r;
+}
+__device__ __forceinline__ f32x4 silu_times4(f32x4 g, f32x4 v) {
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = silu_times(g[e], v[e]);
+    return r;
+}
+
 __device__ __forceinline__ void store_y4(void* Y, int64_t off, int32_t y_dtype, f32x4 v) {
     if (y_dtype == HTS_F32) {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + off) = v;

@@ -229,7 +229,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
         for (int w = 0; w < KS; ++w)
             sum += reinterpret_cast<const f32x4*>(wbuf[w])[(h * PP + q2) * 64 + m + 16 * (rr >> 2)][rr & 3];
         const int64_t row = 16 * h + m;
-        if (row < a.M) store_y1(a.Y, row * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
+        if (row < a.M) {
+            const int64_t n = n0 + 16 * q2 + rr;
+            if (a.gate) sum = silu_times(gate_value(a.gate, row * a.ldg + n, a.y_dtype), sum);
+            store_y1(a.Y, row * a.ldy + n, a.y_dtype, sum);
+        }
     }
 }
 
@@ -452,7 +456,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a)
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < KS; ++w) sum += red[w][q2][m + 16 * (rr >> 2)][rr & 3];
-        if (m < a.M) store_y1(a.Y, (int64_t)m * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
+        if (m < a.M) {
+            const int64_t n = n0 + 16 * q2 + rr;
+            if (a.gate) sum = silu_times(gate_value(a.gate, (int64_t)m * a.ldg + n, a.y_dtype), sum);
+            store_y1(a.Y, (int64_t)m * a.ldy + n, a.y_dtype, sum);
+        }
     }
 }
 
@@ -589,7 +597,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode32_kernel(const GemmArgs a
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < KS; ++w) sum += red[w][q2][m + 16 * (rr >> 2)][rr & 3];
-        if (m < a.M) store_y1(a.Y, (int64_t)m * a.ldy + n0 + 16 * q2 + rr, a.y_dtype, sum);
+        if (m < a.M) {
+            const int64_t n = n0 + 16 * q2 + rr;
+            if (a.gate) sum = silu_times(gate_value(a.gate, (int64_t)m * a.ldg + n, a.y_dtype), sum);
+            store_y1(a.Y, (int64_t)m * a.ldy + n, a.y_dtype, sum);
+        }
     }
 }
 

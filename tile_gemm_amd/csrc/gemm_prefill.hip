@@ -527,6 +527,22 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         odt = HTS_F32;
     }
     const int j = lane & 15, q = lane >> 4;
+    if (a.gate && nsplit == 1) {
+        // gated output (a split product applies the gate in the sum of its parts): every gate value
+        // of the lane is loaded before the first store, since G may be Y
+        f32x4 gv[4][NBJ];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int bj = 0; bj < NBJ; ++bj) {
+                const int64_t m = m0 + wm * WTM + 16 * bj + j, n = C.n0 + 64 * wn + 16 * b + 4 * q;
+                gv[b][bj] = m < a.M ? load_gate4(a.gate, m * a.ldg + n, a.y_dtype) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int bj = 0; bj < NBJ; ++bj) acc[b][bj] = silu_times4(gv[b][bj], acc[b][bj]);
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int64_t n = C.n0 + 64 * wn + 16 * b + 4 * q;
@@ -540,7 +556,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
 
 // Sum of the parts of a split product, in part order (deterministic), rounded once to y_dtype.
 // One thread per 4 consecutive outputs of a row (N is a multiple of 64).
-__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int nsplit, int64_t M,
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int nsplit, const void* gate,
+                                                        int64_t ldg, int64_t M,
                                                         int64_t N, void* Y, int64_t ldy, int32_t y_dtype) {
     const int64_t nq = N / 4;
     const int64_t qi = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -551,6 +568,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
         const f32x4 v = *reinterpret_cast<const f32x4*>(part + ((int64_t)i * M + m) * N + n);
         acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
     }
+    if (gate) acc = silu_times4(load_gate4(gate, m * ldg + n, y_dtype), acc);
     store_y4(Y, m * ldy + n, y_dtype, acc);
 }
 
@@ -590,7 +608,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     const int64_t quads = a.M * (a.N / 4);
-    split_sum_kernel<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s>>>(a.part, nsplit, a.M, a.N, a.Y,
+    split_sum_kernel<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s>>>(a.part, nsplit, a.gate, a.ldg, a.M, a.N, a.Y,
                                                                               a.ldy, a.y_dtype);
     return hipGetLastError();
 }

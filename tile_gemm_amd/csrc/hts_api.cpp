@@ -190,6 +190,74 @@ hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
     return hip_status(e, "product kernel launch");
 }
 
+// hts_gemm and hts_gemm_silu_mul (gate: G[M,N] in y_dtype, or nullptr)
+hts_status gemm_impl(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta, int64_t M,
+                     const void* X, int64_t ldx, const void* gate, int64_t ldg, void* Y, int64_t ldy, int32_t y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
+    if (!is_out(y_dtype)) return fail(HTS_ERR_DTYPE, "y_dtype %d is not F32, F16 or BF16", y_dtype);
+    if ((st = check_ptr(index, "index")) || (st = check_ptr(values, "values"))) return st;
+    if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
+    if ((st = check_ld(ldx, d->K, ld_mult(d->dtype), "ldx")) || (st = check_ld(ldy, d->N, 4, "ldy"))) return st;
+    if (M == 0) return ok();
+    if ((st = check_ptr(X, "X")) || (st = check_ptr(Y, "Y"))) return st;
+    if (gate && (st = check_ptr(gate, "G"))) return st;
+    const uint64_t ws = unpack_workspace_bytes(d, M);
+    if (ws) {
+        if (!workspace || workspace_bytes < ws)
+            return fail(HTS_ERR_WORKSPACE, "tiles of %dx%d at M=%lld need a %llu-byte workspace (got %zu)", d->bn,
+                        d->bk, (long long)M, (unsigned long long)ws, workspace_bytes);
+        if (!aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
+        if (d->N % 64 || d->K % 64)
+            return fail(HTS_ERR_UNSUPPORTED, "the unpacked product needs N and K multiples of 64");
+        // the unpacked weight, row-major with ldw = K, then the same-library dense product on it
+        hipError_t e = hts::launch_unpack(*d, index, static_cast<const uint16_t*>(values), meta,
+                                          static_cast<uint16_t*>(workspace), d->K, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_status(e, "unpack kernel launch");
+        hts::GemmArgs a{};
+        a.dtype = d->dtype;
+        a.y_dtype = y_dtype;
+        a.M = M;
+        a.N = d->N;
+        a.K = d->K;
+        a.bn = 64;
+        a.bk = (d->K % 128 == 0) ? 128 : 64;
+        a.W = static_cast<const uint16_t*>(workspace);
+        a.ldw = d->K;
+        a.X = static_cast<const uint16_t*>(X);
+        a.ldx = ldx;
+        a.Y = Y;
+        a.ldy = ldy;
+        a.gate = gate;
+        a.ldg = ldg;
+        attach_split(a, prefill_split(M, d->N, d->K, d->dtype, a.bk, 128), static_cast<uint8_t*>(workspace) + ws,
+                     workspace_bytes - ws);
+        return run_gemm(a, static_cast<hipStream_t>(stream));
+    }
+    if (workspace && !aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
+    hts::GemmArgs a{};
+    a.dtype = d->dtype;
+    a.y_dtype = y_dtype;
+    a.M = M;
+    a.N = d->N;
+    a.K = d->K;
+    a.bn = d->bn;
+    a.bk = d->bk;
+    a.index = index;
+    a.values = static_cast<const uint16_t*>(values);
+    a.meta = meta;
+    a.X = static_cast<const uint16_t*>(X);
+    a.ldx = ldx;
+    a.Y = Y;
+    a.ldy = ldy;
+    a.gate = gate;
+    a.ldg = ldg;
+    attach_split(a, prefill_split(M, d->N, d->K, d->dtype, d->bk, d->bn == 64 ? 64 : 128), workspace, workspace_bytes);
+    return run_gemm(a, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -310,63 +378,19 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes) {
 hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta, int64_t M,
                     const void* X, int64_t ldx, void* Y, int64_t ldy, int32_t y_dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
-    hts_status st = check_desc(d);
-    if (st) return st;
-    if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
-    if (!is_out(y_dtype)) return fail(HTS_ERR_DTYPE, "y_dtype %d is not F32, F16 or BF16", y_dtype);
-    if ((st = check_ptr(index, "index")) || (st = check_ptr(values, "values"))) return st;
-    if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
-    if ((st = check_ld(ldx, d->K, ld_mult(d->dtype), "ldx")) || (st = check_ld(ldy, d->N, 4, "ldy"))) return st;
-    if (M == 0) return ok();
-    if ((st = check_ptr(X, "X")) || (st = check_ptr(Y, "Y"))) return st;
-    const uint64_t ws = unpack_workspace_bytes(d, M);
-    if (ws) {
-        if (!workspace || workspace_bytes < ws)
-            return fail(HTS_ERR_WORKSPACE, "tiles of %dx%d at M=%lld need a %llu-byte workspace (got %zu)", d->bn,
-                        d->bk, (long long)M, (unsigned long long)ws, workspace_bytes);
-        if (!aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
-        if (d->N % 64 || d->K % 64)
-            return fail(HTS_ERR_UNSUPPORTED, "the unpacked product needs N and K multiples of 64");
-        // the unpacked weight, row-major with ldw = K, then the same-library dense product on it
-        hipError_t e = hts::launch_unpack(*d, index, static_cast<const uint16_t*>(values), meta,
-                                          static_cast<uint16_t*>(workspace), d->K, static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return hip_status(e, "unpack kernel launch");
-        hts::GemmArgs a{};
-        a.dtype = d->dtype;
-        a.y_dtype = y_dtype;
-        a.M = M;
-        a.N = d->N;
-        a.K = d->K;
-        a.bn = 64;
-        a.bk = (d->K % 128 == 0) ? 128 : 64;
-        a.W = static_cast<const uint16_t*>(workspace);
-        a.ldw = d->K;
-        a.X = static_cast<const uint16_t*>(X);
-        a.ldx = ldx;
-        a.Y = Y;
-        a.ldy = ldy;
-        attach_split(a, prefill_split(M, d->N, d->K, d->dtype, a.bk, 128), static_cast<uint8_t*>(workspace) + ws,
-                     workspace_bytes - ws);
-        return run_gemm(a, static_cast<hipStream_t>(stream));
+    return gemm_impl(d, index, values, meta, M, X, ldx, nullptr, 0, Y, ldy, y_dtype, workspace, workspace_bytes,
+                     stream);
+}
+
+hts_status hts_gemm_silu_mul(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta,
+                             int64_t M, const void* X, int64_t ldx, const void* G, int64_t ldg, void* Y, int64_t ldy,
+                             int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (M > 0) {
+        if (!G) return fail(HTS_ERR_INVALID_ARG, "G is NULL");
+        hts_status st = check_ld(ldg, d ? d->N : 0, 4, "ldg");
+        if (st) return st;
     }
-    if (workspace && !aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
-    hts::GemmArgs a{};
-    a.dtype = d->dtype;
-    a.y_dtype = y_dtype;
-    a.M = M;
-    a.N = d->N;
-    a.K = d->K;
-    a.bn = d->bn;
-    a.bk = d->bk;
-    a.index = index;
-    a.values = static_cast<const uint16_t*>(values);
-    a.meta = meta;
-    a.X = static_cast<const uint16_t*>(X);
-    a.ldx = ldx;
-    a.Y = Y;
-    a.ldy = ldy;
-    attach_split(a, prefill_split(M, d->N, d->K, d->dtype, d->bk, d->bn == 64 ? 64 : 128), workspace, workspace_bytes);
-    return run_gemm(a, static_cast<hipStream_t>(stream));
+    return gemm_impl(d, index, values, meta, M, X, ldx, G, ldg, Y, ldy, y_dtype, workspace, workspace_bytes, stream);
 }
 
 hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, const void* W,

@@ -28,6 +28,9 @@ struct GemmArgs {
     // write fp32 partial products to part[nsplit][M][N]; a reduction then writes Y
     float* part;
     int32_t nsplit;
+    // gated output (hts_gemm_silu_mul): Y = silu(G) * (X . W^T), G[M,N] (ldg) in y_dtype, or nullptr
+    const void* gate;
+    int64_t ldg;
 };
 
 enum SparsePath { SPARSE_SMFMAC = 0, SPARSE_DECOMPRESS = 1 };

@@ -154,7 +154,7 @@ hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* valu
                       const uint32_t* meta, void* W_out, int64_t ldw, void* stream);
 
 /* Host only.  Bytes of device workspace for the fastest hts_gemm path at this shape and M
- * (0 in the streaming range: M <= 32 for 16-bit data on 128-wide tiles, else M <= 16; the
+ * (0 in the streaming range: M <= 32 on 128-wide tiles, else M <= 16; the
  * environment variable HTS_DECODE_MAX_M lowers it).  Two uses, in this order within the workspace:
  *  - tiles of 32 rows or 32 columns above the streaming range: the product unpacks the weight into the
  *    workspace (N*K elements, row-major, 256-byte rounded) and runs the same-library dense

@@ -245,7 +245,8 @@ def test_split_product_workspace_sizes(monkeypatch):
         assert hts.hts_gemm_workspace(d, M) == (_r256(ns * M * N * 4) if ns else 0), M
         assert hts.hts_dense_gemm_workspace("bf16", M, N, K) == (_r256(ns * M * N * 4) if ns else 0), M
     # 8-bit: 128-wide slices (32 per tile row here); 64x64 tiles: 64-row blocks
-    assert hts.hts_gemm_workspace(hts.make_desc(N, K, 128, 128, "fp8"), 17) == _r256(5 * 17 * N * 4)
+    assert hts.hts_gemm_workspace(hts.make_desc(N, K, 128, 128, "fp8"), 17) == 0     # streams at M <= 32
+    assert hts.hts_gemm_workspace(hts.make_desc(N, K, 128, 128, "fp8"), 33) == _r256(5 * 33 * N * 4)
     assert hts.hts_gemm_workspace(hts.make_desc(4096, 4096, 64, 64, "bf16"), 17) == _r256(8 * 17 * 4096 * 4)
     # few slices: K = 256 has 4 (bf16), too few to split
     assert hts.hts_gemm_workspace(hts.make_desc(1024, 256, 128, 128, "bf16"), 64) == 0

@@ -141,17 +141,18 @@ def test_fp8_strided_x_and_y():
                                  {"HTS_DECODE_PP": "2", "HTS_DECODE_KSPLIT": "4"},
                                  {"HTS_DECODE_XT_MIN_M": "17"},
                                  {"HTS_DECODE_NT": "4", "HTS_DECODE_PP": "2", "HTS_DECODE_XT_MIN_M": "1"}])
-def test_fp8_streaming_launch_shapes(env, monkeypatch):
+@pytest.mark.parametrize("M", [16, 32])
+def test_fp8_streaming_launch_shapes(env, M, monkeypatch):
     # every launch shape of the 8-bit streaming kernel, X loaded in the operand layout or as whole
-    # rows through LDS, on the 7B-shaped layer (M = 16)
+    # rows through LDS, on the 7B-shaped layer; M = 32: two groups of 16 X rows per weight fragment
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     c = wl.config("7b_up_fp8")
     L = c.layers[0]
-    say(f"[fp8-shapes] {env}")
+    say(f"[fp8-shapes] {env} M={M}")
     vals, meta, idx, Wm = oracle_packed(c.cfg_id, L.name)
     pw = hts.pack(_t(weight(c.cfg_id, L.name)), oracle_map(c.cfg_id, L.name), 128, 128)
-    X = activations(c.cfg_id, L.name)[:16]
+    X = activations(c.cfg_id, L.name)[:M]
     Y = hts.gemm(_t(np.ascontiguousarray(X)), pw, out_dtype=torch.float32)
     torch.cuda.synchronize()
     _check(Y.cpu().numpy(), oracle.gemm_ref(X, Wm, "fp8"), f"{env}")

@@ -1,4 +1,4 @@
-// Hybrid tile-sparse product for small M (M <= 16; M <= 32 for 16-bit data on 128-wide tiles,
+// Hybrid tile-sparse product for small M (M <= 16; M <= 32 on 128-wide tiles,
 // where each weight fragment feeds two groups of 16 X rows): the HBM-streaming path.
 //
 // At decode-sized M the weight bytes are almost all of the traffic, so every
@@ -323,15 +323,15 @@ hipError_t launch2(const GemmArgs& a, int ksplit, int nt, int pp, int sp, hipStr
 //   2:4 tile  : stored bytes [16g, 16g+16) of the 64-byte tile row (dense k in [32g, 32g+32))
 //               and code word g of the row's four words -- exactly the sparse instruction's A
 //               operand and index; X as for a dense tile.
-template <int PP>
+template <int PP, int MG = 1>
 struct TileRegs8 {
     u32x4 a[PP][2];   // per panel: dense: the two chunks; 2:4: a[q][0] = 16 stored bytes
     uint32_t m[PP];   // per panel: 2:4 code word
-    u32x4 x[2];       // X chunks, shared by the PP panels
+    u32x4 x[MG][2];   // X chunks of MG groups of 16 rows, shared by the PP panels
 };
 
-template <bool HYB, int PP, bool XT>
-__device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs& a, const hts_tile& e, int tk,
+template <bool HYB, int PP, bool XT, int MG>
+__device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP, MG>& R, const GemmArgs& a, const hts_tile& e, int tk,
                                                int64_t n0, int r0, int lane, const uint8_t* xrow) {
     const int i = lane & 15, g = lane >> 4;
     uint32_t type = HTS_TILE_DENSE;
@@ -365,16 +365,19 @@ __device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP>& R, const GemmArgs&
         for (int q = 0; q < PP; ++q) R.m[q] = mrow[64 * q + g];
     }
     if constexpr (XT) {
-        // whole X rows: instruction v reads rows 8v .. 8v+7 of the 128-byte tile column
+        // whole X rows: instruction v of group h reads rows 16h + 8v .. +7 of the 128-byte tile column
         const uint8_t* X8 = reinterpret_cast<const uint8_t*>(a.X);
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            const int64_t row = 8 * v + (lane >> 3);
-            R.x[v] = ld16(X8 + (row < a.M ? row : a.M - 1) * a.ldx + (int64_t)tk * 128 + 16 * (lane & 7));
-        }
+        for (int h = 0; h < MG; ++h)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int64_t row = 16 * h + 8 * v + (lane >> 3);
+                R.x[h][v] = ld16(X8 + (row < a.M ? row : a.M - 1) * a.ldx + (int64_t)tk * 128 + 16 * (lane & 7));
+            }
     } else {
-        R.x[0] = ld16(xrow + (int64_t)tk * 128 + 16 * g);
-        R.x[1] = ld16(xrow + (int64_t)tk * 128 + 64 + 16 * g);
+        static_assert(MG == 1, "two X row groups are loaded as whole rows");
+        R.x[0][0] = ld16(xrow + (int64_t)tk * 128 + 16 * g);
+        R.x[0][1] = ld16(xrow + (int64_t)tk * 128 + 64 + 16 * g);
     }
     return type;
 }
@@ -396,22 +399,27 @@ __device__ __forceinline__ void x_fragments8(u32x4 (&x)[2], uint8_t* buf, int la
     }
 }
 
-template <int PP>
-__device__ __forceinline__ void mma_tile8(const TileRegs8<PP>& R, uint32_t type, f32x4 (&acc)[PP]) {
-    const u32x8 xb = cat8(R.x[0], R.x[1]);
+template <int PP, int MG>
+__device__ __forceinline__ void mma_tile8(const TileRegs8<PP, MG>& R, uint32_t type, f32x4 (&acc)[MG][PP]) {
     if (type == HTS_TILE_DENSE) {
 #pragma unroll
-        for (int q = 0; q < PP; ++q) {
-            acc[q] = mfma_dense<FP8T>(R.a[q][0], R.x[0], acc[q]);
-            acc[q] = mfma_dense<FP8T>(R.a[q][1], R.x[1], acc[q]);
-        }
+        for (int h = 0; h < MG; ++h)
+#pragma unroll
+            for (int q = 0; q < PP; ++q) {
+                acc[h][q] = mfma_dense<FP8T>(R.a[q][0], R.x[h][0], acc[h][q]);
+                acc[h][q] = mfma_dense<FP8T>(R.a[q][1], R.x[h][1], acc[h][q]);
+            }
     } else {
 #pragma unroll
-        for (int q = 0; q < PP; ++q) acc[q] = mfma_fp8_sparse(R.a[q][0], xb, R.m[q], acc[q]);
+        for (int h = 0; h < MG; ++h) {
+            const u32x8 xb = cat8(R.x[h][0], R.x[h][1]);
+#pragma unroll
+            for (int q = 0; q < PP; ++q) acc[h][q] = mfma_fp8_sparse(R.a[q][0], xb, R.m[q], acc[h][q]);
+        }
     }
 }
 
-template <bool HYB, int KS, int NT, int PP, bool XT>
+template <bool HYB, int KS, int NT, int PP, bool XT, int MG = 1>
 __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -426,46 +434,63 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a)
     const int i = lane & 15;
     const int64_t j = i < a.M ? i : a.M - 1;
     const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.X) + j * a.ldx;
-    __shared__ __attribute__((aligned(16))) uint8_t xbuf[XT ? KS : 1][XT ? 16 * 128 : 16];   // XT: per-wave X staging
-    f32x4 acc[PP];
+    // per-wave LDS: X staging (XT: 2 KB per group of 16 rows), then the wave's partial sums
+    constexpr int XB = XT ? MG * 16 * 128 : 0, RB = MG * PP * 64 * 16, WB = XB > RB ? XB : RB;
+    __shared__ __attribute__((aligned(16))) uint8_t wbuf[KS][WB];
+    f32x4 acc[MG][PP];
 #pragma unroll
-    for (int q2 = 0; q2 < PP; ++q2) acc[q2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < MG; ++h)
+#pragma unroll
+        for (int q2 = 0; q2 < PP; ++q2) acc[h][q2] = f32x4{0.f, 0.f, 0.f, 0.f};
     hts_tile E[NT] = {};
     if (HYB && kb < ke) load_entries<NT>(E, a, t0, kb, ke);
     for (int t = kb; t < ke; t += NT) {
-        TileRegs8<PP> R[NT];
+        TileRegs8<PP, MG> R[NT];
         uint32_t type[NT];
 #pragma unroll
         for (int s = 0; s < NT; ++s)
-            if (t + s < ke) type[s] = load_tile8<HYB, PP, XT>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
+            if (t + s < ke) type[s] = load_tile8<HYB, PP, XT, MG>(R[s], a, E[s], t + s, n0, r0, lane, xrow);
         if (HYB && t + NT < ke) load_entries<NT>(E, a, t0, t + NT, ke);
 #pragma unroll
         for (int s = 0; s < NT; ++s)
             if (t + s < ke) {
-                if constexpr (XT) x_fragments8(R[s].x, xbuf[wave], lane);
-                mma_tile8<PP>(R[s], type[s], acc);
+                if constexpr (XT)
+#pragma unroll
+                    for (int h = 0; h < MG; ++h) x_fragments8(R[s].x[h], wbuf[wave] + h * 16 * 128, lane);
+                mma_tile8<PP, MG>(R[s], type[s], acc);
             }
     }
 
-    __shared__ f32x4 red[KS][PP][64];
+    // partial sums through the wave's own LDS (its X staging is done), added in wave order
+    f32x4* red = reinterpret_cast<f32x4*>(wbuf[wave]);
 #pragma unroll
-    for (int q2 = 0; q2 < PP; ++q2) red[wave][q2][lane] = acc[q2];
+    for (int h = 0; h < MG; ++h)
+#pragma unroll
+        for (int q2 = 0; q2 < PP; ++q2) red[(h * PP + q2) * 64 + lane] = acc[h][q2];
     __syncthreads();
-    for (int o = threadIdx.x; o < 256 * PP; o += 64 * KS) {
-        const int q2 = o >> 8, m = (o >> 4) & 15, rr = o & 15;
+    for (int o = threadIdx.x; o < 256 * PP * MG; o += 64 * KS) {
+        const int h = o / (256 * PP), q2 = (o >> 8) % PP, m = (o >> 4) & 15, rr = o & 15;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < KS; ++w) sum += red[w][q2][m + 16 * (rr >> 2)][rr & 3];
-        if (m < a.M) {
+        for (int w = 0; w < KS; ++w)
+            sum += reinterpret_cast<const f32x4*>(wbuf[w])[(h * PP + q2) * 64 + m + 16 * (rr >> 2)][rr & 3];
+        const int64_t row = 16 * h + m;
+        if (row < a.M) {
             const int64_t n = n0 + 16 * q2 + rr;
-            if (a.gate) sum = silu_times(gate_value(a.gate, (int64_t)m * a.ldg + n, a.y_dtype), sum);
-            store_y1(a.Y, (int64_t)m * a.ldy + n, a.y_dtype, sum);
+            if (a.gate) sum = silu_times(gate_value(a.gate, row * a.ldg + n, a.y_dtype), sum);
+            store_y1(a.Y, row * a.ldy + n, a.y_dtype, sum);
         }
     }
 }
 
 template <bool HYB, int KS, int NT, int PP>
 void launch8x(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    if constexpr (NT <= 4 && KS <= 8) {
+        if (a.M > 16) {             // two groups of 16 X rows per weight fragment (M <= 32)
+            gemm_decode8_kernel<HYB, KS, NT, PP, true, 2><<<grid, block, 0, s>>>(a);
+            return;
+        }
+    }
     if (a.M >= decode_xt_min_m()) gemm_decode8_kernel<HYB, KS, NT, PP, true><<<grid, block, 0, s>>>(a);
     else gemm_decode8_kernel<HYB, KS, NT, PP, false><<<grid, block, 0, s>>>(a);
 }
@@ -475,7 +500,7 @@ hipError_t launch8_nt(const GemmArgs& a, int nt, hipStream_t s) {
     const dim3 grid((unsigned)(a.N / (16 * PP))), block(64 * KS);
     // nt counts 16-bit 128x128 tile columns; an 8-bit tile column is half the bytes
     if constexpr (KS < 16 && PP == 1) {
-        if (nt >= 4) {
+        if (nt >= 4 && a.M <= 16) {
             launch8x<HYB, KS, 8, PP>(a, grid, block, s);
             return hipGetLastError();
         }
@@ -490,7 +515,7 @@ hipError_t launch8(const GemmArgs& a, int ksplit, int nt, int pp, hipStream_t s)
         if (ksplit >= 8) return launch8_nt<HYB, 8, 2>(a, nt, s);
         return launch8_nt<HYB, 4, 2>(a, nt, s);
     }
-    if (ksplit >= 16) return launch8_nt<HYB, 16, 1>(a, nt, s);
+    if (ksplit >= 16 && a.M <= 16) return launch8_nt<HYB, 16, 1>(a, nt, s);
     if (ksplit >= 8) return launch8_nt<HYB, 8, 1>(a, nt, s);
     return launch8_nt<HYB, 4, 1>(a, nt, s);
 }
@@ -624,8 +649,8 @@ hipError_t launch32(const GemmArgs& a, int ksplit, int pp, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s) {
-    // M = 17 .. 32 runs two groups of X rows per weight fragment: 16-bit data, 128-wide tiles
-    if (a.M < 1 || a.M > 32 || (a.M > 16 && (a.dtype == HTS_FP8_E4M3 || a.bk != 128))) return hipErrorInvalidValue;
+    // M = 17 .. 32 runs two groups of X rows per weight fragment: 128-wide tiles
+    if (a.M < 1 || a.M > 32 || (a.M > 16 && a.bk != 128)) return hipErrorInvalidValue;
     if (a.dtype == HTS_FP8_E4M3)   // 8-bit: the sparse instruction only (no expansion fallback)
         return a.index ? launch8<true>(a, ksplit, nt, pp, s) : launch8<false>(a, ksplit, nt, pp, s);
     if (a.bk == 32) {              // 32-wide tiles: expansion in registers

@@ -77,10 +77,11 @@ int sparse_path() {
     return hts::SPARSE_SMFMAC;
 }
 
-// Largest M served by the streaming kernel: 32 for 16-bit data on 128-wide tiles (two groups of
-// 16 X rows per weight fragment), else 16.  HTS_DECODE_MAX_M (0..32) lowers it.
+// Largest M served by the streaming kernel: 32 on 128-wide tiles (two groups of 16 X rows per
+// weight fragment), else 16.  HTS_DECODE_MAX_M (0..32) lowers it.
 int64_t streaming_max_m(int32_t dtype, int bk) {
-    const int64_t lim = (dtype != HTS_FP8_E4M3 && bk == 128) ? 32 : 16;
+    (void)dtype;
+    const int64_t lim = bk == 128 ? 32 : 16;
     const char* v = getenv("HTS_DECODE_MAX_M");
     if (v && *v) {
         long x = strtol(v, nullptr, 10);

@@ -149,7 +149,11 @@ hts_status hts_pack_masked(const hts_desc* d, const hts_tile* index, const void*
                            uint32_t* malformed_groups, void* stream);
 
 /* Device, asynchronous.  Inverse of hts_pack: writes mask(W) into W_out[N,K]
- * (ldw), +0.0 at the dropped positions of 2:4 tiles. */
+ * (ldw), +0.0 at the dropped positions of 2:4 tiles -- the masked weight the hybrid layer
+ * computes with (page "PATCH: Learnable Tile-level Hybrid Sparsity for LLMs", section 2, core
+ * mechanism: dense tiles keep every weight, 2:4 tiles zero two of every four along K).
+ * values / meta: as written by hts_pack under `index`; W_out: device, 16-byte aligned, ldw >= K
+ * and a multiple of 8 (16 for HTS_FP8_E4M3).  Errors as hts_pack's. */
 hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* values,
                       const uint32_t* meta, void* W_out, int64_t ldw, void* stream);
 
@@ -168,8 +172,10 @@ hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* valu
  *    product runs unsplit, with the same result up to fp32 rounding order. */
 hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes);
 
-/* Device, asynchronous.  Y[M,N] = X[M,K] . mask(W)^T from the packed weight,
- * fp32 accumulation, Y written as y_dtype (HTS_F32, HTS_F16 or HTS_BF16; 16-bit
+/* Device, asynchronous.  The hybrid linear layer (page "PATCH: Learnable Tile-level Hybrid Sparsity
+ * for LLMs", section 2, core mechanism and inference/deployment: per-tile dense or 2:4 weights,
+ * dense tiles on the dense matrix cores and 2:4 tiles on the sparse ones, from compressed storage):
+ * Y[M,N] = X[M,K] . mask(W)^T from the packed weight, fp32 accumulation, Y written as y_dtype (HTS_F32, HTS_F16 or HTS_BF16; 16-bit
  * outputs rounded to nearest even).  In the streaming range (see hts_gemm_workspace) one
  * kernel streams the weight from HBM once; above it a tiled kernel stages weight and X
  * slices through LDS.  Dense tiles use dense MFMA, 2:4 tiles
@@ -187,7 +193,10 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
 
 /* Device, asynchronous.  The same-library dense product Y = X . W^T on a
  * row-major W[N,K] (ldw) with the same kernels and no tile index: the
- * reference point for speedups.  N and K multiples of 64.  workspace: optional, as the
+ * reference point for speedups (the dense model the PATCH page measures its speed-up against,
+ * section 4, results).  X, W, Y: device, 16-byte aligned; ldx, ldw >= K and ldy >= N, leading
+ * dimensions multiples of 8 (16 for HTS_FP8_E4M3) and 4; y_dtype HTS_F32, HTS_F16 or HTS_BF16.
+ * M == 0 is a no-op; errors as hts_gemm's.  N and K multiples of 64.  workspace: optional, as the
  * split-product part of hts_gemm's (size from hts_dense_gemm_workspace). */
 hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K,
                           const void* X, int64_t ldx, const void* W, int64_t ldw,

@@ -72,9 +72,10 @@ def activations(cfg_id: int, layer_name: str):
     return wl.activation_bits(c, L, max(c.Ms))
 
 
-def sample_rows(M: int, k: int = 48, seed: int = 0):
-    if M <= k:
-        return np.arange(M)
-    g = np.random.default_rng(seed + M)
-    r = np.unique(np.concatenate([[0, M - 1], g.choice(M, size=k - 2, replace=False)]))
-    return r
+@functools.lru_cache(maxsize=2)
+def layer_ref(cfg_id: int, layer_name: str, M: int) -> np.ndarray:
+    """Oracle Y = X[:M] . mask(W)^T (fp64) of a named layer, every row and column."""
+    c = wl.config(cfg_id)
+    L = next(x for x in c.layers if x.name == layer_name)
+    Wm = oracle_packed(cfg_id, layer_name)[3]
+    return oracle.gemm_ref(np.ascontiguousarray(activations(cfg_id, layer_name)[:M]), Wm, L.dtype)

@@ -11,7 +11,7 @@ import oracle
 import tile_gemm_amd as hts
 import tile_gemm_amd.block as block
 import workloads as wl
-from helpers import DEV, activations, oracle_map, say, sample_rows, weight
+from helpers import DEV, activations, oracle_map, say, weight
 
 pytestmark = pytest.mark.gpu
 TOL = 5e-3
@@ -55,8 +55,9 @@ def _masked(c, name):
 
 @pytest.mark.parametrize("hybrid", [True, False])
 def test_block_step_parity(hybrid):
+    # the block at its workload's M = 2048, every element of every output
     c = wl.config("7b_block")
-    M = 300
+    M = 2048
     say(f"[block] hybrid={hybrid} M={M}")
     W = _weights(c, M, hybrid)
     X = activations(c.cfg_id, "q")[:M]
@@ -64,7 +65,7 @@ def test_block_step_parity(hybrid):
     bufs = block.buffers(M, W, Xt.dtype, DEV)
     block.forward(Xt, W, bufs)
     torch.cuda.synchronize()
-    rows = sample_rows(M)
+    rows = np.arange(M)
     bits = {k: hts.bits_from_tensor(v) for k, v in bufs.items()}
     weights_m = {L.name: (_masked(c, L.name) if hybrid else weight(c.cfg_id, L.name)) for L in c.layers}
     inputs = {"q": X, "k": X, "v": X, "gate": X, "up": X, "o": bits["q"], "down": bits["h"]}
@@ -82,7 +83,7 @@ def test_block_step_fused_gate_parity():
     # the up product writes silu(gate) * up in its output stage: h against the oracle's gated step
     # on the unrounded up product, and the down projection against h
     c = wl.config("7b_block")
-    M = 300
+    M = 2048
     say(f"[block-fused] M={M}")
     W = _weights(c, M, True)
     X = activations(c.cfg_id, "q")[:M]
@@ -90,7 +91,7 @@ def test_block_step_fused_gate_parity():
     bufs = block.buffers(M, W, Xt.dtype, DEV)
     block.forward(Xt, W, bufs, fused=True)
     torch.cuda.synchronize()
-    rows = sample_rows(M)
+    rows = np.arange(M)
     bits = {k: hts.bits_from_tensor(v) for k, v in bufs.items()}
     up_ref = oracle.gemm_ref(X[rows], _masked(c, "up"), "bf16")
     h_ref = oracle.gated_ref(bits["gate"][rows], up_ref, "bf16")

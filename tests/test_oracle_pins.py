@@ -453,12 +453,15 @@ def test_pack_from_well_formed_mask_brute_force(dtype):
     vals, meta, index, bad = oracle.pack_masked(W, dtype, tmap, mask, bn, bk)
     assert bad == 0
     back = oracle.unpack(vals, meta, index, N, K, bn, bk)
+    # the expected value of the GPU masked unpack and of the product over a mask-packed weight
+    Wm = oracle.masked_weights_from_mask(W, tmap, mask, bn, bk)
     Tk = K // bk
     for n in range(N):
         for k in range(K):
             sparse = tmap[(n // bn) * Tk + k // bk] == 1
             want = W[n, k] if (not sparse or mask[n, k]) else 0
             assert back[n, k] == want
+            assert Wm[n, k] == want
     # codes name the marked positions (found here group by group with np.nonzero)
     for t in np.nonzero(tmap)[0]:
         vo, mo, _, _ = index[t]
@@ -470,23 +473,55 @@ def test_pack_from_well_formed_mask_brute_force(dtype):
                 assert (word >> (4 * (gi % 8))) & 0xF == int(pos[0]) | (int(pos[1]) << 2)
 
 
-def test_pack_from_malformed_mask_brute_force():
-    g = np.random.default_rng(43)
+def _malformed_case(seed=43):
+    """A 2:4 layer whose mask marks any number of weights per group, with marked entries of
+    arbitrary nonzero value (nonzero = keep), and the pair each group must keep."""
+    g = np.random.default_rng(seed)
     N, K, bn, bk = 4, 64, 4, 32
     W = wl.gaussian_bits((N, K), 0.02, "bf16", g)
-    mask = (g.random((N, K)) < 0.5).astype(np.uint8)       # any number marked per group
+    marked = g.random((N, K)) < 0.5                  # any number marked per group
+    mask = np.where(marked, g.integers(1, 256, size=(N, K)), 0).astype(np.uint8)
     tmap = np.array([1, 1], np.uint8)
-    vals, meta, index, bad = oracle.pack_masked(W, "bf16", tmap, mask, bn, bk)
-    groups = mask.reshape(N, K // 4, 4)
-    assert bad == int(np.count_nonzero(groups.sum(axis=-1) != 2))
-    back = oracle.unpack(vals, meta, index, N, K, bn, bk).reshape(N, K // 4, 4)
+    want = np.zeros((N, K // 4, 4), np.uint16)
+    groups = marked.reshape(N, K // 4, 4)
     for n in range(N):
         for gi in range(K // 4):
             order = [i for i in range(4) if groups[n, gi, i]] + [i for i in range(4) if not groups[n, gi, i]]
             kept = sorted(order[:2])              # marked first, lower index first among equals
-            want = np.zeros(4, np.uint16)
-            want[kept] = W[n, 4 * gi + np.array(kept)]
-            assert np.array_equal(back[n, gi], want)
+            want[n, gi, kept] = W[n, 4 * gi + np.array(kept)]
+    return W, mask, tmap, (N, K, bn, bk), groups, want.reshape(N, K)
+
+
+def test_pack_from_malformed_mask_brute_force():
+    W, mask, tmap, (N, K, bn, bk), groups, want = _malformed_case()
+    vals, meta, index, bad = oracle.pack_masked(W, "bf16", tmap, mask, bn, bk)
+    assert bad == int(np.count_nonzero(groups.sum(axis=-1) != 2))
+    assert np.array_equal(oracle.unpack(vals, meta, index, N, K, bn, bk), want)
+    assert np.array_equal(oracle.masked_weights_from_mask(W, tmap, mask, bn, bk), want)
+
+
+def test_planted_mask_mistakes_are_caught(monkeypatch):
+    # masked_weights_from_mask must fail the brute-force pin when its selection is wrong
+    W, mask, tmap, (N, K, bn, bk), _, want = _malformed_case()
+
+    def pin_ok():
+        return np.array_equal(oracle.masked_weights_from_mask(W, tmap, mask, bn, bk), want)
+
+    assert pin_ok()
+    real = oracle.hybrid.mask_scores
+    # (1) the mask's raw byte values used as the score instead of marked / unmarked
+    monkeypatch.setattr(oracle.hybrid, "mask_scores", lambda m: np.asarray(m).astype(np.float32))
+    assert not pin_ok()
+    # (2) marked and unmarked swapped (the mask read as a drop mask)
+    monkeypatch.setattr(oracle.hybrid, "mask_scores", lambda m: (np.asarray(m) == 0).astype(np.float32))
+    assert not pin_ok()
+    monkeypatch.setattr(oracle.hybrid, "mask_scores", real)
+    # (3) ties among marked weights to the higher index
+    real_keep = oracle.hybrid.keep_two_of_four
+    monkeypatch.setattr(oracle.hybrid, "keep_two_of_four", lambda s: real_keep(np.asarray(s)[..., ::-1])[..., ::-1])
+    assert not pin_ok()
+    monkeypatch.setattr(oracle.hybrid, "keep_two_of_four", real_keep)
+    assert pin_ok()
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -42,6 +42,16 @@ __device__ __forceinline__ u32x4 ldw16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Lanes of one wave exchange data through that wave's own LDS (X staging, partial sums).  The LDS
+// operations of a wave execute in issue order, so no wait is needed between a write and a read of
+// another lane's slot; this keeps the compiler from moving LDS accesses across the exchange
+// (release and acquire fences at wavefront scope around a wave barrier emit no instructions).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int BK, int PP, int MG = 1>
 struct TileRegs {
     u32x4 a[PP][BK / 32];      // per panel: dense: BK/32 chunks; 2:4: BK/64 chunks
@@ -109,15 +119,17 @@ __device__ __forceinline__ uint32_t load_tile(TileRegs<BK, PP, MG>& R, const Gem
 // X chunks loaded as whole rows (lane L: row 4v + L/16, chunk L%16 of register v) into the operand
 // layout (lane i + 16g, substep u: row i, chunk koff(u, g) / 8) through the wave's own 4 KB of LDS:
 // row r at r * 256 bytes, chunk c in slot c ^ r, so the 16 rows a read instruction serves fall in
-// distinct banks.  LDS operations of one wave complete in order, so the next tile's writes cannot
-// overtake this tile's reads.
+// distinct banks.  Fences before the writes (the previous tile's reads of the buffer) and between
+// the writes and the reads.
 template <int SP>
 __device__ __forceinline__ void x_fragments(u32x4 (&x)[4], uint8_t* buf, int lane) {
+    wave_lds_fence();
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int row = 4 * v + (lane >> 4), ch = lane & 15;
         *reinterpret_cast<u32x4*>(buf + row * 256 + 16 * (ch ^ row)) = x[v];
     }
+    wave_lds_fence();
     const int i = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -213,8 +225,9 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode_kernel(const GemmArgs a) 
             }
     }
 
-    // the partial sums go to the wave's own LDS (its X staging is done: one wave's LDS operations
-    // complete in order), then the KS partials of each output are added in wave order
+    // the partial sums go to the wave's own LDS (after its last X staging reads), then the KS
+    // partials of each output are added in wave order
+    wave_lds_fence();
     f32x4* red = reinterpret_cast<f32x4*>(wbuf[wave]);
 #pragma unroll
     for (int h = 0; h < MG; ++h)
@@ -386,11 +399,13 @@ __device__ __forceinline__ uint32_t load_tile8(TileRegs8<PP, MG>& R, const GemmA
 // chunks g and 4 + g of row i) through the wave's 2 KB of LDS: row r at r * 128 bytes, chunk c in
 // slot c ^ ((r >> 1) & 7), so the 16 rows a read serves fall in distinct banks.
 __device__ __forceinline__ void x_fragments8(u32x4 (&x)[2], uint8_t* buf, int lane) {
+    wave_lds_fence();
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
         const int row = 8 * v + (lane >> 3), ch = lane & 7;
         *reinterpret_cast<u32x4*>(buf + row * 128 + 16 * (ch ^ ((row >> 1) & 7))) = x[v];
     }
+    wave_lds_fence();
     const int i = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -461,7 +476,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_decode8_kernel(const GemmArgs a)
             }
     }
 
-    // partial sums through the wave's own LDS (its X staging is done), added in wave order
+    // partial sums through the wave's own LDS (after its last X staging reads), added in wave order
+    wave_lds_fence();
     f32x4* red = reinterpret_cast<f32x4*>(wbuf[wave]);
 #pragma unroll
     for (int h = 0; h < MG; ++h)

@@ -595,17 +595,17 @@ template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int 
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     using Lo = Layout<BN, BM, NSTAGE, meta_group_bytes<Elem<T>::bytes>()>;
     auto kern = gemm_prefill_kernel<T, BK, HYB, SP, BN, BM, NSTAGE, NW>;
-    static bool attr_set = false;   // per instantiation; raising the dynamic-LDS limit is idempotent
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Lo::TOTAL);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // one flag set per instantiation (this static) and device
+    static DeviceOnce lds_limit;
+    hipError_t e = lds_limit.run([&] {
+        return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Lo::TOTAL);
+    });
+    if (e != hipSuccess) return e;
     const int NB = (int)((a.N + BN - 1) / BN), MB = (int)((a.M + BM - 1) / BM);
     const int nsplit = a.nsplit > 1 ? a.nsplit : 1;
     kern<<<dim3((unsigned)(NB * MB), (unsigned)nsplit), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order(),
                                                                                    prefill_chunk_log2(BK));
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;
     const int64_t quads = a.M * (a.N / 4);
     split_sum_kernel<<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s>>>(a.part, nsplit, a.gate, a.ldg, a.M, a.N, a.Y,

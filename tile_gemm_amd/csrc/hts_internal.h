@@ -4,9 +4,36 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "hts.h"
 
 namespace hts {
+
+// A host-side action done once per device (e.g. raising a kernel's dynamic-LDS limit, which
+// applies to the current device): thread-safe, retried on a later call if it failed.
+class DeviceOnce {
+  public:
+    static constexpr int kMaxDevices = 64;
+    template <typename F>
+    hipError_t run(F&& f) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        if (done_[dev].load(std::memory_order_acquire)) return hipSuccess;
+        std::lock_guard<std::mutex> lock(mu_);
+        if (done_[dev].load(std::memory_order_relaxed)) return hipSuccess;
+        e = f();
+        if (e == hipSuccess) done_[dev].store(true, std::memory_order_release);
+        return e;
+    }
+
+  private:
+    std::mutex mu_;
+    std::atomic<bool> done_[kMaxDevices] = {};
+};
 
 // Everything a product kernel needs, by value.  Exactly one weight source is
 // used: the packed hybrid weight (index/values/meta) or a row-major W (W/ldw).

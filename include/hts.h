@@ -207,6 +207,20 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K,
  * product would be split, see hts_gemm_workspace). */
 hts_status hts_dense_gemm_workspace(int32_t dtype, int64_t M, int64_t N, int64_t K, size_t* bytes);
 
+/* Device, asynchronous.  hts_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  This call allocates nothing: the workspace hts_gemm would take (the fp32 parts of a
+ * split product, the unpacked weight of 32-wide tiles) is a library-owned static device array of
+ * 64 MiB per GPU, held from the first use on that GPU until the process ends.  The result equals
+ * hts_gemm's with a workspace of hts_gemm_workspace() bytes, bit for bit.  A shape and M whose
+ * hts_gemm_workspace() exceeds 64 MiB are rejected with HTS_ERR_WORKSPACE.  Every call on one GPU
+ * uses the same array: calls that overlap on one GPU (different streams, threads or graphs
+ * running concurrently) race and must be serialized by the caller.  Other arguments and errors as
+ * hts_gemm's; HTS_ERR_HIP if the array's device address cannot be obtained. */
+hts_status hts_gemm_noalloc(const hts_desc* d, const hts_tile* index, const void* values,
+                            const uint32_t* meta, int64_t M, const void* X, int64_t ldx,
+                            void* Y, int64_t ldy, int32_t y_dtype, void* stream);
+
 /* Device, asynchronous.  The hybrid product with the gated-MLP step in its output stage:
  * Y[M,N] = silu(G) * (X[M,K] . mask(W)^T), silu(x) = x / (1 + e^-x), with G[M,N] (ldg) in
  * y_dtype.  The up projection of a decoder block whose linear layers are hybrid tile-sparse

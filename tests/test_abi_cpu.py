@@ -261,3 +261,14 @@ def test_split_product_workspace_sizes(monkeypatch):
     # override: a forced count
     monkeypatch.setenv("HTS_PREFILL_SPLIT", "3")
     assert hts.hts_gemm_workspace(d, 300) == _r256(3 * 300 * N * 4)
+
+
+def test_noalloc_rejects_before_any_device_call():
+    # the scratch maximum (64 MiB) and the argument checks come before any HIP call
+    desc = hts.make_desc(11008, 4096, 32, 32, "bf16")
+    L = hts.lib()
+    st = L.hts_gemm_noalloc(ctypes.byref(desc), 16, 16, 16, 64, 16, 4096, 16, 11008, hts.HTS_F32, None)
+    assert st == 6 and b"64" in L.hts_last_error()
+    st = L.hts_gemm_noalloc(ctypes.byref(desc), 16, 16, 16, -1, 16, 4096, 16, 11008, hts.HTS_F32, None)
+    assert st == 3
+    assert L.hts_gemm_noalloc(None, 16, 16, 16, 1, 16, 4096, 16, 11008, hts.HTS_F32, None) == 1

@@ -60,6 +60,8 @@ _SIGS = {
     "hts_gemm_workspace": (ctypes.c_int, [ctypes.POINTER(hts_desc), _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "hts_gemm": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _I32,
                                 _VP, ctypes.c_size_t, _VP]),
+    "hts_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _I32,
+                                        _VP]),
     "hts_gemm_silu_mul": (ctypes.c_int, [ctypes.POINTER(hts_desc), _VP, _VP, _VP, _I64, _VP, _I64, _VP, _I64, _VP,
                                          _I64, _I32, _VP, ctypes.c_size_t, _VP]),
     "hts_dense_gemm": (ctypes.c_int, [_I32, _I64, _I64, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _I32, _VP,
@@ -181,6 +183,13 @@ def hts_gemm(desc, index, values, meta, X, Y, y_dtype=None, workspace=None, stre
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hts_gemm(ctypes.byref(desc), _ptr(index), _ptr(values), _ptr(meta), M, _ptr(X), X.stride(0),
                           _ptr(Y), Y.stride(0), yd, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hts_gemm_noalloc(desc, index, values, meta, X, Y, y_dtype=None, stream=None, M=None) -> None:
+    M = X.shape[0] if M is None else M
+    yd = _dt(Y.dtype) if y_dtype is None else y_dtype
+    _check(lib().hts_gemm_noalloc(ctypes.byref(desc), _ptr(index), _ptr(values), _ptr(meta), M, _ptr(X), X.stride(0),
+                                  _ptr(Y), Y.stride(0), yd, _stream(stream)))
 
 
 def hts_gemm_silu_mul(desc, index, values, meta, X, G, Y, y_dtype=None, workspace=None, stream=None) -> None:

@@ -8,6 +8,9 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <atomic>
+#include <mutex>
+
 #include "hts.h"
 #include "hts_internal.h"
 
@@ -259,6 +262,51 @@ hts_status gemm_impl(const hts_desc* d, const hts_tile* index, const void* value
     return run_gemm(a, static_cast<hipStream_t>(stream));
 }
 
+// Scratch of hts_gemm_noalloc: library-owned device memory, one copy per GPU (each device holds
+// its own instance of a __device__ array, at its own address, from module load until the process
+// ends).  Host code never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+class ScratchAddress {
+  public:
+    static constexpr int kMaxDevices = 64;
+    hts_status get(void** out) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(HTS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        if (dev < 0 || dev >= kMaxDevices) return fail(HTS_ERR_HIP, "device %d beyond the %d supported", dev, kMaxDevices);
+        void* p = ptr_[dev].load(std::memory_order_acquire);
+        if (!p) {
+            std::lock_guard<std::mutex> lock(mu_);
+            p = ptr_[dev].load(std::memory_order_relaxed);
+            if (!p) {
+                e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+                if (e != hipSuccess || !p)
+                    return fail(HTS_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+                ptr_[dev].store(p, std::memory_order_release);
+            }
+        }
+        *out = p;
+        return HTS_OK;
+    }
+
+  private:
+    std::mutex mu_;
+    std::atomic<void*> ptr_[kMaxDevices] = {};
+};
+ScratchAddress g_scratch;
+
+// Workspace bytes hts_gemm uses at this shape and M (what hts_gemm_workspace reports).
+uint64_t gemm_workspace_bytes(const hts_desc* d, int64_t M) {
+    const uint64_t ws = unpack_workspace_bytes(d, M);
+    // the unpacked weight (tiles of 32), then the parts of a split product
+    const int br = (ws || d->bn != 64) ? 128 : 64;
+    const int bk = ws ? ((d->K % 128 == 0) ? 128 : 64) : d->bk;   // the unpacked product's slices
+    return ws + split_bytes(M, d->N, prefill_split(M, d->N, d->K, d->dtype, bk, br));
+}
+
 }  // namespace
 
 extern "C" {
@@ -368,11 +416,7 @@ hts_status hts_gemm_workspace(const hts_desc* d, int64_t M, size_t* bytes) {
     if (st) return st;
     if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
     if (!bytes) return fail(HTS_ERR_INVALID_ARG, "bytes is NULL");
-    const uint64_t ws = unpack_workspace_bytes(d, M);
-    // the unpacked weight (tiles of 32), then the parts of a split product
-    const int br = (ws || d->bn != 64) ? 128 : 64;
-    const int bk = ws ? ((d->K % 128 == 0) ? 128 : 64) : d->bk;   // the unpacked product's slices
-    *bytes = (size_t)(ws + split_bytes(M, d->N, prefill_split(M, d->N, d->K, d->dtype, bk, br)));
+    *bytes = (size_t)gemm_workspace_bytes(d, M);
     return ok();
 }
 
@@ -380,6 +424,23 @@ hts_status hts_gemm(const hts_desc* d, const hts_tile* index, const void* values
                     const void* X, int64_t ldx, void* Y, int64_t ldy, int32_t y_dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
     return gemm_impl(d, index, values, meta, M, X, ldx, nullptr, 0, Y, ldy, y_dtype, workspace, workspace_bytes,
+                     stream);
+}
+
+hts_status hts_gemm_noalloc(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta,
+                            int64_t M, const void* X, int64_t ldx, void* Y, int64_t ldy, int32_t y_dtype,
+                            void* stream) {
+    hts_status st = check_desc(d);
+    if (st) return st;
+    if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
+    const uint64_t need = gemm_workspace_bytes(d, M);
+    if (need > kScratchBytes)
+        return fail(HTS_ERR_WORKSPACE, "M=%lld on this weight needs %llu bytes of scratch, above the %zu-byte maximum "
+                    "of hts_gemm_noalloc (use hts_gemm with a workspace)",
+                    (long long)M, (unsigned long long)need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && (st = g_scratch.get(&ws))) return st;
+    return gemm_impl(d, index, values, meta, M, X, ldx, nullptr, 0, Y, ldy, y_dtype, ws, ws ? kScratchBytes : 0,
                      stream);
 }
 

@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhts.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["hts_api.cpp", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "wanda.hip", "elementwise.hip"]
+SOURCES = ["hts_api.cpp", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_xr.hip", "wanda.hip",
+           "elementwise.hip"]
 
 ARCH = "gfx950"
 COMMON = [
@@ -26,12 +27,13 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # no contraction of separate multiplies and adds: bit-exact selection and sums
     "-ffp-contract=off",
-    # matrix-core accumulators in VGPRs: dense and sparse instructions then share them
-    # without AGPR<->VGPR copies at the type branches
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# matrix-core accumulators in VGPRs: dense and sparse instructions then share them without
+# AGPR<->VGPR copies at the type branches (the AGPR file still takes register spills)
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+PER_FILE: dict = {}
 
 
 def hipcc() -> str:
@@ -44,7 +46,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     # every source, the host API included, is compiled as HIP (it calls the HIP runtime)
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *PER_FILE.get(src, VGPR_FORM), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -76,6 +76,10 @@ hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int
 // Tiled kernel (one tile row x 128 X rows per workgroup); with a.nsplit > 1 it also launches the
 // fixed-order sum of the partial products into Y.
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s);
+// The tiled kernel with X in registers (one tile row x 256 X rows per workgroup): whether it takes
+// this product (unsplit; 128-row tiles or a row-major W), and its launch.
+bool prefill_xr_applies(const GemmArgs& a);
+hipError_t launch_gemm_prefill_xr(const GemmArgs& a, int sparse_path, hipStream_t s);
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the
 // tiled kernel holds the index records of one tile row in LDS.
 constexpr int kMaxTileColsPerRow = 256;

@@ -1,0 +1,244 @@
+// Pieces shared by the tiled (large-M) product kernels: LDS layout of a stage, the copies of a
+// weight slice (and of an X slice) from global memory into LDS, the ordered tile list of a tile
+// row, the workgroup order, and explicit waits on outstanding copies.
+#pragma once
+
+#include "gemm_common.h"
+
+namespace hts {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_t;
+
+constexpr int kGroupBytes = 64 * 128;   // one 64-row weight group, dense (2:4 uses half)
+constexpr int kMetaGroupBytes = 64 * 8; // codes of one 64-row group for one slice (16-bit elements)
+// The single-tile-row kernel also takes 8-bit elements: a slice is always 128 bytes of every
+// row (64 16-bit or 128 8-bit elements), so the LDS image of X and of the weights is the same;
+// only the codes grow, to 16 bytes per row and slice.
+template <int ES> constexpr int slice_k() { return 128 / ES; }
+template <int ES> constexpr int meta_group_bytes() { return 64 * slice_k<ES>() / 8; }
+constexpr int kMaxTileCols = 256;       // K/bk limit: the tile list of a tile row is kept in LDS
+constexpr int kGroupN = 8;
+
+// Block id -> output block (nb, mb).  ord = xcd | (gsn << 1) | (mfast << 6):
+//   xcd   : 1 = each XCD (block id % 8) receives a contiguous range of the order below
+//   gsn   : N-blocks per group (1..31); groups are walked in order
+//   mfast : inside a group, 1 = M-blocks fastest, 0 = N-blocks fastest
+// Default: contiguous per XCD, groups of 8 N-blocks, N fastest, so that the workgroups running
+// together on one XCD cover about 8 N-blocks x 8 M-blocks and share W and X slices in its L2.
+__device__ __forceinline__ void block_of(int L, int NB, int MB, int ord, int& nb, int& mb) {
+    const int total = NB * MB;
+    int id = L;
+    if (ord & 1) {
+        const int P = total / 8;
+        id = (L < 8 * P) ? (L % 8) * P + L / 8 : L;
+    }
+    const int g = (ord >> 1) & 31, mfast = (ord >> 6) & 1;
+    const int gsz = g * MB;
+    const int grp = id / gsz, inb = id % gsz;
+    const int nb0 = grp * g;
+    const int gn = (NB - nb0 < g) ? (NB - nb0) : g;
+    if (mfast) {
+        nb = nb0 + inb / MB;
+        mb = inb % MB;
+    } else {
+        nb = nb0 + inb % gn;
+        mb = inb / gn;
+    }
+}
+
+// LDS image of one stage: X slice (BM rows x 128 B), BN/64 weight groups, their codes.
+template <int BN, int BM, int NSTAGE, int MGB = kMetaGroupBytes>
+struct Layout {
+    static constexpr int NG = BN / 64;
+    static constexpr int WOFF = BM * 128;
+    static constexpr int MOFF = WOFF + NG * kGroupBytes;
+    static constexpr int STAGE = MOFF + NG * MGB;
+    static constexpr int SINK = NSTAGE * STAGE;              // target of padding copies / writes (2 KiB)
+    static constexpr int LIST = SINK + 2048;                 // ordered tile list: {val_off, meta_off}
+    static constexpr int LCOL = LIST + kMaxTileCols * 8;     // ... and the tile column of each entry
+    static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // dense tiles of each chunk (bytes)
+    static constexpr int TOTAL = WCNT + 64;
+};
+
+// Dynamic LDS of the tiled kernels; copies address it by byte offset from an LDS-typed base,
+// so no generic-to-LDS pointer conversion is needed per copy.
+extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ lds_u8* lds_base() { return (lds_u8*)smem; }
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t*)(lds_base() + lds_off), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_off) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t*)(lds_base() + lds_off), 4, 0, 0);
+}
+// The same copies through a buffer resource: a scalar base and byte bound, a per-lane 32-bit
+// offset fixed for the K loop and a scalar offset per slice -- no 64-bit address arithmetic per
+// copy.  Lanes past the bound read zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ void buf16(rsrc_t r, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)(lds_base() + lds_off), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf4(rsrc_t r, uint32_t lds_off, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)(lds_base() + lds_off), 4, voff, soff, 0, 0);
+}
+
+// Everything the copy jobs need, fixed for the whole K loop.  A job moves 1 KiB (64
+// lanes x 16 B) into contiguous LDS; each lane picks the global chunk whose swizzled
+// LDS position is its slot.
+template <int BK, bool HYB, int BN, int BM, int NW>
+struct Ctx {
+    static constexpr int NG = BN / 64;
+    static constexpr int JPG = 8 / NW;  // copy jobs per 64-row group per wave
+    static constexpr int XJ = BM / (8 * NW);  // X copy jobs per wave
+    int64_t ldw;
+    int64_t N, n0;
+    int r0;                     // first row of the block inside its tile (0 when BN == bn)
+    int wave, lane;
+    uint32_t lnd;               // lane c: dense tiles of chunk c (they come first in the chunk)
+    // the ordered list in registers, 64 entries per register (K / bk <= 256).  It is read in order,
+    // and after each block of 64 entries the registers move down by one (shift_list), so entry p
+    // is always lane p % 64 of the first register: one lane read, no register select.
+    uint32_t lv[4], lm[4], lc[4];
+    int Tk;
+    rsrc_t xr;                          // X rows m0 .. M-1
+    rsrc_t wr;                          // values of the tile row from its first tile (or W rows n0 ..)
+    rsrc_t mr;                          // codes of the tile row from its first tile
+    uint32_t vbase, mbase;              // first value / code word of the tile row
+    uint32_t xso;                       // bytes: tile column and slice of the X copies of a slice
+    uint32_t xvo[XJ > 0 ? XJ : 1];      // per-lane byte offsets: X jobs (none when X bypasses LDS)
+    uint32_t dvo[JPG];                  // dense group jobs (row * BK + chunk, or row * ldw + chunk)
+    uint32_t svo;                       // 2:4 values job
+    uint32_t mvo;                       // 2:4 codes job
+    bool meta_to_sink;                  // a codes job past the codes of a slice repeats one into the sink
+    int mjob;                           // this wave's codes job (256 bytes each)
+    __device__ __forceinline__ bool gvalid(int gi) const { return n0 + 64 * gi < N; }
+    __device__ __forceinline__ void shift_list() {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            lv[w] = lv[w + 1];
+            lm[w] = lm[w + 1];
+            lc[w] = lc[w + 1];
+        }
+        lv[3] = lm[3] = lc[3] = 0u;
+    }
+};
+
+// Entry p of a list held one entry per lane (a uniform read: no LDS access); the caller has
+// shifted the registers so that the block of entry p is in the first one.
+__device__ __forceinline__ uint32_t list_entry(const uint32_t (&r)[4], int p) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)r[0], p & 63);
+}
+
+// Copies of one slice into an LDS stage.  Per 64-row weight group there are 8 copy jobs:
+// dense = 8 x 1 KiB; 2:4 = 4 x 1 KiB of stored values, 2 x 256 B of codes and 2 padding copies
+// of the codes into a sink.  Each of the NW waves issues BM/(8 NW) X copies and 8/NW copies per
+// group for every slice, whatever the tile types, so the wait for one slice is a fixed count
+// of outstanding copies.  KIND (dense / 2:4) is known at compile time: no branch per copy.
+template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW, int ES = 2>
+__device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, int ks, uint32_t stage) {
+    constexpr int JPG = 8 / NW;
+    constexpr int KSL = slice_k<ES>(), MGB = meta_group_bytes<ES>();
+    using Lo = Layout<BN, BM, NSTAGE, MGB>;
+    constexpr int SPT = BK / KSL;
+    const int p = ks / SPT, s = ks % SPT;     // list position, slice of the tile
+    // read the list entry before any copy is issued: an LDS read after a copy into LDS makes
+    // the compiler wait for every copy in flight
+    uint32_t voff = 0, moff = 0;
+    if (HYB) {                                // every group of the block is in the same tile
+        voff = list_entry(C.lv, p);
+        moff = list_entry(C.lm, p);
+    }
+#pragma unroll
+    for (int v = 0; v < BM / (8 * NW); ++v) buf16(C.xr, stage + 1024 * (C.wave + NW * v), C.xvo[v], C.xso);
+#pragma unroll
+    for (int gi = 0; gi < Lo::NG; ++gi) {
+        const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
+        if (!HYB) {                             // rows past N read zeros (bound of the resource)
+#pragma unroll
+            for (int v = 0; v < JPG; ++v)
+                buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v],
+                      (uint32_t)(ES * 64 * gi * C.ldw + 128 * (int64_t)ks));
+            continue;
+        }
+        const uint32_t r = 64 * gi;             // a block is one tile row: groups at rows 0, 64
+        if (DENSE) {
+            // packed tile: slice s is chunk columns 8s .. 8s+7 of every row, 2048 bytes per 8 columns
+            const uint32_t so = ES * (voff - C.vbase + r * BK) + 2048 * s;
+#pragma unroll
+            for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
+        } else {
+            // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
+            // codes, then the same two again into the sink).  With 4 waves wave w does jobs w and
+            // 4 + w, with 8 waves job w.
+            if (NW == 4 || C.wave < 4)
+                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
+            if (NW == 4 || C.wave >= 4)
+                buf4(C.mr,
+                     C.meta_to_sink ? (uint32_t)Lo::SINK
+                                    : stage + Lo::MOFF + gi * MGB + 256 * C.mjob,
+                     C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt with vmcnt = N (low 4 bits and bits 14..15), expcnt and lgkmcnt left at their maxima
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Reads the tile row's index records (one tile column per thread: K / bk <= 256 <= threads) and
+// leaves the ordered list in C's registers: the row cut into chunks of 2^lch tile columns (inside
+// one wave: lch <= 6), each ordered dense first; C.lnd lane c = dense tiles of chunk c.  Tile rows
+// then walk K chunk by chunk, so workgroups of different tile rows that run together stay within a
+// chunk of each other and find each other's X slices in L2.  Uses LDS at Lo::LIST .. Lo::TOTAL.
+template <typename Lo, int BK, bool HYB, int BN, int BM, int NW>
+__device__ __forceinline__ void load_tile_list(Ctx<BK, HYB, BN, BM, NW>& C, const GemmArgs& a, int lch, int tid,
+                                               int lane) {
+    uint2* list = reinterpret_cast<uint2*>(smem + Lo::LIST);
+    uint16_t* lcol = reinterpret_cast<uint16_t*>(smem + Lo::LCOL);
+    uint8_t* cnd = reinterpret_cast<uint8_t*>(smem + Lo::WCNT);   // dense tiles per chunk (<= 64 chunks)
+    const int tn = (int)(C.n0 / a.bn);
+    const int t = tid;
+    hts_tile e = {0u, 0u, 0u, 0u};
+    const bool have = t < C.Tk;
+    if (have) e = a.index[(int64_t)tn * C.Tk + t];
+    const bool isd = have && e.type == HTS_TILE_DENSE, iss = have && !isd;
+    const uint64_t bd = __ballot(isd), bs = __ballot(iss);
+    const int ch = 1 << lch, cl = lane & ~(ch - 1);             // first lane of this chunk
+    const uint64_t cm = (lch == 6 ? ~0ull : ((1ull << ch) - 1)) << cl;
+    const uint64_t lt = (1ull << lane) - 1;                      // lanes below this one
+    const int nd_c = __popcll(bd & cm);
+    const int below_d = __popcll(bd & cm & lt), below_s = __popcll(bs & cm & lt);
+    if (have) {
+        const int pos = (t & ~(ch - 1)) + (isd ? below_d : nd_c + below_s);
+        list[pos] = uint2{e.val_off, e.meta_off};
+        lcol[pos] = (uint16_t)t;
+        if (lane == cl) cnd[t >> lch] = (uint8_t)nd_c;
+    }
+    __syncthreads();
+    const int nch = (C.Tk + ch - 1) >> lch;
+    C.lnd = lane < nch ? (uint32_t)cnd[lane] : 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int q = 64 * w + lane;
+        const bool in = q < C.Tk;
+        C.lv[w] = in ? list[q].x : 0u;
+        C.lm[w] = in ? list[q].y : 0u;
+        C.lc[w] = in ? (uint32_t)lcol[q] : 0u;
+    }
+}
+
+}  // namespace
+
+// Host side (gemm_prefill.hip): tile columns per dense-first chunk of the ordered list, as log2.
+int prefill_chunk_log2(int bk);
+
+}  // namespace hts

@@ -37,11 +37,13 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// X fragments of one slice for a wave's four 16-row blocks: lane j + 16 g reads chunks c0(g) and
-// c1(g) (16 bytes each) of row 16 bj + j.  Rows past M read zeros (resource bound).
+// X fragments of one slice for a wave's four 16-row blocks, from X rearranged into 16-row panels
+// (chunk c of panel row j at (16 c + j) * 16 bytes from the panel start): lane j + 16 g takes chunks
+// c0(g) and c1(g) of row j of the slice.  In the sparse-instruction order (c0 = g, c1 = 4 + g) each
+// load is one contiguous kilobyte.  Panels past the packed rows read zeros (resource bound).
 template <int SP>
 __device__ __forceinline__ void load_xr(u32x8 (&B)[4], rsrc_t xr, const uint32_t (&xv)[4], uint32_t so) {
-    constexpr uint32_t dch = SP == SPARSE_SMFMAC ? 64u : 16u;   // c1 - c0 in bytes
+    constexpr uint32_t dch = SP == SPARSE_SMFMAC ? 1024u : 256u;   // (c1 - c0) * 256 bytes
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
         const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xv[bj], so, 0));
@@ -50,119 +52,81 @@ __device__ __forceinline__ void load_xr(u32x8 (&B)[4], rsrc_t xr, const uint32_t
     }
 }
 
-// Instruction interleaving inside one slice (sched_group_barrier masks: MFMA 0x8, VMEM read 0x20,
-// DS read 0x100, DS write 0x200).  The wave runs alone on its SIMD, so its global loads and LDS
-// writes are issued between matrix-core instructions -- each of which runs for 16 cycles while the
-// next ones issue -- instead of ahead of them.
-#define HTS_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+// Half-slice software pipeline.  A slice is fed to the matrix cores in two halves -- dense: the
+// two 32-deep substeps over all 8 row blocks (32 MFMA each); 2:4: row blocks 0-3, then 4-7 (16
+// SMFMAC each) -- and the weight fragments of each half are read from LDS during the previous
+// half, so no product waits for LDS.  Fragment registers have one shape for both tile types (8
+// value kilobytes and 4 code words; a 2:4 half uses 4 + 4, and its other reads repeat those), so a
+// half of either type can follow a half of the other with no register copies.
+struct Frags {
+    u32x4 a[8];
+    uint32_t idx[4];
+};
 
-// One dense slice: the weight fragments of the 8 row blocks from LDS (PANEL: packed stored order,
-// chunk c of row i at (16 c + i) * 16; otherwise row-major W with XOR-swizzled chunks), X fragments
-// from registers; `loads` issues the next slices' global loads (13 instructions) and `store`
-// writes the next weight slice into LDS (6 writes), both spread over the 64 products.
-template <typename T, int SP, bool PANEL, typename FL, typename FS>
-__device__ __forceinline__ void dense_slice_xr(f32x4 (&acc)[8][4], const u32x8 (&B)[4], const uint8_t* ws, int lane,
-                                               FL&& loads, FS&& store) {
-    const int i = lane & 15, g = lane >> 4;
-    const int c0 = (SP == SPARSE_SMFMAC) ? g : 2 * g;
-    const int c1 = (SP == SPARSE_SMFMAC) ? 4 + g : 2 * g + 1;
-    const int a0 = PANEL ? 16 * (16 * c0 + i) : i * 128 + 16 * (c0 ^ ((i >> 1) & 7));
-    const int a1 = PANEL ? 16 * (16 * c1 + i) : i * 128 + 16 * (c1 ^ ((i >> 1) & 7));
-    u32x4 A[2][8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) A[u][b] = ld16(ws + b * 2048 + (u ? a1 : a0));
-    loads();
-    store();
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int bj = 0; bj < 4; ++bj)
-                acc[b][bj] = mfma_dense<T>(A[u][b], u ? hi4(B[bj]) : lo4(B[bj]), acc[b][bj]);
-    // substep-0 fragments first; the substep-1 fragments under the first products; then the global
-    // loads and the LDS writes among the rest
-    HTS_SGB(0x100, 8);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        HTS_SGB(0x008, 2);
-        HTS_SGB(0x100, 1);
-    }
-#pragma unroll
-    for (int r = 0; r < 13; ++r) {
-        HTS_SGB(0x008, 2);
-        HTS_SGB(0x020, 1);
-    }
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
-        HTS_SGB(0x008, 2);
-        HTS_SGB(0x200, 1);
-    }
-    HTS_SGB(0x008, 64);
-}
-
-// One 2:4 slice: stored values (1 KiB per 16-row block) and codes of both 64-row groups of the stage.
-template <typename T, int SP, typename FL, typename FS>
-__device__ __forceinline__ void sparse_slice_xr(f32x4 (&acc)[8][4], const u32x8 (&B)[4], const uint8_t* ws,
-                                                const uint32_t* ms, int lane, FL&& loads, FS&& store) {
+// Reads the fragments of half h of the slice in the LDS stage `ws` (codes at ws + 2 groups).
+// PANEL: packed stored order (chunk c of row i at (16 c + i) * 16); otherwise row-major W with
+// XOR-swizzled chunks (dense only).
+template <typename T, int SP, bool PANEL, int h>
+__device__ __forceinline__ void read_half(Frags& F, const uint8_t* ws, bool dense, int lane) {
     constexpr int MW = meta_group_bytes<Elem<T>::bytes>() / 4;   // code words of a 64-row group
     const int i = lane & 15, g = lane >> 4;
-    const int s0 = 16 * (16 * g + i);    // stored order: chunk g of row i of the 16-row block
-    if constexpr (SP == SPARSE_SMFMAC) {
-        u32x4 A[8];
-        uint32_t idx[8];
+    const int c = (SP == SPARSE_SMFMAC) ? (h ? 4 + g : g) : (2 * g + h);
+    const int ad = PANEL ? 16 * (16 * c + i) : i * 128 + 16 * (c ^ ((i >> 1) & 7));
+    const int as = h * kGroupBytes + 16 * (16 * g + i);        // 2:4 values: chunk g of row i of block b
+    const uint32_t* ms = reinterpret_cast<const uint32_t*>(ws + 2 * kGroupBytes) + h * MW;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            A[b] = ld16(ws + (b >> 2) * kGroupBytes + (b & 3) * 1024 + s0);
-            const uint32_t* mg = ms + (b >> 2) * MW;
-            const int r = 16 * (b & 3) + i;
-            // 16-bit: a 16-bit half of the row's word g/2; 8-bit: the row's whole word g
-            idx[b] = Elem<T>::bytes == 1 ? mg[4 * r + g] : mg[2 * r + (g >> 1)] >> (16 * (g & 1));
+    for (int b = 0; b < 8; ++b) F.a[b] = ld16(ws + (dense ? b * 2048 + ad : (b & 3) * 1024 + as));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int r = 16 * b + i;
+        // 16-bit: a 16-bit half of the row's word g/2 (SMFMAC) or the row's word g/2 (expansion,
+        // both halves); 8-bit: the row's whole word g
+        F.idx[b] = Elem<T>::bytes == 1 ? ms[4 * r + g] : ms[2 * r + (g >> 1)];
+    }
+}
+
+// Products of half h (dense: substep u = h) with X fragments B.
+// Products of half h (dense: substep u = h) with X fragments B, for fragment rows [R0, R1) of the
+// half (dense: row blocks R0..R1-1 of 8; 2:4: row blocks 4h + R0 .. of 4, R1 <= 4).
+template <typename T, int SP, bool DENSE, int h, int R0, int R1>
+__device__ __forceinline__ void mma_part(f32x4 (&acc)[8][4], const Frags& F, const u32x8 (&B)[4], int lane) {
+    const int g = lane >> 4;
+    if constexpr (DENSE) {
+#pragma unroll
+        for (int b = R0; b < R1; ++b)
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+                acc[b][bj] = mfma_dense<T>(F.a[b], h ? hi4(B[bj]) : lo4(B[bj]), acc[b][bj]);
+    } else if constexpr (SP == SPARSE_SMFMAC) {
+#pragma unroll
+        for (int b = R0; b < R1; ++b) {
+            const uint32_t idx = Elem<T>::bytes == 1 ? F.idx[b] : F.idx[b] >> (16 * (g & 1));
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+                acc[4 * h + b][bj] = mfma_sparse<T, 0>(F.a[b], B[bj], idx, acc[4 * h + b][bj]);
         }
-        loads();
-        store();
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int bj = 0; bj < 4; ++bj) acc[b][bj] = mfma_sparse<T, 0>(A[b], B[bj], idx[b], acc[b][bj]);
-        HTS_SGB(0x100, 16);
-#pragma unroll
-        for (int r = 0; r < 13; ++r) {
-            HTS_SGB(0x008, 1);
-            HTS_SGB(0x020, 1);
-        }
-#pragma unroll
-        for (int r = 0; r < 6; ++r) {
-            HTS_SGB(0x008, 1);
-            HTS_SGB(0x200, 1);
-        }
-        HTS_SGB(0x008, 32);
     } else {
         // expansion order: lane group g, substep u covers dense k [16g + 8u, +8) of the slice =
         // groups 4g + 2u, +1: stored bytes 16g + 8u of the row, codes at bit 16g + 8u
-        uint2 v[2][8];
-        uint32_t code[8];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint8_t* p = ws + (b >> 2) * kGroupBytes + (b & 3) * 1024 + s0;
-            v[0][b] = *reinterpret_cast<const uint2*>(p);
-            v[1][b] = *reinterpret_cast<const uint2*>(p + 8);
-            code[b] = ms[(b >> 2) * MW + 2 * (16 * (b & 3) + i) + (g >> 1)] >> (16 * (g & 1));
-        }
-        loads();
-        store();
+        for (int b = R0; b < R1; ++b) {
+            const uint32_t code = F.idx[b] >> (16 * (g & 1));
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < 2; ++u) {
+                const u32x4 e = expand_two_groups(uint2{F.a[b][2 * u], F.a[b][2 * u + 1]}, (code >> (8 * u)) & 0xFFu);
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const u32x4 e = expand_two_groups(v[u][b], (code[b] >> (8 * u)) & 0xFFu);
-#pragma unroll
-                for (int bj = 0; bj < 4; ++bj) acc[b][bj] = mfma_dense<T>(e, u ? hi4(B[bj]) : lo4(B[bj]), acc[b][bj]);
+                for (int bj = 0; bj < 4; ++bj)
+                    acc[4 * h + b][bj] = mfma_dense<T>(e, u ? hi4(B[bj]) : lo4(B[bj]), acc[4 * h + b][bj]);
             }
+        }
     }
 }
+
+// Order barrier between the parts of a half (the compiler keeps program order across it).
+__device__ __forceinline__ void part_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Weight slice of the block in registers on its way to LDS: a wave's share (4 x 1 KiB of a dense
 // slice; 2 x 1 KiB of 2:4 values and its code words of a 2:4 slice).
@@ -248,7 +212,7 @@ template <typename T, int BK, bool HYB, int SP>
 __global__ __launch_bounds__(256) void gemm_prefill_xr_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
     constexpr int ES = Elem<T>::bytes, KSL = slice_k<ES>(), MGB = meta_group_bytes<ES>();
     constexpr int BN = 128, BMX = 256, NW = 4, SPT = BK / KSL;
-    using Lo = Layout<BN, 0, 2, MGB>;          // two LDS stages of the weight slice
+    using Lo = Layout<BN, 0, 3, MGB>;          // three LDS stages of the weight slice
     static_assert(Lo::WOFF == 0 && Lo::MOFF == 2 * kGroupBytes, "stage layout");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -306,15 +270,17 @@ __global__ __launch_bounds__(256) void gemm_prefill_xr_kernel(const GemmArgs a, 
         }
     }
 
-    // X: this wave's 64 rows of the block (rows past M read zeros)
+    // X: this wave's four 16-row panels of the block, from the panel copy of X (xpanel)
     const int i = lane & 15, g = lane >> 4;
-    const int c0 = (SP == SPARSE_SMFMAC) ? g : 2 * g;
     const int64_t xrow0 = m0 + 64 * wave;
-    const uint8_t* Xb = reinterpret_cast<const uint8_t*>(a.X);
-    const rsrc_t xr = make_rsrc(Xb + ES * xrow0 * a.ldx, xrow0 < a.M ? (uint64_t)(a.M - xrow0) * a.ldx * ES : 0ull);
+    const int64_t pstride = 16 * a.K * ES;                          // bytes per 16-row panel
+    const int64_t npanel = (a.M + 15) / 16, p0 = xrow0 / 16;
+    const rsrc_t xr = make_rsrc(reinterpret_cast<const uint8_t*>(a.xpanel) + p0 * pstride,
+                                p0 < npanel ? (uint64_t)(npanel - p0) * pstride : 0ull);
     uint32_t xv[4];
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) xv[bj] = (uint32_t)(ES * (int64_t)(16 * bj + i) * a.ldx + 16 * c0);
+    for (int bj = 0; bj < 4; ++bj)
+        xv[bj] = (uint32_t)(bj * pstride + (SP == SPARSE_SMFMAC ? 16 * lane : 512 * g + 16 * i));
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -324,25 +290,23 @@ __global__ __launch_bounds__(256) void gemm_prefill_xr_kernel(const GemmArgs a, 
 
     const int S = Tk * SPT, lcs = lch + (SPT == 2 ? 1 : 0);   // slices per chunk: 2^lcs
     // slice kn is dense when it lies in the dense run at the start of its chunk (chunk-ordered list)
-    auto dense_slice = [&](int kn) {
+    auto dense_slice = [&](int kn) __attribute__((always_inline)) {
         return !HYB || (kn & ((1 << lcs) - 1)) < SPT * (int)__builtin_amdgcn_readlane((int)C.lnd, kn >> lcs);
     };
-    // list readers: weight loads run two slices ahead of the products, X loads one; each keeps its
-    // own copy of the list registers, shifted on its own schedule (called with kn = 0, 1, ...)
-    uint32_t xlc[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) xlc[w] = C.lc[w];
     // Loads past the last slice are issued anyway, of the last slice again: every path then issues
     // the same loads, so the compiler's count of outstanding loads (and the waits it derives for the
     // operands) is exact at every join instead of assuming the shortest path.
-    auto load_w = [&](WRegs& R, int kn) {
+    uint32_t xlc[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) xlc[w] = C.lc[w];
+    auto load_w = [&](WRegs& R, int kn) __attribute__((always_inline)) {     // called with kn = 0, 1, 2, ...
         if (HYB && kn < S && kn > 0 && kn % (64 * SPT) == 0) C.shift_list();
         const int kc = kn < S ? kn : S - 1;
         const int p = kc / SPT;
         const uint32_t voff = HYB ? list_entry(C.lv, p) : 0u, moff = HYB ? list_entry(C.lm, p) : 0u;
         WC.load(R, dense_slice(kc), voff, moff, kc);
     };
-    auto load_x = [&](u32x8 (&B)[4], int kn) {
+    auto load_x = [&](u32x8 (&B)[4], int kn) __attribute__((always_inline)) {   // called with kn = 0, 1, 2, ...
         if (HYB && kn < S && kn > 0 && kn % (64 * SPT) == 0) {
 #pragma unroll
             for (int w = 0; w < 3; ++w) xlc[w] = xlc[w + 1];
@@ -351,47 +315,81 @@ __global__ __launch_bounds__(256) void gemm_prefill_xr_kernel(const GemmArgs a, 
         const int kc = kn < S ? kn : S - 1;
         const int p = kc / SPT, s = kc % SPT;
         const int tk = HYB ? (int)__builtin_amdgcn_readlane((int)xlc[0], p & 63) : p;
-        load_xr<SP>(B, xr, xv, (uint32_t)(ES * tk * BK + 128 * s));
+        load_xr<SP>(B, xr, xv, (uint32_t)(16 * (ES * tk * BK + 128 * s)));   // chunk column * 256 bytes
     };
+    auto stage = [&](int kn) __attribute__((always_inline)) { return smem + (kn % 3) * Lo::STAGE; };
 
-    // prologue: W(0) -> stage 0, W(1) and X(0) in flight
-    WRegs R[2];
-    u32x8 B[2][4];
+    // prologue: W(0), W(1) into stages 0 and 1, W(2) and X(0) in flight, half 0 of slice 0 read
+    // register sets rotate with the slice: P = ks % 3 -- X(ks) in B[P] (loaded two slices ahead),
+    // W(ks+3) loaded into R[P], W(ks+2) (loaded one slice ago, in R[(P+2) % 3]) written to LDS
+    WRegs R[3];
+    u32x8 B[3][4];
+    Frags H0, H1;
     load_w(R[0], 0);
     load_x(B[0], 0);
     load_w(R[1], 1);
-    WC.store(R[0], dense_slice(0), smem, smem + Lo::SINK);
+    load_x(B[1], 1);
+    WC.store(R[0], dense_slice(0), stage(0), smem + Lo::SINK);
+    WC.store(R[1], dense_slice(S > 1 ? 1 : 0), stage(1), smem + Lo::SINK);
+    load_w(R[2], 2);
+    barrier_lds();
+    read_half<T, SP, HYB, 0>(H0, stage(0), dense_slice(0), lane);
 
-    // slice ks (register set P = ks % 2, type DENSE known per run): barrier (stage ks % 2 complete
-    // in LDS; stage (ks+1) % 2 no longer read); fragments of slice ks from LDS; then, under those
-    // reads, the X(ks+1) and W(ks+2) loads; the products; last, W(ks+1) (loaded one slice ago) into
-    // stage (ks+1) % 2 (past the last slice: the last slice again, into a stage no one reads)
-    auto slice = [&](auto PP, auto DD, int ks) {
+    // slice ks (B and R register sets P = ks % 2; weight stage ks % 3): barrier -- stage ks+1
+    // complete, stage ks+2 no longer read; first half: products of half 0 while half 1 of slice ks
+    // is read and the X(ks+1) and W(ks+3) loads issue; second half: products of half 1 while half 0
+    // of slice ks+1 is read and W(ks+2) is written to its stage
+    auto slice = [&](auto PP, auto DD, int ks) __attribute__((always_inline)) {
         constexpr int P = decltype(PP)::value;
         constexpr bool DENSE = decltype(DD)::value;
         barrier_lds();
-        const uint8_t* st = smem + P * Lo::STAGE;
-        auto loads = [&] {
-            load_x(B[1 - P], ks + 1);
-            load_w(R[P], ks + 2);
-        };
-        auto store = [&] {
-            WC.store(R[1 - P], dense_slice(ks + 1 < S ? ks + 1 : S - 1), smem + (1 - P) * Lo::STAGE, smem + Lo::SINK);
-        };
-        if constexpr (DENSE) dense_slice_xr<T, SP, HYB>(acc, B[P], st, lane, loads, store);
-        else sparse_slice_xr<T, SP>(acc, B[P], st, reinterpret_cast<const uint32_t*>(st + Lo::MOFF), lane, loads, store);
+        const int kn1 = ks + 1 < S ? ks + 1 : S - 1;
+        const bool next_dense = dense_slice(kn1);
+        // rows of a half: dense 8 (32 products), 2:4 4 (16)
+        constexpr int RH = DENSE ? 8 : 4, Q = RH / 4;
+        // first half: products of half 0 (fragments read in the previous slice), with the reads of
+        // half 1 and the global loads of later slices issued among them
+        read_half<T, SP, HYB, 1>(H1, stage(ks), DENSE, lane);
+        part_fence();
+        mma_part<T, SP, DENSE, 0, 0, Q>(acc, H0, B[P], lane);
+        part_fence();
+        load_x(B[(P + 2) % 3], ks + 2);
+        part_fence();
+        mma_part<T, SP, DENSE, 0, Q, 2 * Q>(acc, H0, B[P], lane);
+        part_fence();
+        load_w(R[P], ks + 3);
+        part_fence();
+        mma_part<T, SP, DENSE, 0, 2 * Q, RH>(acc, H0, B[P], lane);
+        part_fence();
+        wait_lgkm0();                        // half 1 has long landed: no later wait counts these reads
+        // second half: products of half 1, with the reads of half 0 of slice ks+1 and the weight
+        // writes of slice ks+2 among them
+        mma_part<T, SP, DENSE, 1, 0, Q>(acc, H1, B[P], lane);
+        part_fence();
+        read_half<T, SP, HYB, 0>(H0, stage(ks + 1), next_dense, lane);
+        part_fence();
+        mma_part<T, SP, DENSE, 1, Q, 3 * Q>(acc, H1, B[P], lane);
+        part_fence();
+        WC.store(R[(P + 2) % 3], dense_slice(ks + 2 < S ? ks + 2 : S - 1), stage(ks + 2), smem + Lo::SINK);
+        part_fence();
+        mma_part<T, SP, DENSE, 1, 3 * Q, RH>(acc, H1, B[P], lane);
+        part_fence();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    // slices ks .. end-1, all of one type: the register set follows the slice's parity, so the
-    // unrolled pairs start on an even slice
-    auto run = [&](int& ks, int end, auto DD) {
-        if (ks < end && (ks & 1)) slice(I1{}, DD, ks++);
-        for (; ks + 1 < end; ks += 2) {
+    // slices ks .. end-1, all of one type: the register sets follow ks % 3, so the unrolled triples
+    // start on a multiple of three
+    using I2 = std::integral_constant<int, 2>;
+    auto run = [&](int& ks, int end, auto DD) __attribute__((always_inline)) {
+        if (ks < end && ks % 3 == 1) slice(I1{}, DD, ks++);
+        if (ks < end && ks % 3 == 2) slice(I2{}, DD, ks++);
+        for (; ks + 2 < end; ks += 3) {
             slice(I0{}, DD, ks);
             slice(I1{}, DD, ks + 1);
+            slice(I2{}, DD, ks + 2);
         }
         if (ks < end) slice(I0{}, DD, ks++);
+        if (ks < end) slice(I1{}, DD, ks++);
     };
     using DenseT = std::true_type;
     using SparseT = std::false_type;
@@ -440,6 +438,19 @@ __global__ __launch_bounds__(256) void gemm_prefill_xr_kernel(const GemmArgs a, 
     }
 }
 
+// X[M,K] rearranged into 16-row panels: chunk c (16 bytes) of panel row j at (16 c + j) * 16 bytes
+// from the panel start, rows past M zero.  One chunk per thread, consecutive threads on consecutive
+// destination chunks (whole cache lines written).
+__global__ __launch_bounds__(256) void pack_xpanel_kernel(const uint8_t* __restrict__ X, int64_t ldxb, int64_t M,
+                                                          int64_t cpr, uint8_t* __restrict__ P, int64_t total) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int64_t p = t / (16 * cpr), rem = t - p * 16 * cpr, c = rem >> 4, j = rem & 15;
+    const int64_t row = 16 * p + j;
+    const u32x4 v = row < M ? ld16(X + row * ldxb + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+    st16(P + 16 * t, v);
+}
+
 // Workgroup order: each XCD a contiguous range, groups of 4 N-blocks, N fastest (the 32 workgroups
 // an XCD runs together then cover 4 tile rows x 8 blocks of 256 X rows).  HTS_PREFILL_XR_ORDER
 // overrides (code as for the LDS-staged kernel's order).
@@ -453,12 +464,19 @@ int prefill_xr_order() {
 
 template <typename T, int BK, bool HYB, int SP>
 hipError_t launch_xr(const GemmArgs& a, hipStream_t s) {
-    using Lo = Layout<128, 0, 2, meta_group_bytes<Elem<T>::bytes>()>;
+    using Lo = Layout<128, 0, 3, meta_group_bytes<Elem<T>::bytes>()>;
     auto kern = gemm_prefill_xr_kernel<T, BK, HYB, SP>;
     static DeviceOnce lds_limit;   // per instantiation and device
     hipError_t e = lds_limit.run([&] {
         return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Lo::TOTAL);
     });
+    if (e != hipSuccess) return e;
+    // X into 16-row panels (the caller's workspace), then the product
+    constexpr int ES = Elem<T>::bytes;
+    const int64_t cpr = a.K * ES / 16, total = ((a.M + 15) / 16) * 16 * cpr;
+    pack_xpanel_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(
+        reinterpret_cast<const uint8_t*>(a.X), a.ldx * ES, a.M, cpr, static_cast<uint8_t*>(a.xpanel), total);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int NB = (int)((a.N + 127) / 128), MB = (int)((a.M + 255) / 256);
     kern<<<dim3((unsigned)(NB * MB)), dim3(256), Lo::TOTAL, s>>>(a, NB, MB, prefill_xr_order(), prefill_chunk_log2(BK));
@@ -485,12 +503,17 @@ hipError_t launch_xr_bk(const GemmArgs& a, int sp, hipStream_t s) {
 
 }  // namespace
 
-// HTS_PREFILL_KERNEL=lds keeps every product on the LDS-staged kernel; =xr sends every unsplit
-// product on 128-row tiles (or a row-major W) here.
-bool prefill_xr_applies(const GemmArgs& a) {
+// HTS_PREFILL_KERNEL=xr sends every unsplit product on 128-row tiles (or a row-major W) with X
+// panels in the workspace here; otherwise (default, or =lds) the LDS-staged kernel runs.
+bool prefill_xr_wanted(int64_t M, int32_t bn, bool packed) {
+    (void)M;
     const char* e = getenv("HTS_PREFILL_KERNEL");
     if (!(e && !strcmp(e, "xr"))) return false;
-    return a.nsplit <= 1 && (!a.index || a.bn == 128);
+    return !packed || bn == 128;
+}
+
+bool prefill_xr_applies(const GemmArgs& a) {
+    return a.xpanel != nullptr && a.nsplit <= 1 && prefill_xr_wanted(a.M, a.bn, a.index != nullptr);
 }
 
 hipError_t launch_gemm_prefill_xr(const GemmArgs& a, int sparse_path, hipStream_t s) {

@@ -46,14 +46,18 @@ def parse():
     p.add_argument("--no-tiles", action="store_true", help="skip the tile-size leg")
     p.add_argument("--no-shard", action="store_true", help="skip the one-GPU-share (8-way N split) leg")
     p.add_argument("--no-mid", action="store_true", help="skip the moderate-M (17..256) leg")
+    p.add_argument("--no-13b", action="store_true", help="skip the 13B-shaped layers")
+    p.add_argument("--no-sweep", action="store_true", help="skip the sparsity sweep")
+    p.add_argument("--no-decompress", action="store_true", help="skip the expansion-fallback leg")
+    p.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run three plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
 # Sources whose change invalidates a recorded counter measurement of the tiled kernel.
-PREFILL_SOURCES = ["tile_gemm_amd/csrc/gemm_prefill.hip", "tile_gemm_amd/csrc/gemm_common.h",
-                   "tile_gemm_amd/csrc/device_common.h"]
+PREFILL_SOURCES = ["tile_gemm_amd/csrc/gemm_prefill.hip", "tile_gemm_amd/csrc/prefill_common.h",
+                   "tile_gemm_amd/csrc/gemm_common.h", "tile_gemm_amd/csrc/device_common.h"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_prefill_7b_up_m2048_hbm_traffic.md")
 
 
@@ -265,6 +269,118 @@ def run_shard(hts, wl, dev, time_graph, time_launches, quick):
     return out
 
 
+def packed_copies(hts, pw0, n):
+    """pw0 and n-1 device copies of it (rotation beyond the Infinity Cache)."""
+    return [pw0] + [hts.PackedWeight(pw0.desc, pw0.index.clone(), pw0.values.clone(), pw0.meta.clone(),
+                                     pw0.sizes, pw0.tile_map) for _ in range(n - 1)]
+
+
+def run_layer(hts, wl, dev, time_graph, time_launches, quick, cfg, L, Ms):
+    """One named layer at each M: the hybrid product against the same weight packed with an
+    all-dense map (same kernels and storage order), the row-major same-library dense product and
+    torch.matmul, every one timed the same way -- M <= 32 as HIP-graph replays of 8 launches per
+    rotated weight copy, larger M as back-to-back launches (best of 3 windows) -- with weight
+    copies rotated beyond the Infinity Cache.  M <= 16 is reported in GB/s of algorithmic bytes
+    (packed weight + X + Y), larger M in TFLOP/s of kept multiply-adds."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[L.dtype]
+    W = hts.tensor_from_bits(wl.weight_bits(cfg, L), L.dtype, dev)
+    tmap = wl.tile_map(cfg, L)
+    Xall = hts.tensor_from_bits(wl.activation_bits(cfg, L, max(Ms)), L.dtype, dev)
+    pw0 = hts.pack(W, tmap, L.bn, L.bk)
+    pd0 = hts.pack(W, np.zeros_like(tmap), L.bn, L.bk)
+    torch.cuda.synchronize()
+    n_rot = max(2, -(-ROTATE_BYTES // pw0.packed_bytes))
+    n_rd = max(2, -(-ROTATE_BYTES // (2 * L.N * L.K)))
+    pws, pds = packed_copies(hts, pw0, n_rot), packed_copies(hts, pd0, n_rd)
+    Ws = [W] + [W.clone() for _ in range(n_rd - 1)]
+    ns = int(tmap.sum())
+    kept = L.N * L.K - ns * L.bn * L.bk // 2
+    rows = []
+    for M in Ms:
+        X = Xall[:M].contiguous()
+        n = max(n_rot, n_rd)
+        Ys = [torch.empty((M, L.N), dtype=tdt, device=dev) for _ in range(n if M <= 32 else 2)]
+        ws = hts.hts_gemm_workspace(pw0.desc, M)
+        WS = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        wd = hts.hts_dense_gemm_workspace(X.dtype, M, L.N, L.K)
+        WSd = torch.empty(wd, dtype=torch.uint8, device=dev) if wd else None
+        fns = {"hyb": lambda i: hts.gemm(X, pws[i % n_rot], out=Ys[i % len(Ys)], workspace=WS),
+               "dpk": lambda i: hts.gemm(X, pds[i % n_rd], out=Ys[i % len(Ys)], workspace=WS),
+               "den": lambda i: hts.dense_gemm(X, Ws[i % n_rd], out=Ys[i % len(Ys)], workspace=WSd),
+               "mm": lambda i: torch.matmul(X, Ws[i % n_rd].t(), out=Ys[i % len(Ys)])}
+        if M <= 32:
+            per, reps = (4, 2) if quick else (8 * n, 10)
+            t = {k: time_graph(f, per, reps) for k, f in fns.items()}
+        else:
+            t = {k: time_launches(f, 5 if quick else 30) for k, f in fns.items()}
+        row = {"M": M, "us": round(t["hyb"] * 1e6, 2), "dense_packed_us": round(t["dpk"] * 1e6, 2),
+               "dense_same_library_us": round(t["den"] * 1e6, 2), "torch_matmul_us": round(t["mm"] * 1e6, 2),
+               "speedup_vs_dense_packed": round(t["dpk"] / t["hyb"], 3),
+               "speedup_vs_dense": round(t["den"] / t["hyb"], 3)}
+        if M <= 16:
+            alg = pw0.packed_bytes + 2 * M * L.K + 2 * M * L.N
+            row.update({"GB/s": round(alg / t["hyb"] / 1e9, 1), "frac_hbm": round(alg / t["hyb"] / 1e9 / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes": alg})
+        else:
+            tf = 2.0 * M * kept / t["hyb"] / 1e12
+            row.update({"TFLOP/s": round(tf, 1), "frac_mfma": round(tf / MFMA_PEAK_TFLOPS[L.dtype], 4),
+                        "dense_equivalent_TFLOP/s": round(2.0 * M * L.N * L.K / t["hyb"] / 1e12, 1)})
+        rows.append(row)
+    out = {"layer": f"{L.name}: W[{L.N}x{L.K}] {L.dtype}, {L.bn}x{L.bk} tiles, {ns}/{L.T} tiles 2:4 "
+                    f"({100.0 * 0.5 * ns / L.T:.1f}% sparsity)",
+           "packed_bytes": pw0.packed_bytes, "rows": rows}
+    del pws, pds, Ws
+    return out
+
+
+def run_13b(hts, wl, dev, time_graph, time_launches, quick):
+    """The two 13B-shaped layers (5120x5120 and 13824x5120, half the tiles 2:4) at M = 1, 16, 4096."""
+    cfg = wl.config("13b")
+    return [run_layer(hts, wl, dev, time_graph, time_launches, quick, cfg, L, list(cfg.Ms)) for L in cfg.layers]
+
+
+def run_sweep(hts, wl, dev, time_graph, time_launches, quick):
+    """The 4096x4096 fp16 layer at sparse-tile fractions p = 0, .25, .5, .75, 1 (0-50% sparsity), M = 1
+    and 2048, with the speed-up ceilings of the packed format (bytes at M = 1, kept flops at 2048)."""
+    cfg = wl.config("sweep")
+    out = []
+    for L in cfg.layers:
+        r = run_layer(hts, wl, dev, time_graph, time_launches, quick, cfg, L, list(cfg.Ms))
+        p = int(wl.tile_map(cfg, L).sum()) / L.T
+        r["p"] = p
+        r["ceiling_bytes"] = round(2.0 / (2.0 - 0.875 * p), 3)
+        r["ceiling_flops"] = round(1.0 / (1.0 - 0.5 * p), 3)
+        out.append(r)
+    return out
+
+
+def run_decompress(hts, wl, dev, time_graph, time_launches, quick):
+    """The 7B up-projection with 2:4 tiles expanded in registers to the dense matrix instruction
+    (the measured fallback of the sparse instruction), at M = 1, 16, 2048."""
+    cfg = wl.config("7b_up")
+    old = os.environ.get("HTS_SPARSE_PATH")
+    os.environ["HTS_SPARSE_PATH"] = "decompress"
+    try:
+        r = run_layer(hts, wl, dev, time_graph, time_launches, quick, cfg, cfg.layers[0], list(cfg.Ms))
+    finally:
+        if old is None:
+            os.environ.pop("HTS_SPARSE_PATH", None)
+        else:
+            os.environ["HTS_SPARSE_PATH"] = old
+    return r
+
+
+def run_peaks(quick):
+    """Measured denominators: one streaming read of 2 GiB, and the matrix-core instructions of the
+    product with register operands (algorithmic TFLOP/s: kept multiply-adds)."""
+    import tile_gemm_amd.peak as peak
+    out = {"hbm_stream_read_GB/s": round(peak.stream_read_gbs(reps=2 if quick else 5), 1)}
+    for k in peak.KINDS:
+        out[f"{k}_TFLOP/s"] = round(peak.mfma_tflops(k, reps=2 if quick else 5), 1)
+    return out
+
+
 def run_block(hts, wl, dev, time_graph, quick):
     """One 7B decoder block's seven projections (+ the gated-MLP step) at M = 2048 on packed weights
     with Wanda tile maps at 30 % overall sparsity -- per layer and with one global budget -- against
@@ -472,6 +588,8 @@ def main():
 
     Ydd = [torch.empty((M, L.N), dtype=tdt, device=dev) for _ in range(2)]
     n_pf = 10 if args.quick else 50
+    # the hybrid timed like its comparators (best of 3 windows of n_pf launches) for the speed-ups
+    t_step_ll = time_launches(step, n_pf)
     t_dense = time_launches(lambda i: hts.dense_gemm(Xm, Ws[i % n_rot_d], out=Ydd[i % 2]), n_pf)
     # (not in profiling runs: it launches the timed step's kernel on another map)
     t_dense_packed = None if args.quick else time_launches(lambda i: hts.gemm(Xm, pds[i % n_rot_d], out=Ydd[i % 2]), n_pf)
@@ -514,6 +632,10 @@ def main():
     tiles_res = None if args.no_tiles else run_tile_sizes(hts, wl, dev, time_graph, time_launches, args.quick)
     shard_res = None if args.no_shard else run_shard(hts, wl, dev, time_graph, time_launches, args.quick)
     mid_res = None if args.no_mid else run_mid_m(hts, wl, dev, time_graph, args.quick)
+    r13 = None if args.no_13b else run_13b(hts, wl, dev, time_graph, time_launches, args.quick)
+    sweep_res = None if args.no_sweep else run_sweep(hts, wl, dev, time_graph, time_launches, args.quick)
+    dec_res = None if args.no_decompress else run_decompress(hts, wl, dev, time_graph, time_launches, args.quick)
+    peaks = None if args.no_peaks else run_peaks(args.quick)
 
     # ---------------- CPU oracle on the host cores ----------------
     cpu = None
@@ -541,11 +663,12 @@ def main():
         "TFLOP/s": round(tflops, 2),
         "dense_equivalent_TFLOP/s": round(dense_flops / t_step / 1e12, 2),
         "frac_mfma": round(tflops / MFMA_PEAK_TFLOPS[L.dtype], 4),
+        "us_timed_like_comparators": round(t_step_ll * 1e6, 2),
         "dense_same_library_us": round(t_dense * 1e6, 2),
         "dense_same_library_TFLOP/s": round(dense_flops / t_dense / 1e12, 2),
-        "speedup_vs_dense": round(t_dense / t_step, 3),
+        "speedup_vs_dense": round(t_dense / t_step_ll, 3),
         "dense_packed_us": None if t_dense_packed is None else round(t_dense_packed * 1e6, 2),
-        "speedup_vs_dense_packed": None if t_dense_packed is None else round(t_dense_packed / t_step, 3),
+        "speedup_vs_dense_packed": None if t_dense_packed is None else round(t_dense_packed / t_step_ll, 3),
         "torch_matmul_us": round(t_torch * 1e6, 2),
         "torch_matmul_TFLOP/s": round(dense_flops / t_torch / 1e12, 2),
     }
@@ -585,10 +708,21 @@ def main():
         "tile_sizes": tiles_res,
         "shard": shard_res,
         "mid_m": mid_res,
+        "13b": r13,
+        "sweep": sweep_res,
+        "decompress_fallback": dec_res,
+        "measured_peaks": peaks,
         "packed_bytes": packed_bytes,
         "rotation_copies": n_rot,
         "wall_s_timed_region": round(wall, 4),
     }
+    if peaks:
+        # fractions against the measured denominators beside the published ones
+        mp = peaks.get(f"{L.dtype}_dense_TFLOP/s") or peaks.get("bf16_dense_TFLOP/s")
+        line["roofline"]["measured_peak"] = mp
+        line["roofline"]["frac_of_measured_peak"] = round(tflops / mp, 4) if mp else None
+        for d in decode:
+            d["frac_of_measured_hbm"] = round(d["GB/s"] / peaks["hbm_stream_read_GB/s"], 4)
     print(json.dumps(line), flush=True)
 
 

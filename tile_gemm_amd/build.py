@@ -15,10 +15,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhts.so")
+# measured roofline denominators (streaming read, register-operand matrix-core throughput)
+PEAK_LIB = os.path.join(PKG, "libhts_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["hts_api.cpp", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_xr.hip", "wanda.hip",
-           "elementwise.hip"]
+SOURCES = ["hts_api.cpp", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "wanda.hip", "elementwise.hip"]
 
 ARCH = "gfx950"
 COMMON = [
@@ -33,7 +35,6 @@ COMMON = [
 # matrix-core accumulators in VGPRs: dense and sparse instructions then share them without
 # AGPR<->VGPR copies at the type branches (the AGPR file still takes register spills)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-PER_FILE: dict = {}
 
 
 def hipcc() -> str:
@@ -46,25 +47,31 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     # every source, the host API included, is compiled as HIP (it calls the HIP runtime)
-    cmd = [hipcc(), *COMMON, *PER_FILE.get(src, VGPR_FORM), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *VGPR_FORM, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAK_SOURCES], PEAK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAK_LIB}")
     return LIB
 
 

@@ -426,7 +426,6 @@ int prefill_chunk_log2(int bk) {
 }
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s) {
-    if (prefill_xr_applies(a)) return launch_gemm_prefill_xr(a, sparse_path, s);
     if (a.dtype == HTS_FP8_E4M3)   // 128x128 tiles only
         return a.index ? launch3<FP8T, 128, true>(a, sparse_path, s) : launch3<FP8T, 128, false>(a, sparse_path, s);
     return a.dtype == HTS_BF16 ? launch2<BF16T>(a, sparse_path, s) : launch2<F16T>(a, sparse_path, s);

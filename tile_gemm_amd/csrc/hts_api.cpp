@@ -166,25 +166,14 @@ uint64_t split_bytes(int64_t M, int64_t N, int nsplit) {
     return ((uint64_t)nsplit * M * N * 4 + 255) & ~uint64_t(255);
 }
 
-// Workspace of the X panels of the X-in-registers tiled kernel (unsplit products that kernel takes).
-uint64_t xpanel_ws_bytes(int64_t M, int64_t K, int32_t dtype, int bn, bool packed, int nsplit) {
-    if (nsplit > 1 || M <= streaming_max_m(dtype, 128) || !hts::prefill_xr_wanted(M, bn, packed)) return 0;
-    return hts::xpanel_bytes(M, K, dtype);
-}
-
-// Attach the partial-product buffer when the workspace holds it; otherwise run unsplit.  Then the
-// X panels when that kernel applies and the rest of the workspace holds them.
+// Attach the partial-product buffer when the workspace holds it; otherwise run unsplit.
 void attach_split(hts::GemmArgs& a, int nsplit, void* ws, size_t ws_bytes) {
     a.nsplit = 1;
     a.part = nullptr;
-    a.xpanel = nullptr;
     if (nsplit > 1 && ws && ws_bytes >= split_bytes(a.M, a.N, nsplit)) {
         a.nsplit = nsplit;
         a.part = static_cast<float*>(ws);
-        return;
     }
-    const uint64_t xb = xpanel_ws_bytes(a.M, a.K, a.dtype, a.index ? a.bn : 128, a.index != nullptr, 1);
-    if (xb && ws && ws_bytes >= xb) a.xpanel = ws;
 }
 
 hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
@@ -315,10 +304,7 @@ uint64_t gemm_workspace_bytes(const hts_desc* d, int64_t M) {
     // the unpacked weight (tiles of 32), then the parts of a split product
     const int br = (ws || d->bn != 64) ? 128 : 64;
     const int bk = ws ? ((d->K % 128 == 0) ? 128 : 64) : d->bk;   // the unpacked product's slices
-    const int ns = prefill_split(M, d->N, d->K, d->dtype, bk, br);
-    const uint64_t sp = split_bytes(M, d->N, ns);
-    const uint64_t xp = xpanel_ws_bytes(M, d->K, d->dtype, ws ? 128 : d->bn, ws == 0, ns);
-    return ws + (sp > xp ? sp : xp);
+    return ws + split_bytes(M, d->N, prefill_split(M, d->N, d->K, d->dtype, bk, br));
 }
 
 }  // namespace
@@ -511,9 +497,7 @@ hts_status hts_dense_gemm_workspace(int32_t dtype, int64_t M, int64_t N, int64_t
         return fail(HTS_ERR_SHAPE, "M=%lld N=%lld K=%lld (M >= 0, N and K positive)", (long long)M, (long long)N,
                     (long long)K);
     if (!bytes) return fail(HTS_ERR_INVALID_ARG, "bytes is NULL");
-    const int ns = prefill_split(M, N, K, dtype, (K % 128 == 0) ? 128 : 64, 128);
-    const uint64_t sp = split_bytes(M, N, ns), xp = xpanel_ws_bytes(M, K, dtype, 128, false, ns);
-    *bytes = (size_t)(sp > xp ? sp : xp);
+    *bytes = (size_t)split_bytes(M, N, prefill_split(M, N, K, dtype, (K % 128 == 0) ? 128 : 64, 128));
     return ok();
 }
 

@@ -58,16 +58,7 @@ struct GemmArgs {
     // gated output (hts_gemm_silu_mul): Y = silu(G) * (X . W^T), G[M,N] (ldg) in y_dtype, or nullptr
     const void* gate;
     int64_t ldg;
-    // tiled kernel with X in registers: workspace for X rearranged into 16-row panels
-    // (xpanel_bytes(M, K, dtype) bytes), or nullptr (that kernel is then not used)
-    void* xpanel;
 };
-
-// Bytes of X rearranged into 16-row panels: ceil(M / 16) panels of 16 rows x K elements.
-inline uint64_t xpanel_bytes(int64_t M, int64_t K, int32_t dtype) {
-    const uint64_t es = dtype == HTS_FP8_E4M3 ? 1 : 2;
-    return (((uint64_t)(M + 15) / 16) * 16 * (uint64_t)K * es + 255) & ~uint64_t(255);
-}
 
 enum SparsePath { SPARSE_SMFMAC = 0, SPARSE_DECOMPRESS = 1 };
 
@@ -85,12 +76,6 @@ hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int
 // Tiled kernel (one tile row x 128 X rows per workgroup); with a.nsplit > 1 it also launches the
 // fixed-order sum of the partial products into Y.
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s);
-// The tiled kernel with X in registers (one tile row x 256 X rows per workgroup): whether it takes
-// this product (unsplit; 128-row tiles or a row-major W), and its launch.
-bool prefill_xr_applies(const GemmArgs& a);
-// Whether that kernel would take an unsplit product of this shape (it then wants the X panels).
-bool prefill_xr_wanted(int64_t M, int32_t bn, bool packed);
-hipError_t launch_gemm_prefill_xr(const GemmArgs& a, int sparse_path, hipStream_t s);
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the
 // tiled kernel holds the index records of one tile row in LDS.
 constexpr int kMaxTileColsPerRow = 256;

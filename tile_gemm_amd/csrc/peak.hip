@@ -1,0 +1,100 @@
+// Measured roofline denominators for MI355X (gfx950): an HBM streaming read, and matrix-core
+// instruction throughput with operands in registers (dense MFMA and sparse SMFMAC, 16-bit and
+// 8-bit).  The product kernels' fractions are reported against these as well as against the
+// published peaks.  Exported through include/hts_peak.h; built as libhts_peak.so.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "hts_peak.h"
+
+namespace {
+
+using namespace hts;
+
+// Streaming read: every thread reads 16-byte chunks grid-stride (consecutive lanes on
+// consecutive chunks, four loads in flight), non-temporal; the xor of what it read goes to
+// `sink` only if it equals a value no input produces, so the loads are kept.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, uint64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+    const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (x == 0x9E3779B9u) sink[0] = x;
+}
+
+// Matrix-core throughput: each wave issues `iters` rounds of 8 independent instructions on register
+// operands (no memory traffic in the loop); the accumulators are stored once so nothing is removed.
+enum { KIND_BF16_DENSE = 0, KIND_BF16_SPARSE = 1, KIND_FP8_DENSE = 2, KIND_FP8_SPARSE = 3 };
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ out) {
+    const uint32_t lane = threadIdx.x & 63;
+    u32x4 a = {lane * 2654435761u, lane + 1u, lane ^ 0x3C3C3C3Cu, 0x3F803F80u};
+    u32x8 b = {lane, lane * 3u, 0x3F803F80u, lane + 7u, 0x3F003F00u, lane * 5u, 0x3E803E80u, lane + 11u};
+    const uint32_t idx = 0x4E4E4E4Eu;   // valid 2:4 codes (positions 2,3 / 0,1 ... of every group)
+    f32x4 acc[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (KIND == KIND_BF16_DENSE) acc[r] = mfma_dense<BF16T>(a, lo4(b), acc[r]);
+            else if constexpr (KIND == KIND_BF16_SPARSE) acc[r] = mfma_sparse<BF16T, 0>(a, b, idx, acc[r]);
+            else if constexpr (KIND == KIND_FP8_DENSE)
+                acc[r] = mfma_fp8_dense32(uint2{a[0], a[1]}, uint2{b[0], b[1]}, acc[r]);
+            else acc[r] = mfma_fp8_sparse(a, b, idx, acc[r]);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s += acc[r][0] + acc[r][1] + acc[r][2] + acc[r][3];
+    out[(uint64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hts_peak_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int blocks, void* stream) {
+    if (!src || !sink || bytes < 16 || blocks <= 0) return 1;
+    stream_read_kernel<<<dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const u32x4*>(src), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+int hts_peak_mfma(int kind, int iters, int blocks, float* out, void* stream) {
+    if (!out || iters <= 0 || blocks <= 0) return 1;
+    const dim3 g((unsigned)blocks), t(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (kind) {
+        case KIND_BF16_DENSE: mfma_loop_kernel<KIND_BF16_DENSE><<<g, t, 0, s>>>(iters, out); break;
+        case KIND_BF16_SPARSE: mfma_loop_kernel<KIND_BF16_SPARSE><<<g, t, 0, s>>>(iters, out); break;
+        case KIND_FP8_DENSE: mfma_loop_kernel<KIND_FP8_DENSE><<<g, t, 0, s>>>(iters, out); break;
+        case KIND_FP8_SPARSE: mfma_loop_kernel<KIND_FP8_SPARSE><<<g, t, 0, s>>>(iters, out); break;
+        default: return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+double hts_peak_mfma_flops_per_instruction(int kind) {
+    // algorithmic flops: 2 x (kept multiply-adds); a sparse instruction keeps half of its dense K
+    switch (kind) {
+        case KIND_BF16_DENSE: return 2.0 * 16 * 16 * 32;
+        case KIND_BF16_SPARSE: return 2.0 * 16 * 16 * 32;    // 16x16x64, two of every four kept
+        case KIND_FP8_DENSE: return 2.0 * 16 * 16 * 32;
+        case KIND_FP8_SPARSE: return 2.0 * 16 * 16 * 64;     // 16x16x128, two of every four kept
+        default: return 0.0;
+    }
+}
+
+}  // extern "C"

@@ -54,8 +54,8 @@ struct Layout {
     static constexpr int WOFF = BM * 128;
     static constexpr int MOFF = WOFF + NG * kGroupBytes;
     static constexpr int STAGE = MOFF + NG * MGB;
-    static constexpr int SINK = NSTAGE * STAGE;              // target of padding copies / writes (2 KiB)
-    static constexpr int LIST = SINK + 2048;                 // ordered tile list: {val_off, meta_off}
+    static constexpr int SINK = NSTAGE * STAGE;              // target of the padding copies
+    static constexpr int LIST = SINK + 1024;                 // ordered tile list: {val_off, meta_off}
     static constexpr int LCOL = LIST + kMaxTileCols * 8;     // ... and the tile column of each entry
     static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // dense tiles of each chunk (bytes)
     static constexpr int TOTAL = WCNT + 64;
@@ -111,7 +111,7 @@ struct Ctx {
     rsrc_t mr;                          // codes of the tile row from its first tile
     uint32_t vbase, mbase;              // first value / code word of the tile row
     uint32_t xso;                       // bytes: tile column and slice of the X copies of a slice
-    uint32_t xvo[XJ > 0 ? XJ : 1];      // per-lane byte offsets: X jobs (none when X bypasses LDS)
+    uint32_t xvo[XJ];                   // per-lane byte offsets: X jobs
     uint32_t dvo[JPG];                  // dense group jobs (row * BK + chunk, or row * ldw + chunk)
     uint32_t svo;                       // 2:4 values job
     uint32_t mvo;                       // 2:4 codes job

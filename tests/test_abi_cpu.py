@@ -272,3 +272,20 @@ def test_noalloc_rejects_before_any_device_call():
     st = L.hts_gemm_noalloc(ctypes.byref(desc), 16, 16, 16, -1, 16, 4096, 16, 11008, hts.HTS_F32, None)
     assert st == 3
     assert L.hts_gemm_noalloc(None, 16, 16, 16, 1, 16, 4096, 16, 11008, hts.HTS_F32, None) == 1
+
+
+def test_peak_library_exports_every_declared_symbol():
+    # libhts_peak.so: the measured roofline denominators declared in include/hts_peak.h
+    import tile_gemm_amd.peak as peak
+    text = open(os.path.join(ROOT, "include", "hts_peak.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:int|double)\s+(hts_\w+)\s*\(", text, re.M)))
+    L = peak.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(peak.EXPORTED) == names
+    # algorithmic flops per instruction: kept multiply-adds only (sparse = half its dense K)
+    assert [L.hts_peak_mfma_flops_per_instruction(k) for k in range(4)] == [16384.0, 16384.0, 16384.0, 32768.0]
+    assert L.hts_peak_mfma_flops_per_instruction(9) == 0.0
+    # invalid arguments are rejected before any launch
+    assert L.hts_peak_mfma(0, 0, 1, 16, None) == 1
+    assert L.hts_peak_stream_read(None, 1024, 16, 1, None) == 1

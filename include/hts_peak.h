@@ -29,6 +29,7 @@ int hts_peak_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int bl
  * `iters` rounds of 8 independent instructions of `kind`:
  *   0: v_mfma_f32_16x16x32_bf16      1: v_smfmac_f32_16x16x64_bf16 (2:4)
  *   2: v_mfma_f32_16x16x32_fp8_fp8   3: v_smfmac_f32_16x16x128_fp8_fp8 (2:4)
+ *   4: v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 operands, unit scales)
  * out: device float[blocks * 256] (one value per thread, kept so the work is not removed). */
 int hts_peak_mfma(int kind, int iters, int blocks, float* out, void* stream);
 

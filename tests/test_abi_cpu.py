@@ -284,7 +284,7 @@ def test_peak_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
     assert sorted(peak.EXPORTED) == names
     # algorithmic flops per instruction: kept multiply-adds only (sparse = half its dense K)
-    assert [L.hts_peak_mfma_flops_per_instruction(k) for k in range(4)] == [16384.0, 16384.0, 16384.0, 32768.0]
+    assert [L.hts_peak_mfma_flops_per_instruction(k) for k in range(5)] == [16384.0, 16384.0, 16384.0, 32768.0, 65536.0]
     assert L.hts_peak_mfma_flops_per_instruction(9) == 0.0
     # invalid arguments are rejected before any launch
     assert L.hts_peak_mfma(0, 0, 1, 16, None) == 1

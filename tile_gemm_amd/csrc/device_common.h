@@ -101,8 +101,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // shared by A and B gives the same product, so the data keeps the chunk layout of the sparse
 // 16x16x128 instruction below (lane group g: 16-byte chunks g and 4 + g of a 128-byte row) and
 // each 16-byte chunk feeds two of these instructions, one per 8-byte half: every k is used once.
-// (The 16x16x128 dense form, with unit block scales, gave wrong sums on gfx950 when its
-// accumulator was copied between dependent products, so it is not used.)
 __device__ __forceinline__ f32x4 mfma_fp8_dense32(uint2 a, uint2 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)__builtin_bit_cast(uint64_t, a),
                                                       (long)__builtin_bit_cast(uint64_t, b), c, 0, 0, 0);
@@ -112,6 +110,19 @@ template <>
 __device__ __forceinline__ f32x4 mfma_dense<FP8T>(u32x4 a, u32x4 b, f32x4 c) {
     c = mfma_fp8_dense32(uint2{a[0], a[1]}, uint2{b[0], b[1]}, c);
     return mfma_fp8_dense32(uint2{a[2], a[3]}, uint2{b[2], b[3]}, c);
+}
+
+// Dense 16x16x128 8-bit MFMA (the f8f6f4 form, E4M3 for A and B, unit block scales: E8M0 exponent
+// 127): lane (i + 16g) holds 32 values of row i of A and of column i of B.  Fed with the chunk
+// layout of the sparse 16x16x128 instruction below (16-byte chunks g and 4 + g of the 128-byte row)
+// for both operands, every k of the 128 is used once; one instruction does the work of four
+// 16x16x32 ones at twice their rate.  It takes twice the cycles of the sparse instruction below:
+// where one accumulator is written by both on the two arms of a branch, the compiler has read it
+// after the join with the sparse instruction's wait states (stale sums), so callers keep the two
+// in separate loops or separate accumulators.
+__device__ __forceinline__ f32x4 mfma_fp8_dense128(u32x8 a, u32x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                            c, 0, 0, 0, 127, 0, 127);
 }
 
 // Sparse 16x16x128 8-bit SMFMAC: A lane (i + 16h) holds the 16 stored values of row i for dense

@@ -53,6 +53,20 @@ __device__ __forceinline__ void compute_dense(f32x4 (&acc)[NBI][NBJ], const uint
     const int a1 = PANEL ? 16 * (16 * c1 + i) : i * 128 + 16 * (c1 ^ ((i >> 1) & 7));
     u32x8 Bx[NBJ];
     load_x<SP, NBJ>(Bx, xs, lane);
+    if constexpr (Elem<T>::bytes == 1) {
+        // 8-bit: both chunks of a row block form one 16x16x128 operand (one instruction per block)
+        u32x4 A[2][NBI];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int b = 0; b < NBI; ++b) A[u][b] = ld16(ws + b * 2048 + (u ? a1 : a0));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NBI; ++b)
+#pragma unroll
+            for (int bj = 0; bj < NBJ; ++bj) acc[b][bj] = mfma_fp8_dense128(cat8(A[0][b], A[1][b]), Bx[bj], acc[b][bj]);
+        return;
+    }
     if constexpr (NBI == 4) {
         // every fragment of the slice is read before the first product: one LDS wait per slice
         u32x4 A[2][4];

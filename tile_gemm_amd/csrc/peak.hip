@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 
 // Matrix-core throughput: each wave issues `iters` rounds of 8 independent instructions on register
 // operands (no memory traffic in the loop); the accumulators are stored once so nothing is removed.
-enum { KIND_BF16_DENSE = 0, KIND_BF16_SPARSE = 1, KIND_FP8_DENSE = 2, KIND_FP8_SPARSE = 3 };
+enum { KIND_BF16_DENSE = 0, KIND_BF16_SPARSE = 1, KIND_FP8_DENSE = 2, KIND_FP8_SPARSE = 3, KIND_FP8_DENSE128 = 4 };
 
 template <int KIND>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ out) {
@@ -52,6 +52,7 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
             else if constexpr (KIND == KIND_BF16_SPARSE) acc[r] = mfma_sparse<BF16T, 0>(a, b, idx, acc[r]);
             else if constexpr (KIND == KIND_FP8_DENSE)
                 acc[r] = mfma_fp8_dense32(uint2{a[0], a[1]}, uint2{b[0], b[1]}, acc[r]);
+            else if constexpr (KIND == KIND_FP8_DENSE128) acc[r] = mfma_fp8_dense128(cat8(a, a), b, acc[r]);
             else acc[r] = mfma_fp8_sparse(a, b, idx, acc[r]);
         }
     }
@@ -81,6 +82,7 @@ int hts_peak_mfma(int kind, int iters, int blocks, float* out, void* stream) {
         case KIND_BF16_SPARSE: mfma_loop_kernel<KIND_BF16_SPARSE><<<g, t, 0, s>>>(iters, out); break;
         case KIND_FP8_DENSE: mfma_loop_kernel<KIND_FP8_DENSE><<<g, t, 0, s>>>(iters, out); break;
         case KIND_FP8_SPARSE: mfma_loop_kernel<KIND_FP8_SPARSE><<<g, t, 0, s>>>(iters, out); break;
+        case KIND_FP8_DENSE128: mfma_loop_kernel<KIND_FP8_DENSE128><<<g, t, 0, s>>>(iters, out); break;
         default: return 1;
     }
     return hipGetLastError() == hipSuccess ? 0 : 8;
@@ -93,6 +95,7 @@ double hts_peak_mfma_flops_per_instruction(int kind) {
         case KIND_BF16_SPARSE: return 2.0 * 16 * 16 * 32;    // 16x16x64, two of every four kept
         case KIND_FP8_DENSE: return 2.0 * 16 * 16 * 32;
         case KIND_FP8_SPARSE: return 2.0 * 16 * 16 * 64;     // 16x16x128, two of every four kept
+        case KIND_FP8_DENSE128: return 2.0 * 16 * 16 * 128;
         default: return 0.0;
     }
 }

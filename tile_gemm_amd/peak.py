@@ -10,7 +10,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhts_peak.so")
-KINDS = {"bf16_dense": 0, "bf16_sparse24": 1, "fp8_dense": 2, "fp8_sparse24": 3}
+KINDS = {"bf16_dense": 0, "bf16_sparse24": 1, "fp8_dense": 2, "fp8_sparse24": 3, "fp8_dense_k128": 4}
 _SIGS = {
     "hts_peak_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                             ctypes.c_void_p]),

@@ -378,6 +378,14 @@ def run_peaks(quick):
     out = {"hbm_stream_read_GB/s": round(peak.stream_read_gbs(reps=2 if quick else 5), 1)}
     for k in peak.KINDS:
         out[f"{k}_TFLOP/s"] = round(peak.mfma_tflops(k, reps=2 if quick else 5), 1)
+    # on-chip paths per CU, in bytes per cycle at the clock the 16-bit matrix cores ran at above
+    # (1,024 flops per cycle per SIMD, 4 SIMDs per CU)
+    clk = out["bf16_dense_TFLOP/s"] * 1e12 / (1024 * 4 * 256)
+    out["clock_from_mfma_GHz"] = round(clk / 1e9, 3)
+    for m in peak.ONCHIP:
+        g = peak.onchip_gbs(m, reps=2 if quick else 5)
+        out[f"{m}_GB/s"] = round(g, 1)
+        out[f"{m}_B_per_clk_per_CU"] = round(g * 1e9 / 256 / clk, 1)
     return out
 
 

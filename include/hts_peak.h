@@ -33,6 +33,15 @@ int hts_peak_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int bl
  * out: device float[blocks * 256] (one value per thread, kept so the work is not removed). */
 int hts_peak_mfma(int kind, int iters, int blocks, float* out, void* stream);
 
+/* On-chip copy and read paths: `blocks` workgroups of 4 waves, each reading its own 64 KiB window
+ * of src (window = workgroup index modulo bytes / 65536; keep bytes small enough to stay in L2,
+ * e.g. 2 MiB) `iters` times, 16 bytes per lane:
+ *   mode 0: global -> LDS by the direct copy (buffer load to LDS), the tiled product's copy path;
+ *   mode 1: global -> registers;
+ *   mode 2: LDS -> registers (16-byte LDS reads; src is not read).
+ * Bytes moved = blocks x iters x 65536.  src: device memory of `bytes` >= 65536; sink as above. */
+int hts_peak_onchip(int mode, const void* src, uint64_t bytes, int iters, int blocks, uint32_t* sink, void* stream);
+
 /* Algorithmic flops of one instruction of `kind`: 2 x the multiply-adds of kept weights (a sparse
  * instruction keeps two of every four of its dense K); 0 for an unknown kind. */
 double hts_peak_mfma_flops_per_instruction(int kind);

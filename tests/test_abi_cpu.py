@@ -289,3 +289,6 @@ def test_peak_library_exports_every_declared_symbol():
     # invalid arguments are rejected before any launch
     assert L.hts_peak_mfma(0, 0, 1, 16, None) == 1
     assert L.hts_peak_stream_read(None, 1024, 16, 1, None) == 1
+    assert L.hts_peak_onchip(0, None, 1 << 21, 1, 1, 16, None) == 1
+    assert L.hts_peak_onchip(0, 16, 1024, 1, 1, 16, None) == 1
+    assert L.hts_peak_onchip(0, 16, 1 << 21, 0, 1, 16, None) == 1

@@ -62,6 +62,60 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
     out[(uint64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// On-chip paths of a CU.  Every workgroup (4 waves) reads its own 64 KiB window of `src` (window
+// blockIdx % nwin; the windows stay in L2 after the first pass) over and over, 16 bytes per lane,
+// 1 KiB per wave instruction:
+//   MODE 0: into LDS by the direct global-to-LDS copy (buffer load to LDS);
+//   MODE 1: into registers (their xor is kept);
+//   MODE 2: no global traffic: 16-byte LDS reads of the workgroup's 32 KiB of LDS (xor kept).
+// The window offset goes through an empty asm each pass, so no load is hoisted out of the loop.
+template <int MODE>
+__global__ __launch_bounds__(256) void onchip_kernel(const uint8_t* __restrict__ src, uint32_t nwin, int iters,
+                                                     uint32_t* __restrict__ sink) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[32768];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const uint8_t* win = src + (uint64_t)(blockIdx.x % nwin) * 65536;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    if constexpr (MODE == 0) {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(win), (short)0, 65536, 0x00020000);
+        typedef __attribute__((address_space(3))) void lds_void;
+        lds_void* dst = (lds_void*)((__attribute__((address_space(3))) uint8_t*)lds + wave * 8192);
+        for (int it = 0; it < iters; ++it) {
+            uint32_t base = 0;
+            asm volatile("" : "+s"(base));
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)((__attribute__((address_space(3))) uint8_t*)dst +
+                                                                       1024 * (j & 7)),
+                                                         16, tid * 16, base + 4096 * j, 0, 0);
+            // keep at most 32 copies in flight per wave
+            __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (15 << 8));
+        }
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+    } else if constexpr (MODE == 1) {
+        for (int it = 0; it < iters; ++it) {
+            uint32_t base = 0;
+            asm volatile("" : "+v"(base));
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc ^= *reinterpret_cast<const u32x4*>(win + base + 4096 * j + 16 * tid);
+        }
+    } else {
+        for (int i = tid; i < 2048; i += 256) reinterpret_cast<u32x4*>(lds)[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+        __syncthreads();
+        for (int it = 0; it < iters; ++it) {
+            uint32_t base = 0;
+            asm volatile("" : "+v"(base));
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc ^= *reinterpret_cast<const u32x4*>(lds + ((base + 4096 * (j & 7) + 16 * tid) & 32767));
+        }
+    }
+    const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (x == 0x9E3779B9u) sink[0] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,6 +137,21 @@ int hts_peak_mfma(int kind, int iters, int blocks, float* out, void* stream) {
         case KIND_FP8_DENSE: mfma_loop_kernel<KIND_FP8_DENSE><<<g, t, 0, s>>>(iters, out); break;
         case KIND_FP8_SPARSE: mfma_loop_kernel<KIND_FP8_SPARSE><<<g, t, 0, s>>>(iters, out); break;
         case KIND_FP8_DENSE128: mfma_loop_kernel<KIND_FP8_DENSE128><<<g, t, 0, s>>>(iters, out); break;
+        default: return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 8;
+}
+
+int hts_peak_onchip(int mode, const void* src, uint64_t bytes, int iters, int blocks, uint32_t* sink, void* stream) {
+    if (!src || !sink || bytes < 65536 || iters <= 0 || blocks <= 0) return 1;
+    const uint32_t nwin = (uint32_t)((bytes >> 16) < 0xFFFFFFFFull ? (bytes >> 16) : 0xFFFFFFFFull);
+    const dim3 g((unsigned)blocks), t(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t* p = static_cast<const uint8_t*>(src);
+    switch (mode) {
+        case 0: onchip_kernel<0><<<g, t, 0, s>>>(p, nwin, iters, sink); break;
+        case 1: onchip_kernel<1><<<g, t, 0, s>>>(p, nwin, iters, sink); break;
+        case 2: onchip_kernel<2><<<g, t, 0, s>>>(p, nwin, iters, sink); break;
         default: return 1;
     }
     return hipGetLastError() == hipSuccess ? 0 : 8;

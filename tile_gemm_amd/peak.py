@@ -16,7 +16,10 @@ _SIGS = {
                                             ctypes.c_void_p]),
     "hts_peak_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "hts_peak_mfma_flops_per_instruction": (ctypes.c_double, [ctypes.c_int]),
+    "hts_peak_onchip": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]),
 }
+ONCHIP = {"l2_to_lds": 0, "l2_to_vgpr": 1, "lds_read": 2}
 EXPORTED = tuple(_SIGS)
 _lib = None
 
@@ -73,6 +76,18 @@ def mfma_tflops(kind: str, iters: int = 256, reps: int = 5, device: str = "cuda:
     t = _time(lambda: _check(lib().hts_peak_mfma(k, iters, blocks, out.data_ptr(), stream)), reps)
     per = lib().hts_peak_mfma_flops_per_instruction(k)
     return blocks * 4 * iters * 8 * per / t / 1e12
+
+
+def onchip_gbs(mode: str, iters: int = 64, reps: int = 5, device: str = "cuda:0") -> float:
+    """Chip-wide GB/s of one on-chip path (`ONCHIP`), 4 workgroups of 4 waves per CU, sources in L2."""
+    m = ONCHIP[mode]
+    nbytes, blocks = 2 << 20, 256 * 4
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=device)
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
+    stream = torch.cuda.current_stream().cuda_stream
+    t = _time(lambda: _check(lib().hts_peak_onchip(m, src.data_ptr(), nbytes, iters, blocks, sink.data_ptr(), stream)),
+              reps)
+    return blocks * iters * 65536 / t / 1e9
 
 
 def _check(status: int) -> None:

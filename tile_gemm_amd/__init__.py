@@ -273,9 +273,19 @@ class PackedWeight:
     def packed_bytes(self) -> int:
         return int(self.sizes["values_bytes"] + self.sizes["meta_bytes"] + self.sizes["index_bytes"])
 
+    def save(self, path: str) -> None:
+        """Write this packed weight to a versioned, checksummed file (see ``packed_io``)."""
+        from . import packed_io
+        packed_io.save(self, path)
 
-def _device_buffers(desc: hts_desc, tile_map: np.ndarray, device):
-    index_np, sizes = hts_pack_plan(desc, tile_map)
+    @staticmethod
+    def load(path: str, device="cuda") -> "PackedWeight":
+        """Read a file written by ``save`` onto ``device`` without packing again."""
+        from . import packed_io
+        return packed_io.load(path, device)
+
+
+def _buffers_for(desc: hts_desc, sizes: dict, index_np: np.ndarray, device):
     index = torch.from_numpy(index_np.view(np.int32).copy()).to(device)
     if desc.dtype == HTS_FP8_E4M3:
         values = torch.empty(max(sizes["values_bytes"], 16), dtype=torch.uint8, device=device)
@@ -283,6 +293,11 @@ def _device_buffers(desc: hts_desc, tile_map: np.ndarray, device):
         values = torch.empty(max(sizes["values_bytes"] // 2, 8), dtype=torch.int16, device=device)
     meta = torch.empty(max(sizes["meta_bytes"] // 4, 4), dtype=torch.int32, device=device)
     return index, values, meta, sizes
+
+
+def _device_buffers(desc: hts_desc, tile_map: np.ndarray, device):
+    index_np, sizes = hts_pack_plan(desc, tile_map)
+    return _buffers_for(desc, sizes, index_np, device)
 
 
 def pack(W: torch.Tensor, tile_map: np.ndarray, bn: int, bk: int,

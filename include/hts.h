@@ -22,13 +22,25 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
  *     work is enqueued on it and the call returns without waiting; results are
  *     ready when the stream reaches that point.
- *   - The caller owns every buffer.  The library allocates no device memory,
- *     frees nothing and keeps no pointer after a call returns.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     (outside HTS_DEBUG mode, below), frees nothing and keeps no pointer after
+ *     a call returns.
  *   - Every argument check is made on the host before anything is enqueued: a
  *     failing call has no side effect and returns a status (details in
  *     hts_last_error()).  Buffer sizes and the validity of device pointers
- *     cannot be checked and are preconditions.
+ *     cannot be checked cheaply and are preconditions.
  *   - Calls are thread-safe; calls that write the same buffers race.
+ *   - Debug mode, environment variable HTS_DEBUG=1 (any value but "0"): before
+ *     anything is enqueued, each device buffer a call touches must lie inside
+ *     one device allocation of this process with the bytes the call needs
+ *     (else HTS_ERR_INVALID_ARG for memory that is not device memory,
+ *     HTS_ERR_SHAPE for a short buffer), and a device tile index is checked
+ *     by a small kernel: every record must equal the prefix sums hts_pack_plan
+ *     writes (else HTS_ERR_MAP, naming the first bad record); the values and
+ *     codes buffers must then hold the sizes that index implies.  The index
+ *     check synchronises the stream (it is refused during graph capture) and
+ *     keeps one 24-byte result buffer per device, allocated on first use.
+ *     hts_gemm_noalloc runs none of these checks.
  */
 #ifndef HTS_H
 #define HTS_H

@@ -73,6 +73,89 @@ hts_status hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
+// HTS_DEBUG=1 (any value but "0"): before anything is enqueued, every device buffer a call will
+// touch is checked to lie inside one allocation of this process (hipMemGetAddressRange) with the
+// bytes the call needs, and a device tile index is checked by a small kernel (its records must be
+// the prefix sums of hts_pack_plan: record t = record t-1 plus that tile's stored size), which
+// also yields the sizes of the values and codes the index implies.  The checks synchronise the
+// stream, so they are refused during graph capture.  hts_gemm_noalloc runs none of them.
+bool debug_mode() {
+    const char* v = getenv("HTS_DEBUG");
+    return v && *v && strcmp(v, "0") != 0;
+}
+
+// Bytes of a row-major block of `rows` rows of `cols` elements of `es` bytes, leading dimension ld.
+uint64_t block_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
+    return rows > 0 ? (uint64_t)((rows - 1) * ld + cols) * (uint64_t)es : 0;
+}
+
+hts_status debug_range(const void* p, uint64_t bytes, const char* name) {
+    if (!p || bytes == 0) return HTS_OK;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    const hipError_t e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+    if (e != hipSuccess || !base) {
+        (void)hipGetLastError();   // leave no stale error for the next launch check
+        return fail(HTS_ERR_INVALID_ARG, "HTS_DEBUG: %s is not device memory of this process", name);
+    }
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    if (q < lo || q - lo + bytes > size)
+        return fail(HTS_ERR_SHAPE, "HTS_DEBUG: %s needs %llu bytes; its allocation ends %llu bytes after it", name,
+                    (unsigned long long)bytes, (unsigned long long)(q >= lo && q - lo <= size ? size - (q - lo) : 0));
+    return HTS_OK;
+}
+
+// Per-device result buffer of the index check (allocated on first use in debug mode).
+class DebugIndex {
+  public:
+    static constexpr int kMaxDevices = 64;
+    hts_status run(const hts_desc* d, const hts_tile* index, hipStream_t s, uint64_t* values_bytes,
+                   uint64_t* meta_bytes) {
+        const int64_t T = (d->N / d->bn) * (d->K / d->bk);
+        hts_status st = debug_range(index, 16 * (uint64_t)T, "index");
+        if (st) return st;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+            return fail(HTS_ERR_INVALID_ARG, "HTS_DEBUG checks synchronise the stream and cannot run during graph capture");
+        std::lock_guard<std::mutex> lock(mu_);
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(HTS_ERR_HIP, "HTS_DEBUG: no current device");
+        if (!buf_[dev] && (e = hipMalloc(reinterpret_cast<void**>(&buf_[dev]), sizeof(hts::IndexCheck))) != hipSuccess)
+            return hip_status(e, "HTS_DEBUG: index check buffer");
+        const hts::IndexCheck init = {0u, 0xFFFFFFFFu, 0u, 0u};
+        hts::IndexCheck r{};
+        if ((e = hipMemcpyAsync(buf_[dev], &init, sizeof init, hipMemcpyHostToDevice, s)) != hipSuccess ||
+            (e = hts::launch_index_check(*d, index, buf_[dev], s)) != hipSuccess ||
+            (e = hipMemcpyAsync(&r, buf_[dev], sizeof r, hipMemcpyDeviceToHost, s)) != hipSuccess ||
+            (e = hipStreamSynchronize(s)) != hipSuccess)
+            return hip_status(e, "HTS_DEBUG: index check");
+        if (r.bad)
+            return fail(HTS_ERR_MAP, "HTS_DEBUG: %u tile index records are inconsistent with the plan (first: record %u)",
+                        r.bad, r.first_bad);
+        *values_bytes = r.values_end * (uint64_t)elem_bytes(d->dtype);
+        *meta_bytes = 4 * r.meta_end;
+        return HTS_OK;
+    }
+
+  private:
+    std::mutex mu_;
+    hts::IndexCheck* buf_[kMaxDevices] = {};
+};
+DebugIndex g_debug_index;
+
+// The packed weight's buffers: the index, then the values and codes it implies.
+hts_status debug_packed(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta,
+                        hipStream_t s, bool writes) {
+    uint64_t vb = 0, mb = 0;
+    hts_status st = g_debug_index.run(d, index, s, &vb, &mb);
+    if (st) return st;
+    if ((st = debug_range(values, vb, writes ? "values (output)" : "values"))) return st;
+    if (mb && !meta) return fail(HTS_ERR_INVALID_ARG, "HTS_DEBUG: the index has 2:4 tiles but meta is NULL");
+    return debug_range(meta, mb, writes ? "meta (output)" : "meta");
+}
+
+
 // Sparse-tile path: SMFMAC unless HTS_SPARSE_PATH=decompress.
 int sparse_path() {
     const char* v = getenv("HTS_SPARSE_PATH");
@@ -197,7 +280,7 @@ hts_status run_gemm(const hts::GemmArgs& a, hipStream_t s) {
 // hts_gemm and hts_gemm_silu_mul (gate: G[M,N] in y_dtype, or nullptr)
 hts_status gemm_impl(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta, int64_t M,
                      const void* X, int64_t ldx, const void* gate, int64_t ldg, void* Y, int64_t ldy, int32_t y_dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream, bool debug_ok = true) {
     hts_status st = check_desc(d);
     if (st) return st;
     if (M < 0) return fail(HTS_ERR_SHAPE, "M=%lld is negative", (long long)M);
@@ -208,6 +291,15 @@ hts_status gemm_impl(const hts_desc* d, const hts_tile* index, const void* value
     if (M == 0) return ok();
     if ((st = check_ptr(X, "X")) || (st = check_ptr(Y, "Y"))) return st;
     if (gate && (st = check_ptr(gate, "G"))) return st;
+    if (debug_ok && debug_mode()) {
+        const int ys = y_dtype == HTS_F32 ? 4 : 2;
+        if ((st = debug_packed(d, index, values, meta, static_cast<hipStream_t>(stream), false)) ||
+            (st = debug_range(X, block_bytes(M, d->K, ldx, elem_bytes(d->dtype)), "X")) ||
+            (st = debug_range(Y, block_bytes(M, d->N, ldy, ys), "Y")) ||
+            (st = debug_range(gate, block_bytes(M, d->N, ldg, ys), "G")) ||
+            (st = debug_range(workspace, workspace_bytes, "workspace")))
+            return st;
+    }
     const uint64_t ws = unpack_workspace_bytes(d, M);
     if (ws) {
         if (!workspace || workspace_bytes < ws)
@@ -374,6 +466,11 @@ hts_status hts_pack(const hts_desc* d, const hts_tile* index, const void* W, int
     if (col_scale && (reinterpret_cast<uintptr_t>(col_scale) & 3u))
         return fail(HTS_ERR_ALIGN, "col_scale is not 4-byte aligned");
     if ((st = check_ld(ldw, d->K, ld_mult(d->dtype), "ldw"))) return st;
+    if (debug_mode() &&
+        ((st = debug_packed(d, index, values, meta, static_cast<hipStream_t>(stream), true)) ||
+         (st = debug_range(W, block_bytes(d->N, d->K, ldw, elem_bytes(d->dtype)), "W")) ||
+         (st = debug_range(col_scale, 4 * (uint64_t)d->K, "col_scale"))))
+        return st;
     return hip_status(hts::launch_pack(*d, index, static_cast<const uint16_t*>(W), ldw, col_scale,
                                        static_cast<uint16_t*>(values), meta, static_cast<hipStream_t>(stream)),
                       "pack kernel launch");
@@ -392,6 +489,12 @@ hts_status hts_pack_masked(const hts_desc* d, const hts_tile* index, const void*
         return fail(HTS_ERR_ALIGN, "malformed_groups is not 4-byte aligned");
     if ((st = check_ld(ldw, d->K, ld_mult(d->dtype), "ldw"))) return st;
     if ((st = check_ld(ldm, d->K, 16, "ldm"))) return st;
+    if (debug_mode() &&
+        ((st = debug_packed(d, index, values, meta, static_cast<hipStream_t>(stream), true)) ||
+         (st = debug_range(W, block_bytes(d->N, d->K, ldw, elem_bytes(d->dtype)), "W")) ||
+         (st = debug_range(mask, block_bytes(d->N, d->K, ldm, 1), "mask")) ||
+         (st = debug_range(malformed_groups, 4, "malformed_groups"))))
+        return st;
     return hip_status(hts::launch_pack_masked(*d, index, static_cast<const uint16_t*>(W), ldw, mask, ldm,
                                               malformed_groups, static_cast<uint16_t*>(values), meta,
                                               static_cast<hipStream_t>(stream)),
@@ -406,6 +509,10 @@ hts_status hts_unpack(const hts_desc* d, const hts_tile* index, const void* valu
         return st;
     if (meta && !aligned16(meta)) return fail(HTS_ERR_ALIGN, "meta is not 16-byte aligned");
     if ((st = check_ld(ldw, d->K, ld_mult(d->dtype), "ldw"))) return st;
+    if (debug_mode() &&
+        ((st = debug_packed(d, index, values, meta, static_cast<hipStream_t>(stream), false)) ||
+         (st = debug_range(W_out, block_bytes(d->N, d->K, ldw, elem_bytes(d->dtype)), "W_out"))))
+        return st;
     return hip_status(hts::launch_unpack(*d, index, static_cast<const uint16_t*>(values), meta,
                                          static_cast<uint16_t*>(W_out), ldw, static_cast<hipStream_t>(stream)),
                       "unpack kernel launch");
@@ -441,7 +548,7 @@ hts_status hts_gemm_noalloc(const hts_desc* d, const hts_tile* index, const void
     void* ws = nullptr;
     if (need > 0 && (st = g_scratch.get(&ws))) return st;
     return gemm_impl(d, index, values, meta, M, X, ldx, nullptr, 0, Y, ldy, y_dtype, ws, ws ? kScratchBytes : 0,
-                     stream);
+                     stream, false);
 }
 
 hts_status hts_gemm_silu_mul(const hts_desc* d, const hts_tile* index, const void* values, const uint32_t* meta,
@@ -473,6 +580,12 @@ hts_status hts_dense_gemm(int32_t dtype, int64_t M, int64_t N, int64_t K, const 
     if (M == 0) return ok();
     if ((st = check_ptr(X, "X")) || (st = check_ptr(W, "W")) || (st = check_ptr(Y, "Y"))) return st;
     if (workspace && !aligned16(workspace)) return fail(HTS_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (debug_mode() &&
+        ((st = debug_range(X, block_bytes(M, K, ldx, elem_bytes(dtype)), "X")) ||
+         (st = debug_range(W, block_bytes(N, K, ldw, elem_bytes(dtype)), "W")) ||
+         (st = debug_range(Y, block_bytes(M, N, ldy, y_dtype == HTS_F32 ? 4 : 2), "Y")) ||
+         (st = debug_range(workspace, workspace_bytes, "workspace"))))
+        return st;
     hts::GemmArgs a{};
     a.dtype = dtype;
     a.y_dtype = y_dtype;
@@ -511,6 +624,10 @@ hts_status hts_silu_mul(int32_t dtype, int64_t M, int64_t N, const void* G, int6
     if ((st = check_ptr(G, "G")) || (st = check_ptr(U, "U")) || (st = check_ptr(H, "H"))) return st;
     if ((st = check_ld(ldg, N, 8, "ldg")) || (st = check_ld(ldu, N, 8, "ldu")) || (st = check_ld(ldh, N, 8, "ldh")))
         return st;
+    if (debug_mode() && ((st = debug_range(G, block_bytes(M, N, ldg, 2), "G")) ||
+                         (st = debug_range(U, block_bytes(M, N, ldu, 2), "U")) ||
+                         (st = debug_range(H, block_bytes(M, N, ldh, 2), "H"))))
+        return st;
     return hip_status(hts::launch_silu_mul(dtype, M, N, static_cast<const uint16_t*>(G), ldg,
                                            static_cast<const uint16_t*>(U), ldu, static_cast<uint16_t*>(H), ldh,
                                            static_cast<hipStream_t>(stream)),
@@ -526,6 +643,9 @@ hts_status hts_col_norms(int32_t dtype, int64_t rows, int64_t K, const void* X, 
     if (!X || !col_scale) return fail(HTS_ERR_INVALID_ARG, "X or col_scale is NULL");
     if ((reinterpret_cast<uintptr_t>(X) & 1u) || (reinterpret_cast<uintptr_t>(col_scale) & 3u))
         return fail(HTS_ERR_ALIGN, "X must be 2-byte and col_scale 4-byte aligned");
+    if (debug_mode() && ((st = debug_range(X, block_bytes(rows, K, ldx, 2), "X")) ||
+                         (st = debug_range(col_scale, 4 * (uint64_t)K, "col_scale"))))
+        return st;
     return hip_status(hts::launch_col_norms(dtype, rows, K, static_cast<const uint16_t*>(X), ldx, col_scale,
                                             static_cast<hipStream_t>(stream)),
                       "column-norm kernel launch");
@@ -540,6 +660,10 @@ hts_status hts_wanda_tile_cost(const hts_desc* d, const void* W, int64_t ldw, co
     if (!col_scale || !cost) return fail(HTS_ERR_INVALID_ARG, "col_scale or cost is NULL");
     if ((reinterpret_cast<uintptr_t>(col_scale) & 3u) || (reinterpret_cast<uintptr_t>(cost) & 7u))
         return fail(HTS_ERR_ALIGN, "col_scale must be 4-byte and cost 8-byte aligned");
+    if (debug_mode() && ((st = debug_range(W, block_bytes(d->N, d->K, ldw, 2), "W")) ||
+                         (st = debug_range(col_scale, 4 * (uint64_t)d->K, "col_scale")) ||
+                         (st = debug_range(cost, 8 * (uint64_t)((d->N / d->bn) * (d->K / d->bk)), "cost"))))
+        return st;
     return hip_status(hts::launch_wanda_cost(*d, static_cast<const uint16_t*>(W), ldw, col_scale, cost,
                                              static_cast<hipStream_t>(stream)),
                       "tile-cost kernel launch");
@@ -550,6 +674,9 @@ hts_status hts_wanda_map(int64_t T, const double* cost, int64_t n_sparse, uint8_
     if (n_sparse < 0 || n_sparse > T) return fail(HTS_ERR_SHAPE, "n_sparse=%lld outside 0..T", (long long)n_sparse);
     if (!cost || !map) return fail(HTS_ERR_INVALID_ARG, "cost or map is NULL");
     if (reinterpret_cast<uintptr_t>(cost) & 7u) return fail(HTS_ERR_ALIGN, "cost must be 8-byte aligned");
+    hts_status st;
+    if (debug_mode() && ((st = debug_range(cost, 8 * (uint64_t)T, "cost")) || (st = debug_range(map, (uint64_t)T, "map"))))
+        return st;
     return hip_status(hts::launch_wanda_map(T, cost, n_sparse, map, static_cast<hipStream_t>(stream)),
                       "tile-map kernel launch");
 }

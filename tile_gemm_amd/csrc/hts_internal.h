@@ -70,6 +70,14 @@ hipError_t launch_pack_masked(const hts_desc& d, const hts_tile* index, const ui
                               uint32_t* meta, hipStream_t s);
 hipError_t launch_unpack(const hts_desc& d, const hts_tile* index, const uint16_t* values,
                          const uint32_t* meta, uint16_t* W_out, int64_t ldw, hipStream_t s);
+// Debug check of a device tile index (HTS_DEBUG=1): `out` must hold {0, 0xFFFFFFFF, 0, 0} before
+// the launch; afterwards bad = inconsistent records, first_bad = the first of them, and
+// values_end / meta_end = where the last tile's values (elements) and codes (words) end.
+struct IndexCheck {
+    uint32_t bad, first_bad;
+    uint64_t values_end, meta_end;
+};
+hipError_t launch_index_check(const hts_desc& d, const hts_tile* index, IndexCheck* out, hipStream_t s);
 // ksplit: waves per workgroup (4, 8 or 16); nt: 128-wide tile columns per batch of loads (2 or 4);
 // pp: 16-row panels per workgroup (1 or 2; 2 requires N % 32 == 0)
 hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s);

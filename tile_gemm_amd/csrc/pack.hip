@@ -318,7 +318,43 @@ __global__ __launch_bounds__(kPackThreads) void unpack8_kernel(
     }
 }
 
+// Debug check of a tile index in device memory (HTS_DEBUG=1): record t must have type 0 or 1, a
+// zero reserved word, and offsets equal to those of record t-1 plus that tile's stored size
+// (record 0 at offset 0), i.e. the prefix sums the plan wrote.  One thread per record; counts the
+// bad records, keeps the first, and reports where the last tile's values and codes end.
+__global__ __launch_bounds__(256) void index_check_kernel(const hts_tile* __restrict__ index, int64_t T,
+                                                          uint32_t dense, uint32_t sparse, uint32_t mwords,
+                                                          IndexCheck* out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const hts_tile e = index[t];
+    bool ok = e.type <= 1u && e.reserved == 0u;
+    if (t == 0) {
+        ok = ok && e.val_off == 0u && e.meta_off == 0u;
+    } else {
+        const hts_tile p = index[t - 1];
+        ok = ok && p.type <= 1u && e.val_off == p.val_off + (p.type ? sparse : dense) &&
+             e.meta_off == p.meta_off + (p.type ? mwords : 0u);
+    }
+    if (!ok) {
+        atomicAdd(&out->bad, 1u);
+        atomicMin(&out->first_bad, (uint32_t)t);
+    }
+    if (t == T - 1 && e.type <= 1u) {
+        out->values_end = (uint64_t)e.val_off + (e.type ? sparse : dense);
+        out->meta_end = (uint64_t)e.meta_off + (e.type ? mwords : 0u);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_index_check(const hts_desc& d, const hts_tile* index, IndexCheck* out, hipStream_t s) {
+    const int64_t T = (d.N / d.bn) * (d.K / d.bk);
+    const uint32_t dense = (uint32_t)(d.bn * d.bk);
+    index_check_kernel<<<dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s>>>(index, T, dense, dense / 2, dense / 32,
+                                                                               out);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const hts_desc& d, const hts_tile* index, const uint16_t* W, int64_t ldw,
                        const float* col_scale, uint16_t* values, uint32_t* meta, hipStream_t s) {

@@ -77,6 +77,8 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t) 
     if (!(sparse_path == 0 || sparse_path == 1)) complain("sparse path");
     return hipSuccess;
 }
+// the split planner's block height (the kernel side's rule, restated)
+int prefill_block_m(int64_t M, int32_t dtype) { return (dtype != HTS_FP8_E4M3 && M <= 64) ? 64 : 128; }
 hipError_t launch_silu_mul(int32_t, int64_t M, int64_t N, const uint16_t* G, int64_t ldg, const uint16_t* U,
                            int64_t ldu, uint16_t* H, int64_t ldh, hipStream_t) {
     ++g.silu;

@@ -400,10 +400,15 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 template <typename T, int BK, bool HYB, int SP>
 hipError_t launch4(const GemmArgs& a, hipStream_t s) {
-    // one tile row x 128 X rows per workgroup, 4 waves, 2 stages (two workgroups per CU)
+    // one tile row x 128 (or 64, prefill_block_m) X rows per workgroup, 4 waves, 2 stages (two
+    // workgroups per CU)
     if constexpr (Elem<T>::bytes == 1) {
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     } else {
+        if (prefill_block_m(a.M, a.dtype) == 64) {
+            if (HYB && a.bn == 64) return launch_tile<T, BK, HYB, SP, 64, 64, 2>(a, s);
+            return launch_tile<T, BK, HYB, SP, 128, 64, 2>(a, s);
+        }
         if (HYB && a.bn == 64) return launch_tile<T, BK, HYB, SP, 64, 128, 2>(a, s);
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     }
@@ -437,6 +442,19 @@ int prefill_chunk_log2(int bk) {
     for (int l = 2; l <= 6; ++l)
         if (v == (1 << l)) return l;
     return bk == 64 ? 3 : 2;
+}
+
+// X rows per block: 64 for 16-bit data at M <= 64, where a 128-row block would copy (and multiply)
+// at least half padding rows, else 128.  Interleaved A/B, 64 against 128 rows: M = 33 .. 64 on
+// the 7B, 13B and block layers 1.00-1.04x (bit-identical results); M = 96 .. 512 0.65-1.06x,
+// mostly slower (each weight slice is then copied once per 64 X rows).
+// HTS_PREFILL_BLOCK_M = 64 or 128 overrides.
+int prefill_block_m(int64_t M, int32_t dtype) {
+    if (dtype == HTS_FP8_E4M3) return 128;
+    const char* v = getenv("HTS_PREFILL_BLOCK_M");
+    if (v && !strcmp(v, "64")) return 64;
+    if (v && !strcmp(v, "128")) return 128;
+    return M <= 64 ? 64 : 128;
 }
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s) {

@@ -186,20 +186,24 @@ uint64_t unpack_workspace_bytes(const hts_desc* d, int64_t M) {
 }
 
 // Launch shape of the streaming kernel.  Defaults measured on MI355X (bf16, 128x128 tiles):
-//   panels per workgroup pp: 2 (each X fragment feeds two 16-row panels) when K >= 4608 --
-//     K = 5120: M=16 36.9 -> 29.4 us (13824 rows), 20.1 -> 16.4 us (5120 rows) -- else 1
-//     (K = 4096, 11008 rows: 17.2 us at pp = 1 against 20.2 at pp = 2);
+//   panels per workgroup pp: 2 (each X fragment feeds two 16-row panels) when K >= 4608 and that
+//     still leaves at least 160 workgroups -- K = 5120: M=16 36.9 -> 29.4 us (13824 rows), 20.1 ->
+//     16.4 us (5120 rows, 160 workgroups) -- else 1 (K = 4096, 11008 rows: 17.2 us at pp = 1
+//     against 20.2 at pp = 2; K = 11008, 4096 rows: 13.0 against 17.6 us at M = 1, where two
+//     panels would leave 128 workgroups for 256 CUs);
 //   waves per workgroup: 4 when pp = 2 still leaves >= 400 workgroups, else 8 (8-bit packed
 //     weights: 4 -- 7B up, M=1: 10.3 us against 12.3 at 8);
-//   tile columns per batch of loads: 2 (1 at M > 16, where two groups of X rows double the X
-//     registers and a batch of two would leave one wave per SIMD).
+//   tile columns per batch of loads: 1 with two panels (13B layers, M = 1 .. 16: 3-5% faster than
+//     2), on rows of K >= 4608 (K = 11008, 4096 rows: M = 1 12.8 against 13.8 us), or at M > 16,
+//     where two groups of X rows double the X registers and a batch of two would leave one wave
+//     per SIMD; else 2.
 // HTS_DECODE_PP=1|2, HTS_DECODE_KSPLIT=4|8|16 and HTS_DECODE_NT=1|2|4 override.
 int decode_pp(const hts::GemmArgs& a) {
     if (a.N % 32) return 1;                  // every accepted shape has 32 | N; kept as a guard
     const char* v = getenv("HTS_DECODE_PP");
     if (v && !strcmp(v, "2")) return 2;
     if (v && !strcmp(v, "1")) return 1;
-    return a.K >= 4608 ? 2 : 1;
+    return (a.K >= 4608 && a.N / 32 >= 160) ? 2 : 1;
 }
 
 int decode_ksplit(const hts::GemmArgs& a) {
@@ -207,14 +211,17 @@ int decode_ksplit(const hts::GemmArgs& a) {
     if (v && (!strcmp(v, "4") || !strcmp(v, "8") || !strcmp(v, "16"))) return atoi(v);
     // 8-bit tiles are half the bytes: fewer, longer waves stream better -- for the packed weight
     // at every M (7B up: M=8 12.2 -> 10.8 us, M=16 12.6 -> 11.7), for a row-major one below M = 8
-    if (a.dtype == HTS_FP8_E4M3 && (a.index || a.M < 8)) return 4;
-    return (decode_pp(a) == 2 && a.N / 32 >= 400) ? 4 : 8;
+    // -- as long as at least 400 workgroups remain (K = 11008, 4096 rows, 256 workgroups: M = 1
+    // 14.3 us with 4 waves against 9.9 with 8)
+    const int wgs = (int)(a.N / (16 * decode_pp(a)));
+    if (a.dtype == HTS_FP8_E4M3 && (a.index || a.M < 8) && wgs >= 400) return 4;
+    return (decode_pp(a) == 2 && wgs >= 400) ? 4 : 8;
 }
 
 int decode_nt(const hts::GemmArgs& a) {
     const char* v = getenv("HTS_DECODE_NT");
     if (v && (!strcmp(v, "1") || !strcmp(v, "2") || !strcmp(v, "4"))) return atoi(v);
-    return a.M > 16 ? 1 : 2;
+    return (a.M > 16 || decode_pp(a) == 2 || a.K >= 4608) ? 1 : 2;
 }
 
 

@@ -136,6 +136,10 @@ def test_gemm_rejects_bad_arguments_before_any_launch():
     bad = hts.make_desc(256, 256, 64, 96, "f16")
     assert gemm(desc=bad) == 7
     assert b"multiple" in L.hts_last_error() or b"64 or 128" in L.hts_last_error()
+    # above the streaming range a tile row must fit the tiled kernel's 256 tile columns
+    wide = hts.make_desc(128, 128 * 257, 128, 128, "bf16")
+    assert gemm(desc=wide, M=64, ldx=128 * 257, ldy=128) == 7
+    assert b"tile columns" in L.hts_last_error()
 
 
 def test_other_entry_points_reject_bad_arguments():

@@ -187,6 +187,31 @@ def test_tile_rows_of_many_tile_columns(Tk, kind):
     _check(Y.cpu().numpy(), Y_ref, f"Tk={Tk} {kind}")
 
 
+@pytest.mark.parametrize("bk,dtype", [(128, "bf16"), (64, "f16"), (128, "fp8")])
+def test_tile_rows_at_the_column_limit(bk, dtype):
+    # K / bk = 256 tile columns, the most one tile row of the tiled kernel holds (its ordered list
+    # fills all four of its list registers): the streaming kernel, the tiled kernel unsplit (no
+    # workspace) and split over K (parts that start in every register block of the list)
+    bn, Tk = bk, 256
+    N, K, Mmax = 256, bk * Tk, 300
+    T = (N // bn) * Tk
+    g = np.random.default_rng(256 + bk + (dtype == "fp8"))
+    m = (g.random(T) < 0.4).astype(np.uint8)
+    W = wl.gaussian_bits((N, K), 1.0 if dtype == "fp8" else 0.02, dtype, g)
+    X = wl.gaussian_bits((Mmax, K), 1.0, dtype, g)
+    Y_ref = oracle.hybrid_ref(X, W, dtype, m, bn, bk)
+    pw = hts.pack(hts.tensor_from_bits(W, dtype, DEV), m, bn, bk)
+    Xt = hts.tensor_from_bits(X, dtype, DEV)
+    for M in (1, 16, 48, Mmax):
+        say(f"[gemm-limit] Tk=256 bk={bk} {dtype} M={M}")
+        Y = hts.gemm(Xt[:M], pw, out_dtype=torch.float32)
+        Yu = torch.empty_like(Y)
+        hts.hts_gemm(pw.desc, pw.index, pw.values, pw.meta, Xt[:M], Yu)   # no workspace: unsplit
+        torch.cuda.synchronize()
+        _check(Y.cpu().numpy(), Y_ref[:M], f"Tk=256 bk={bk} {dtype} M={M}")
+        _check(Yu.cpu().numpy(), Y_ref[:M], f"Tk=256 bk={bk} {dtype} M={M} unsplit")
+
+
 @pytest.mark.parametrize("M", [1, 16, 300])
 def test_gemm_over_mask_packed_weight(M, sparse_path):
     # a weight packed from frozen 2:4 patterns feeds the same product

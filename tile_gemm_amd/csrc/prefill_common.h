@@ -136,10 +136,13 @@ __device__ __forceinline__ uint32_t list_entry(const uint32_t (&r)[4], int p) {
 }
 
 // Copies of one slice into an LDS stage.  Per 64-row weight group there are 8 copy jobs:
-// dense = 8 x 1 KiB; 2:4 = 4 x 1 KiB of stored values, 2 x 256 B of codes and 2 padding copies
-// of the codes into a sink.  Each of the NW waves issues BM/(8 NW) X copies and 8/NW copies per
-// group for every slice, whatever the tile types, so the wait for one slice is a fixed count
-// of outstanding copies.  KIND (dense / 2:4) is known at compile time: no branch per copy.
+// dense = 8 x 1 KiB; 2:4 = 4 x 1 KiB of stored values and 2 x 256 B of codes (16-bit elements;
+// 4 x 256 B for 8-bit).  With three or more stages the two missing 16-bit jobs are padding
+// copies of the codes into a sink: each of the NW waves then issues BM/(8 NW) X copies and 8/NW
+// copies per group for every slice, whatever the tile types, so the wait for one slice is a
+// fixed count of outstanding copies.  Two stages wait for every copy in flight, so they skip
+// the padding (measured: all-2:4 4096^2 layer 62.0 -> 61.0 us, 13B 5120^2 at M = 4096 192.3 ->
+// 190.6 us).  KIND (dense / 2:4) is known at compile time: no branch per copy.
 template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW, int ES = 2>
 __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, int ks, uint32_t stage) {
     constexpr int JPG = 8 / NW;
@@ -174,11 +177,11 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
             for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
         } else {
             // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
-            // codes, then the same two again into the sink).  With 4 waves wave w does jobs w and
-            // 4 + w, with 8 waves job w.
+            // codes, then the same two again into the sink, or nothing with two stages).  With 4
+            // waves wave w does jobs w and 4 + w, with 8 waves job w.
             if (NW == 4 || C.wave < 4)
                 buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
-            if (NW == 4 || C.wave >= 4)
+            if ((NW == 4 || C.wave >= 4) && (NSTAGE > 2 || !C.meta_to_sink))
                 buf4(C.mr,
                      C.meta_to_sink ? (uint32_t)Lo::SINK
                                     : stage + Lo::MOFF + gi * MGB + 256 * C.mjob,

@@ -78,7 +78,14 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t) 
     return hipSuccess;
 }
 // the split planner's block height (the kernel side's rule, restated)
-int prefill_block_m(int64_t M, int32_t dtype) { return (dtype != HTS_FP8_E4M3 && M <= 64) ? 64 : 128; }
+int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows) {
+    if (dtype == HTS_FP8_E4M3) return 128;
+    if (M <= 64) return 64;
+    if (block_rows != 128) return 128;
+    const int64_t nb = (N + 127) / 128, b128 = nb * ((M + 127) / 128), b192 = nb * ((M + 191) / 192);
+    if (b128 <= 256) return 128;
+    return ((b192 + 511) / 512) * 139 < ((b128 + 511) / 512) * 97 ? 192 : 128;
+}
 hipError_t launch_silu_mul(int32_t, int64_t M, int64_t N, const uint16_t* G, int64_t ldg, const uint16_t* U,
                            int64_t ldu, uint16_t* H, int64_t ldh, hipStream_t) {
     ++g.silu;

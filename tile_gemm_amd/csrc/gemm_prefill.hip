@@ -110,7 +110,7 @@ __device__ __forceinline__ void compute_sparse(f32x4 (&acc)[NBI][NBJ], const uin
 #pragma unroll
     for (int h = 0; h < NBI / 4; ++h) {
         const uint8_t* wg = ws + h * kGroupBytes;
-        const uint32_t* mg = ms + h * (meta_group_bytes<Elem<T>::bytes>() / 4);
+        const uint32_t* mg = ms + h * (kGroupBytes / 4);   // each group's codes sit in its own slot
         if (SP == SPARSE_SMFMAC) {
             u32x4 A[4];
             uint32_t idx[4];
@@ -305,7 +305,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
                 const uint8_t* st = step(ks);
                 if (wvalid)
                     compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
-                                               reinterpret_cast<const uint32_t*>(st + Lo::MOFF + wn * MGB), lane);
+                                               reinterpret_cast<const uint32_t*>(st + Lo::WOFF + wn * kGroupBytes + Lo::MHALF),
+                                               lane);
             }
         }
     }
@@ -400,16 +401,18 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 template <typename T, int BK, bool HYB, int SP>
 hipError_t launch4(const GemmArgs& a, hipStream_t s) {
-    // one tile row x 128 (or 64, prefill_block_m) X rows per workgroup, 4 waves, 2 stages (two
-    // workgroups per CU)
+    // one tile row x 128 (or 64 or 192, prefill_block_m) X rows per workgroup, 4 waves, 2 stages
+    // (two workgroups per CU)
     if constexpr (Elem<T>::bytes == 1) {
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     } else {
-        if (prefill_block_m(a.M, a.dtype) == 64) {
+        const int bm = prefill_block_m(a.M, a.N, a.dtype, (HYB && a.bn == 64) ? 64 : 128);
+        if (bm == 64) {
             if (HYB && a.bn == 64) return launch_tile<T, BK, HYB, SP, 64, 64, 2>(a, s);
             return launch_tile<T, BK, HYB, SP, 128, 64, 2>(a, s);
         }
         if (HYB && a.bn == 64) return launch_tile<T, BK, HYB, SP, 64, 128, 2>(a, s);
+        if (bm == 192) return launch_tile<T, BK, HYB, SP, 128, 192, 2>(a, s);
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     }
 }
@@ -444,17 +447,33 @@ int prefill_chunk_log2(int bk) {
     return bk == 64 ? 3 : 2;
 }
 
-// X rows per block: 64 for 16-bit data at M <= 64, where a 128-row block would copy (and multiply)
-// at least half padding rows, else 128.  Interleaved A/B, 64 against 128 rows: M = 33 .. 64 on
-// the 7B, 13B and block layers 1.00-1.04x (bit-identical results); M = 96 .. 512 0.65-1.06x,
-// mostly slower (each weight slice is then copied once per 64 X rows).
-// HTS_PREFILL_BLOCK_M = 64 or 128 overrides.
-int prefill_block_m(int64_t M, int32_t dtype) {
+// X rows per block (block_rows: weight rows per block, 128 or 64).
+//  - 64 for 16-bit data at M <= 64, where a 128-row block would copy (and multiply) at least half
+//    padding rows.  Interleaved A/B, 64 against 128 rows: M = 33 .. 64 on the 7B, 13B and block
+//    layers 1.00-1.04x (bit-identical results); M = 96 .. 512 0.65-1.06x, mostly slower (each
+//    weight slice is then copied once per 64 X rows).
+//  - 192 or 128 above.  A 128 x 192 block copies 40 KiB per 64-wide slice for 1.5x the products of
+//    a 128 x 128 block (32 KiB), and the copies set the pace: it takes about 1.39x as long.  The
+//    grid runs in rounds of 512 blocks (two per CU) and a partial last round costs nearly a whole
+//    one, so 192 rows are taken when their rounds x 1.39 undercut the 128-row rounds by 3%.
+//    Dense product, interleaved, 128 / 192 rows, us: 7B up M = 2048 189.9 / 175.6 (3 / 2 rounds),
+//    M = 4096 351.5 / 331.3 (6 / 4), 13B 5120^2 M = 4096 214.6 / 207.8 (3 / 2), 13B up M = 4096
+//    528.9 / 521.7 (7 / 5: within the margin, 128 kept); 4096^2 M = 2048 70.6 / 87.9 and 7B up
+//    M = 1024 114.8 / 128.8 (same rounds: 128 kept).
+// HTS_PREFILL_BLOCK_M = 64, 128 or 192 (128-row weight blocks of 16-bit data) overrides.
+int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows) {
     if (dtype == HTS_FP8_E4M3) return 128;
     const char* v = getenv("HTS_PREFILL_BLOCK_M");
     if (v && !strcmp(v, "64")) return 64;
     if (v && !strcmp(v, "128")) return 128;
-    return M <= 64 ? 64 : 128;
+    if (v && !strcmp(v, "192")) return block_rows == 128 ? 192 : 128;
+    if (M <= 64) return 64;
+    if (block_rows != 128) return 128;
+    const int64_t nb = (N + 127) / 128;
+    const int64_t b128 = nb * ((M + 127) / 128), b192 = nb * ((M + 191) / 192);
+    if (b128 <= 256) return 128;                  // split products: the planner fills the chip
+    const int64_t r128 = (b128 + 511) / 512, r192 = (b192 + 511) / 512;
+    return r192 * 139 < r128 * 97 ? 192 : 128;
 }
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s) {

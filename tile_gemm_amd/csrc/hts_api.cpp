@@ -243,7 +243,7 @@ int prefill_split(int64_t M, int64_t N, int64_t K, int32_t dtype, int bk, int bl
         const long x = strtol(v, nullptr, 10);
         if (x >= 1 && x <= 16) return (int)(x < slices ? x : slices);
     }
-    const int bm = hts::prefill_block_m(M, dtype);
+    const int bm = hts::prefill_block_m(M, N, dtype, block_rows);
     const int64_t blocks = ((N + block_rows - 1) / block_rows) * ((M + bm - 1) / bm);
     if (blocks > 256) return 1;
     int64_t sp = 512 / blocks;

@@ -84,9 +84,9 @@ hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int
 // Tiled kernel (one tile row x 128 X rows per workgroup); with a.nsplit > 1 it also launches the
 // fixed-order sum of the partial products into Y.
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s);
-// X rows per block of the tiled kernel at this M (64 or 128); the split planner counts blocks
-// with it.
-int prefill_block_m(int64_t M, int32_t dtype);
+// X rows per block of the tiled kernel (64, 128 or 192) for M rows of X, N weight rows in blocks
+// of block_rows (128 or 64); the split planner counts blocks with it.
+int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows);
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the
 // tiled kernel holds the index records of one tile row in LDS.
 constexpr int kMaxTileColsPerRow = 256;

@@ -47,18 +47,24 @@ __device__ __forceinline__ void block_of(int L, int NB, int MB, int ord, int& nb
     }
 }
 
-// LDS image of one stage: X slice (BM rows x 128 B), BN/64 weight groups, their codes.
+// LDS image of one stage: X slice (BM rows x 128 B), then BN/64 weight-group slots of 8 KiB.  A
+// dense group fills its slot; a 2:4 group's stored values fill the lower half and its codes (MGB
+// bytes) sit in the upper half, so the codes need no space of their own.  The ordered tile list
+// is built once, before the first copy, in stage 0's memory.  With two stages nothing else is
+// needed: a 128 x 192 block then takes 80 KiB, and two such workgroups fit in a CU's 160 KiB.
 template <int BN, int BM, int NSTAGE, int MGB = kMetaGroupBytes>
 struct Layout {
     static constexpr int NG = BN / 64;
     static constexpr int WOFF = BM * 128;
-    static constexpr int MOFF = WOFF + NG * kGroupBytes;
-    static constexpr int STAGE = MOFF + NG * MGB;
-    static constexpr int SINK = NSTAGE * STAGE;              // target of the padding copies
-    static constexpr int LIST = SINK + 1024;                 // ordered tile list: {val_off, meta_off}
+    static constexpr int MHALF = kGroupBytes / 2;            // codes inside a 2:4 group's slot
+    static constexpr int STAGE = WOFF + NG * kGroupBytes;
+    static constexpr int SINK = NSTAGE * STAGE;              // target of the padding copies (3+ stages)
+    static constexpr int TOTAL = SINK + (NSTAGE > 2 ? 1024 : 0);
+    static constexpr int LIST = 0;                           // ordered tile list: {val_off, meta_off}
     static constexpr int LCOL = LIST + kMaxTileCols * 8;     // ... and the tile column of each entry
     static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // dense tiles of each chunk (bytes)
-    static constexpr int TOTAL = WCNT + 64;
+    static_assert(MGB <= MHALF, "codes of a slice fit the upper half of a 2:4 group's slot");
+    static_assert(WCNT + 64 <= STAGE, "the list fits in stage 0");
 };
 
 // Dynamic LDS of the tiled kernels; copies address it by byte offset from an LDS-typed base,
@@ -183,8 +189,7 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
                 buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
             if ((NW == 4 || C.wave >= 4) && (NSTAGE > 2 || !C.meta_to_sink))
                 buf4(C.mr,
-                     C.meta_to_sink ? (uint32_t)Lo::SINK
-                                    : stage + Lo::MOFF + gi * MGB + 256 * C.mjob,
+                     C.meta_to_sink ? (uint32_t)Lo::SINK : ws + Lo::MHALF + 256 * C.mjob,
                      C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
         }
     }
@@ -201,7 +206,9 @@ __device__ __forceinline__ void wait_vm() {
 // leaves the ordered list in C's registers: the row cut into chunks of 2^lch tile columns (inside
 // one wave: lch <= 6), each ordered dense first; C.lnd lane c = dense tiles of chunk c.  Tile rows
 // then walk K chunk by chunk, so workgroups of different tile rows that run together stay within a
-// chunk of each other and find each other's X slices in L2.  Uses LDS at Lo::LIST .. Lo::TOTAL.
+// chunk of each other and find each other's X slices in L2.  Uses LDS at Lo::LIST .. Lo::WCNT + 64
+// (stage 0's memory): it ends with a barrier, so no copy into that stage starts before every
+// wave has read the list.
 template <typename Lo, int BK, bool HYB, int BN, int BM, int NW>
 __device__ __forceinline__ void load_tile_list(Ctx<BK, HYB, BN, BM, NW>& C, const GemmArgs& a, int lch, int tid,
                                                int lane) {
@@ -237,6 +244,7 @@ __device__ __forceinline__ void load_tile_list(Ctx<BK, HYB, BN, BM, NW>& C, cons
         C.lm[w] = in ? list[q].y : 0u;
         C.lc[w] = in ? (uint32_t)lcol[q] : 0u;
     }
+    __syncthreads();   // the list area is stage 0: every wave has read it before the first copy
 }
 
 }  // namespace

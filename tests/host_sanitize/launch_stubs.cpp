@@ -79,8 +79,7 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t) 
 }
 // the split planner's block height (the kernel side's rule, restated)
 int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows) {
-    if (dtype == HTS_FP8_E4M3) return 128;
-    if (M <= 64) return 64;
+    if (M <= 64) return dtype == HTS_FP8_E4M3 ? 128 : 64;
     if (block_rows != 128) return 128;
     const int64_t nb = (N + 127) / 128, b128 = nb * ((M + 127) / 128), b192 = nb * ((M + 191) / 192);
     if (b128 <= 256) return 128;

@@ -1,8 +1,8 @@
 """The tiled kernel's 128 x 192 blocks (taken when they need fewer rounds of workgroups than
 128 x 128 ones, e.g. the 7B up-projection at M = 2048), forced with HTS_PREFILL_BLOCK_M=192 on
 small layers: ragged M (blocks ending inside, at and past M), products split over K into the
-workspace and unsplit, edge maps, both sparse-tile paths, 16-bit outputs, the gated output stage
-and the dense product.  Acceptance as everywhere: max|Y - Y_ref| <= 5e-3 * max|Y_ref|."""
+workspace and unsplit, edge maps, both sparse-tile paths, 16-bit outputs, 8-bit data, the gated
+output stage and the dense product.  Acceptance as everywhere: max|Y - Y_ref| <= 5e-3 * max|Y_ref|."""
 import numpy as np
 import pytest
 import torch
@@ -33,7 +33,7 @@ def _layer(dtype, kind, seed, N=384, K=1024, Mmax=600):
     T = (N // 128) * (K // 128)
     m = {"random": g.random(T) < 0.5, "all_dense": np.zeros(T, bool), "all_sparse": np.ones(T, bool)}[kind]
     m = m.astype(np.uint8)
-    W = wl.gaussian_bits((N, K), 0.02, dtype, g)
+    W = wl.gaussian_bits((N, K), 1.0 if dtype == "fp8" else 0.02, dtype, g)
     X = wl.gaussian_bits((Mmax, K), 1.0, dtype, g)
     return W, X, m
 
@@ -56,6 +56,25 @@ def test_block192_ragged_m(dtype, sparse_path, block192, monkeypatch):
         _check(Y.cpu().numpy(), Y_ref[:M], f"M={M}")
         _check(Yu.cpu().numpy(), Y_ref[:M], f"M={M} unsplit")
         _check(oracle.widen_f64(hts.bits_from_tensor(Yh), dtype), Y_ref[:M], f"M={M} {dtype} out")
+
+
+def test_block192_fp8(block192):
+    # 8-bit data: one 16x16x128 product per 16 x 16 block and slice, SMFMAC 16x16x128 for 2:4 groups
+    W, X, m = _layer("fp8", "random", 19250)
+    Y_ref = oracle.hybrid_ref(X, W, "fp8", m, 128, 128)
+    pw = hts.pack(hts.tensor_from_bits(W, "fp8", DEV), m, 128, 128)
+    Xt = hts.tensor_from_bits(X, "fp8", DEV)
+    Wt = hts.tensor_from_bits(W, "fp8", DEV)
+    for M in (65, 193, 600):
+        say(f"[block192] fp8 M={M}")
+        Y = hts.gemm(Xt[:M], pw, out_dtype=torch.float32)
+        Yu = torch.empty_like(Y)
+        hts.hts_gemm(pw.desc, pw.index, pw.values, pw.meta, Xt[:M], Yu)
+        Yd = hts.dense_gemm(Xt[:M], Wt, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check(Y.cpu().numpy(), Y_ref[:M], f"fp8 M={M}")
+        _check(Yu.cpu().numpy(), Y_ref[:M], f"fp8 M={M} unsplit")
+        _check(Yd.cpu().numpy(), oracle.gemm_ref(X[:M], W, "fp8"), f"fp8 dense M={M}")
 
 
 @pytest.mark.parametrize("kind", ["all_dense", "all_sparse"])

@@ -404,6 +404,7 @@ hipError_t launch4(const GemmArgs& a, hipStream_t s) {
     // one tile row x 128 (or 64 or 192, prefill_block_m) X rows per workgroup, 4 waves, 2 stages
     // (two workgroups per CU)
     if constexpr (Elem<T>::bytes == 1) {
+        if (prefill_block_m(a.M, a.N, a.dtype, 128) == 192) return launch_tile<T, BK, HYB, SP, 128, 192, 2>(a, s);
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     } else {
         const int bm = prefill_block_m(a.M, a.N, a.dtype, (HYB && a.bn == 64) ? 64 : 128);
@@ -459,15 +460,17 @@ int prefill_chunk_log2(int bk) {
 //    Dense product, interleaved, 128 / 192 rows, us: 7B up M = 2048 189.9 / 175.6 (3 / 2 rounds),
 //    M = 4096 351.5 / 331.3 (6 / 4), 13B 5120^2 M = 4096 214.6 / 207.8 (3 / 2), 13B up M = 4096
 //    528.9 / 521.7 (7 / 5: within the margin, 128 kept); 4096^2 M = 2048 70.6 / 87.9 and 7B up
-//    M = 1024 114.8 / 128.8 (same rounds: 128 kept).
-// HTS_PREFILL_BLOCK_M = 64, 128 or 192 (128-row weight blocks of 16-bit data) overrides.
+//    M = 1024 114.8 / 128.8 (same rounds: 128 kept).  8-bit hybrid (its slices are also 128 bytes
+//    of each row): 7B up M = 2048 100.9 / 92.3, M = 4096 182.5 / 169.2, M = 1024 58.5 / 69.4.
+//  8-bit data never takes 64 rows.
+// HTS_PREFILL_BLOCK_M = 64 (16-bit), 128 or 192 (128-row weight blocks) overrides.
 int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows) {
-    if (dtype == HTS_FP8_E4M3) return 128;
+    const bool fp8 = dtype == HTS_FP8_E4M3;
     const char* v = getenv("HTS_PREFILL_BLOCK_M");
-    if (v && !strcmp(v, "64")) return 64;
+    if (v && !strcmp(v, "64") && !fp8) return 64;
     if (v && !strcmp(v, "128")) return 128;
     if (v && !strcmp(v, "192")) return block_rows == 128 ? 192 : 128;
-    if (M <= 64) return 64;
+    if (M <= 64) return fp8 ? 128 : 64;
     if (block_rows != 128) return 128;
     const int64_t nb = (N + 127) / 128;
     const int64_t b128 = nb * ((M + 127) / 128), b192 = nb * ((M + 191) / 192);

@@ -17,8 +17,8 @@
 // The tile index of the workgroup's tile rows is read into LDS once, so no
 // weight load waits on an index load.  Workgroups are numbered so that each XCD
 // (own L2) receives a contiguous range of output blocks, walked in groups of 8
-// N-blocks (N fastest inside a group): blocks running together on one XCD share
-// their W and X slices in its L2.
+// N-blocks (11 for 8-bit data; N fastest inside a group): blocks running together
+// on one XCD share their W and X slices in its L2.
 #include <cstring>
 
 #include "prefill_common.h"
@@ -368,12 +368,17 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
     store_y4(Y, m * ldy + n, y_dtype, acc);
 }
 
-// Block order of the tiled kernels (HTS_PREFILL_ORDER overrides; see block_of).
-int prefill_order() {
+// Block order of the tiled kernels (HTS_PREFILL_ORDER overrides; see block_of): contiguous per XCD,
+// N fastest, in groups of 8 N-blocks for 16-bit data and 11 for 8-bit data.  Interleaved sweeps of
+// 6 to 16 N-blocks per group on two boxes: the 8-bit 7B up-projection at M = 2048 ran 1.05x faster
+// with 11 on both; on the 16-bit layers (7B up, gate and down, 13B, the 4096^2 sweep) no group
+// size won everywhere (0.96-1.05x, box to box), so they keep 8.
+int prefill_order(int elem_bytes) {
     const char* e = getenv("HTS_PREFILL_ORDER");
     const int v = (e && *e) ? atoi(e) : -1;
     const int g = (v >> 1) & 31;
-    if (v < 0 || v > 127 || g == 0) return 1 | (kGroupN << 1);   // groups of at least one N-block
+    if (v < 0 || v > 127 || g == 0)   // groups of at least one N-block
+        return 1 | ((elem_bytes == 1 ? kGroupN8 : kGroupN) << 1);
     return v;
 }
 
@@ -389,7 +394,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int NB = (int)((a.N + BN - 1) / BN), MB = (int)((a.M + BM - 1) / BM);
     const int nsplit = a.nsplit > 1 ? a.nsplit : 1;
-    kern<<<dim3((unsigned)(NB * MB), (unsigned)nsplit), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order(),
+    kern<<<dim3((unsigned)(NB * MB), (unsigned)nsplit), dim3(64 * NW), Lo::TOTAL, s>>>(a, NB, MB, prefill_order(Elem<T>::bytes),
                                                                                    prefill_chunk_log2(BK));
     e = hipGetLastError();
     if (e != hipSuccess || nsplit == 1) return e;

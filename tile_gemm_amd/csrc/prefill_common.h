@@ -18,14 +18,16 @@ constexpr int kMetaGroupBytes = 64 * 8; // codes of one 64-row group for one sli
 template <int ES> constexpr int slice_k() { return 128 / ES; }
 template <int ES> constexpr int meta_group_bytes() { return 64 * slice_k<ES>() / 8; }
 constexpr int kMaxTileCols = 256;       // K/bk limit: the tile list of a tile row is kept in LDS
-constexpr int kGroupN = 8;
+constexpr int kGroupN = 8;              // N-blocks per group of the block order (16-bit data)
+constexpr int kGroupN8 = 11;            // ... and for 8-bit data
 
 // Block id -> output block (nb, mb).  ord = xcd | (gsn << 1) | (mfast << 6):
 //   xcd   : 1 = each XCD (block id % 8) receives a contiguous range of the order below
 //   gsn   : N-blocks per group (1..31); groups are walked in order
 //   mfast : inside a group, 1 = M-blocks fastest, 0 = N-blocks fastest
-// Default: contiguous per XCD, groups of 8 N-blocks, N fastest, so that the workgroups running
-// together on one XCD cover about 8 N-blocks x 8 M-blocks and share W and X slices in its L2.
+// Default: contiguous per XCD, groups of 8 N-blocks (11 for 8-bit data), N fastest, so that the
+// workgroups running together on one XCD cover about 8 N-blocks x 8 M-blocks and share W and X
+// slices in its L2.
 __device__ __forceinline__ void block_of(int L, int NB, int MB, int ord, int& nb, int& mb) {
     const int total = NB * MB;
     int id = L;

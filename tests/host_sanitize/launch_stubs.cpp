@@ -3,6 +3,7 @@
 // records the call and checks what the host code hands to the kernels: workspace pointers and
 // sizes inside the buffer the caller gave, launch-shape parameters in their documented ranges.
 #include <cstdio>
+#include <cstdlib>
 
 #include "hts.h"
 #include "hts_internal.h"
@@ -84,6 +85,12 @@ int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows) {
     const int64_t nb = (N + 127) / 128, b128 = nb * ((M + 127) / 128), b192 = nb * ((M + 191) / 192);
     if (b128 <= 256) return 128;
     return ((b192 + 511) / 512) * 139 < ((b128 + 511) / 512) * 97 ? 192 : 128;
+}
+// weight rows per block on 64-row tiles (the kernel side's rule, restated): two tile rows
+int prefill_weight_rows(int bn) {
+    if (bn != 64) return 128;
+    const char* v = getenv("HTS_PREFILL_TWO_ROWS");
+    return (v && v[0] == '0' && !v[1]) ? 64 : 128;
 }
 hipError_t launch_silu_mul(int32_t, int64_t M, int64_t N, const uint16_t* G, int64_t ldg, const uint16_t* U,
                            int64_t ldu, uint16_t* H, int64_t ldh, hipStream_t) {

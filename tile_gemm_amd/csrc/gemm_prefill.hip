@@ -158,11 +158,17 @@ __device__ __forceinline__ void wait_slice(int later) {
     else wait_vm<0>();
 }
 
-template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
+// TWO: the block covers two 64-row tile rows (64-row tiles, 16-bit data); it walks K in tile-column
+// order and each wave feeds its own row's tile to the matrix cores by that tile's type.  Its
+// per-slice choices of copy source cost registers: it is held to two waves per SIMD (two
+// workgroups per CU), which the 128 x 64 and 128 x 128 forms reach without spills.
+template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW, bool TWO = false>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(TWO ? 2 : 1)))
+void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
     constexpr int ES = Elem<T>::bytes, KSL = slice_k<ES>(), MGB = meta_group_bytes<ES>();
     using Lo = Layout<BN, BM, NSTAGE, MGB>;
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    static_assert(!TWO || (HYB && BN == 128 && NSTAGE == 2 && ES == 2 && NW == 4), "two 64-row tile rows");
     constexpr int NG = BN / 64, WM = NW / NG, WTM = BM / WM, NBJ = WTM / 16, SPT = BK / KSL;
     static_assert(NBJ >= 1 && BM % (8 * NW) == 0 && 2 * NW <= 16, "block shape");
     const int tid = threadIdx.x, lane = tid & 63;
@@ -225,7 +231,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         C.meta_to_sink = cj >= NCJ;
     }
     // ordered tile list of the tile row, tile columns kept for the X copies
-    if (HYB) {
+    if constexpr (TWO) {
+        load_two_lists<Lo>(C, a, tid, lane);
+    } else if (HYB) {
         load_tile_list<Lo>(C, a, lch, tid, lane);
     } else {
         C.lnd = 0u;
@@ -267,8 +275,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         for (int b = 0; b < k0 / (64 * SPT); ++b) C.shift_list();
     auto issue = [&](int kn) {   // called for kn = k0, k0 + 1, ... in order
         if (HYB && kn > k0 && kn % (64 * SPT) == 0) C.shift_list();
-        set_x(kn);
         const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
+        if constexpr (TWO) {
+            C.xso = (uint32_t)(ES * (kn / SPT) * BK + 128 * (kn % SPT));   // tile column in K order
+            issue_slice_two(C, kn, stage);
+            return;
+        }
+        set_x(kn);
         if (dense_slice(kn)) issue_slice<BK, HYB, BN, BM, NSTAGE, true, NW, ES>(C, kn, stage);
         else issue_slice<BK, HYB, BN, BM, NSTAGE, false, NW, ES>(C, kn, stage);
     };
@@ -289,6 +302,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_prefill_kernel(const GemmArgs a,
         for (; ks < k1; ++ks) {
             const uint8_t* st = step(ks);
             if (wvalid) compute_dense<T, SP, 4, NBJ, false>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes, lane);
+        }
+    } else if constexpr (TWO) {
+        // K order; the type of this wave's tile is read before step() issues the next slice (which
+        // may move the list registers on to the next 64 tile columns)
+        for (; ks < k1; ++ks) {
+            const bool sparse = (list_entry(C.lc, ks / SPT) >> wn) & 1u;
+            const uint8_t* st = step(ks);
+            if (!wvalid) continue;
+            const uint8_t* ws = st + Lo::WOFF + wn * kGroupBytes;
+            if (sparse)
+                compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, ws, reinterpret_cast<const uint32_t*>(ws + Lo::MHALF), lane);
+            else
+                compute_dense<T, SP, 4, NBJ, true>(acc, st + xoff, ws, lane);
         }
     } else {
         // chunk by chunk: its dense run, then its 2:4 run (a split part may start or end inside)
@@ -382,10 +408,10 @@ int prefill_order(int elem_bytes) {
     return v;
 }
 
-template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW = 4>
+template <typename T, int BK, bool HYB, int SP, int BN, int BM, int NSTAGE, int NW = 4, bool TWO = false>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     using Lo = Layout<BN, BM, NSTAGE, meta_group_bytes<Elem<T>::bytes>()>;
-    auto kern = gemm_prefill_kernel<T, BK, HYB, SP, BN, BM, NSTAGE, NW>;
+    auto kern = gemm_prefill_kernel<T, BK, HYB, SP, BN, BM, NSTAGE, NW, TWO>;
     // one flag set per instantiation (this static) and device
     static DeviceOnce lds_limit;
     hipError_t e = lds_limit.run([&] {
@@ -412,6 +438,14 @@ hipError_t launch4(const GemmArgs& a, hipStream_t s) {
         if (prefill_block_m(a.M, a.N, a.dtype, 128) == 192) return launch_tile<T, BK, HYB, SP, 128, 192, 2>(a, s);
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);
     } else {
+        if constexpr (HYB) {
+            // 64-row tiles: two tile rows per block, 64 or 128 X rows (192 would need more than the
+            // 256 registers that let two workgroups share a CU)
+            if (a.bn == 64 && prefill_weight_rows(64) == 128) {
+                if (prefill_block_m(a.M, a.N, a.dtype, 128) == 64) return launch_tile<T, BK, HYB, SP, 128, 64, 2, 4, true>(a, s);
+                return launch_tile<T, BK, HYB, SP, 128, 128, 2, 4, true>(a, s);
+            }
+        }
         const int bm = prefill_block_m(a.M, a.N, a.dtype, (HYB && a.bn == 64) ? 64 : 128);
         if (bm == 64) {
             if (HYB && a.bn == 64) return launch_tile<T, BK, HYB, SP, 64, 64, 2>(a, s);
@@ -482,6 +516,14 @@ int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows) {
     if (b128 <= 256) return 128;                  // split products: the planner fills the chip
     const int64_t r128 = (b128 + 511) / 512, r192 = (b192 + 511) / 512;
     return r192 * 139 < r128 * 97 ? 192 : 128;
+}
+
+// Weight rows per block of a packed weight with bn-row tiles (16-bit data): 128, so 64-row tiles
+// go two tile rows to a block (HTS_PREFILL_TWO_ROWS=0: one 64-row tile row per block instead).
+int prefill_weight_rows(int bn) {
+    if (bn != 64) return 128;
+    const char* v = getenv("HTS_PREFILL_TWO_ROWS");
+    return (v && !strcmp(v, "0")) ? 64 : 128;
 }
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s) {

@@ -358,7 +358,10 @@ hts_status gemm_impl(const hts_desc* d, const hts_tile* index, const void* value
     a.ldy = ldy;
     a.gate = gate;
     a.ldg = ldg;
-    attach_split(a, prefill_split(M, d->N, d->K, d->dtype, d->bk, d->bn == 64 ? 64 : 128), workspace, workspace_bytes);
+    attach_split(a,
+                 prefill_split(M, d->N, d->K, d->dtype, d->bk,
+                               d->dtype == HTS_FP8_E4M3 ? 128 : hts::prefill_weight_rows(d->bn)),
+                 workspace, workspace_bytes);
     return run_gemm(a, static_cast<hipStream_t>(stream));
 }
 
@@ -402,7 +405,7 @@ ScratchAddress g_scratch;
 uint64_t gemm_workspace_bytes(const hts_desc* d, int64_t M) {
     const uint64_t ws = unpack_workspace_bytes(d, M);
     // the unpacked weight (tiles of 32), then the parts of a split product
-    const int br = (ws || d->bn != 64) ? 128 : 64;
+    const int br = (ws || d->dtype == HTS_FP8_E4M3) ? 128 : hts::prefill_weight_rows(d->bn);
     const int bk = ws ? ((d->K % 128 == 0) ? 128 : 64) : d->bk;   // the unpacked product's slices
     return ws + split_bytes(M, d->N, prefill_split(M, d->N, d->K, d->dtype, bk, br));
 }

@@ -87,6 +87,8 @@ hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s
 // X rows per block of the tiled kernel (64, 128 or 192) for M rows of X, N weight rows in blocks
 // of block_rows (128 or 64); the split planner counts blocks with it.
 int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows);
+// Weight rows per block of the tiled kernel on a packed weight with bn-row tiles (16-bit data).
+int prefill_weight_rows(int bn);
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the
 // tiled kernel holds the index records of one tile row in LDS.
 constexpr int kMaxTileColsPerRow = 256;

@@ -113,6 +113,9 @@ struct Ctx {
     // and after each block of 64 entries the registers move down by one (shift_list), so entry p
     // is always lane p % 64 of the first register: one lane read, no register select.
     uint32_t lv[4], lm[4], lc[4];
+    // blocks of two 64-row tile rows (64-row tiles): lv / lm hold the first row's records in K order,
+    // lv2 / lm2 the second's, and lc the two rows' types (bit 0: first row 2:4, bit 1: second)
+    uint32_t lv2[4], lm2[4];
     int Tk;
     rsrc_t xr;                          // X rows m0 .. M-1
     rsrc_t wr;                          // values of the tile row from its first tile (or W rows n0 ..)
@@ -132,8 +135,10 @@ struct Ctx {
             lv[w] = lv[w + 1];
             lm[w] = lm[w + 1];
             lc[w] = lc[w + 1];
+            lv2[w] = lv2[w + 1];
+            lm2[w] = lm2[w + 1];
         }
-        lv[3] = lm[3] = lc[3] = 0u;
+        lv[3] = lm[3] = lc[3] = lv2[3] = lm2[3] = 0u;
     }
 };
 
@@ -151,6 +156,39 @@ __device__ __forceinline__ uint32_t list_entry(const uint32_t (&r)[4], int p) {
 // fixed count of outstanding copies.  Two stages wait for every copy in flight, so they skip
 // the padding (measured: all-2:4 4096^2 layer 62.0 -> 61.0 us, 13B 5120^2 at M = 4096 192.3 ->
 // 190.6 us).  KIND (dense / 2:4) is known at compile time: no branch per copy.
+template <int BK, bool HYB, int BN, int BM, int NW>
+__device__ __forceinline__ void issue_x(const Ctx<BK, HYB, BN, BM, NW>& C, uint32_t stage) {
+#pragma unroll
+    for (int v = 0; v < BM / (8 * NW); ++v) buf16(C.xr, stage + 1024 * (C.wave + NW * v), C.xvo[v], C.xso);
+}
+
+// Group gi of a slice from a packed tile: rows r .. r+63 of the tile whose values start at element
+// voff and whose codes start at word moff; s = slice of the tile.
+template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW, int ES>
+__device__ __forceinline__ void issue_packed_group(const Ctx<BK, HYB, BN, BM, NW>& C, int gi, uint32_t r,
+                                                   uint32_t voff, uint32_t moff, int s, uint32_t stage) {
+    constexpr int JPG = 8 / NW;
+    constexpr int KSL = slice_k<ES>(), MGB = meta_group_bytes<ES>();
+    using Lo = Layout<BN, BM, NSTAGE, MGB>;
+    const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
+    if (DENSE) {
+        // packed tile: slice s is chunk columns 8s .. 8s+7 of every row, 2048 bytes per 8 columns
+        const uint32_t so = ES * (voff - C.vbase + r * BK) + 2048 * s;
+#pragma unroll
+        for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
+    } else {
+        // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
+        // codes, then the same two again into the sink, or nothing with two stages).  With 4
+        // waves wave w does jobs w and 4 + w, with 8 waves job w.
+        if (NW == 4 || C.wave < 4)
+            buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
+        if ((NW == 4 || C.wave >= 4) && (NSTAGE > 2 || !C.meta_to_sink))
+            buf4(C.mr,
+                 C.meta_to_sink ? (uint32_t)Lo::SINK : ws + Lo::MHALF + 256 * C.mjob,
+                 C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
+    }
+}
+
 template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW, int ES = 2>
 __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, int ks, uint32_t stage) {
     constexpr int JPG = 8 / NW;
@@ -165,35 +203,40 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
         voff = list_entry(C.lv, p);
         moff = list_entry(C.lm, p);
     }
-#pragma unroll
-    for (int v = 0; v < BM / (8 * NW); ++v) buf16(C.xr, stage + 1024 * (C.wave + NW * v), C.xvo[v], C.xso);
+    issue_x(C, stage);
 #pragma unroll
     for (int gi = 0; gi < Lo::NG; ++gi) {
-        const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
         if (!HYB) {                             // rows past N read zeros (bound of the resource)
+            const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
 #pragma unroll
             for (int v = 0; v < JPG; ++v)
                 buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v],
                       (uint32_t)(ES * 64 * gi * C.ldw + 128 * (int64_t)ks));
             continue;
         }
-        const uint32_t r = 64 * gi;             // a block is one tile row: groups at rows 0, 64
-        if (DENSE) {
-            // packed tile: slice s is chunk columns 8s .. 8s+7 of every row, 2048 bytes per 8 columns
-            const uint32_t so = ES * (voff - C.vbase + r * BK) + 2048 * s;
-#pragma unroll
-            for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
-        } else {
-            // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
-            // codes, then the same two again into the sink, or nothing with two stages).  With 4
-            // waves wave w does jobs w and 4 + w, with 8 waves job w.
-            if (NW == 4 || C.wave < 4)
-                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
-            if ((NW == 4 || C.wave >= 4) && (NSTAGE > 2 || !C.meta_to_sink))
-                buf4(C.mr,
-                     C.meta_to_sink ? (uint32_t)Lo::SINK : ws + Lo::MHALF + 256 * C.mjob,
-                     C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
-        }
+        // a block is one tile row: groups at rows 0, 64 of the tile
+        issue_packed_group<BK, HYB, BN, BM, NSTAGE, DENSE, NW, ES>(C, gi, 64 * gi, voff, moff, s, stage);
+    }
+}
+
+// Copies of one slice of a block of two 64-row tile rows (16-bit data, two stages): the slice's
+// tile column is the same in both rows, each row's tile has its own type and offsets, and a
+// second row past N is not copied.
+template <int BK, bool HYB, int BN, int BM, int NW>
+__device__ __forceinline__ void issue_slice_two(const Ctx<BK, HYB, BN, BM, NW>& C, int ks, uint32_t stage) {
+    static_assert(BN == 128, "two 64-row groups");
+    constexpr int SPT = BK / 64;
+    const int p = ks / SPT, s = ks % SPT;
+    // every list read before the first copy
+    const uint32_t ty = list_entry(C.lc, p);
+    const uint32_t v0 = list_entry(C.lv, p), m0 = list_entry(C.lm, p);
+    const uint32_t v1 = list_entry(C.lv2, p), m1 = list_entry(C.lm2, p);
+    issue_x(C, stage);
+    if (ty & 1u) issue_packed_group<BK, HYB, BN, BM, 2, false, NW, 2>(C, 0, 0u, v0, m0, s, stage);
+    else issue_packed_group<BK, HYB, BN, BM, 2, true, NW, 2>(C, 0, 0u, v0, m0, s, stage);
+    if (C.gvalid(1)) {
+        if (ty & 2u) issue_packed_group<BK, HYB, BN, BM, 2, false, NW, 2>(C, 1, 0u, v1, m1, s, stage);
+        else issue_packed_group<BK, HYB, BN, BM, 2, true, NW, 2>(C, 1, 0u, v1, m1, s, stage);
     }
 }
 
@@ -247,6 +290,41 @@ __device__ __forceinline__ void load_tile_list(Ctx<BK, HYB, BN, BM, NW>& C, cons
         C.lc[w] = in ? (uint32_t)lcol[q] : 0u;
     }
     __syncthreads();   // the list area is stage 0: every wave has read it before the first copy
+}
+
+// Reads the index records of the block's two 64-row tile rows (one tile column per thread) and
+// leaves them in C's registers in K order: lv / lm the first row's {val_off, meta_off}, lv2 / lm2
+// the second's (zeros when that row is past N), lc the two types.  Uses stage 0's memory and ends
+// with a barrier, as load_tile_list.
+template <typename Lo, int BK, bool HYB, int BN, int BM, int NW>
+__device__ __forceinline__ void load_two_lists(Ctx<BK, HYB, BN, BM, NW>& C, const GemmArgs& a, int tid, int lane) {
+    uint2* l0 = reinterpret_cast<uint2*>(smem + Lo::LIST);
+    uint2* l1 = reinterpret_cast<uint2*>(smem + Lo::LIST + kMaxTileCols * 8);
+    uint8_t* ty = reinterpret_cast<uint8_t*>(smem + Lo::LIST + 2 * kMaxTileCols * 8);
+    static_assert(Lo::LIST + 2 * kMaxTileCols * 8 + kMaxTileCols <= Lo::STAGE, "both lists fit in stage 0");
+    const int64_t tn = C.n0 / a.bn;                  // the first of the two tile rows
+    const bool second = C.gvalid(1);
+    if (tid < C.Tk) {
+        const hts_tile e0 = a.index[tn * C.Tk + tid];
+        hts_tile e1 = {0u, 0u, 0u, 0u};
+        if (second) e1 = a.index[(tn + 1) * C.Tk + tid];
+        l0[tid] = uint2{e0.val_off, e0.meta_off};
+        l1[tid] = uint2{e1.val_off, e1.meta_off};
+        ty[tid] = (uint8_t)((e0.type != HTS_TILE_DENSE ? 1u : 0u) | (second && e1.type != HTS_TILE_DENSE ? 2u : 0u));
+    }
+    __syncthreads();
+    C.lnd = 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int q = 64 * w + lane;
+        const bool in = q < C.Tk;
+        C.lv[w] = in ? l0[q].x : 0u;
+        C.lm[w] = in ? l0[q].y : 0u;
+        C.lv2[w] = in ? l1[q].x : 0u;
+        C.lm2[w] = in ? l1[q].y : 0u;
+        C.lc[w] = in ? (uint32_t)ty[q] : 0u;
+    }
+    __syncthreads();   // stage 0: every wave has read the lists before the first copy
 }
 
 }  // namespace

@@ -231,8 +231,9 @@ void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
         C.meta_to_sink = cj >= NCJ;
     }
     // ordered tile list of the tile row, tile columns kept for the X copies
+    SecondRow R2;                  // blocks of two tile rows only
     if constexpr (TWO) {
-        load_two_lists<Lo>(C, a, tid, lane);
+        load_two_lists<Lo>(C, R2, a, tid, lane);
     } else if (HYB) {
         load_tile_list<Lo>(C, a, lch, tid, lane);
     } else {
@@ -272,13 +273,19 @@ void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
     const int xoff = wm * WTM * 128;
     constexpr int PER_SLICE = XJ + NG * (8 / NW);   // copy instructions per wave per slice
     if (HYB)                                         // bring the block of list entry k0 / SPT first
-        for (int b = 0; b < k0 / (64 * SPT); ++b) C.shift_list();
+        for (int b = 0; b < k0 / (64 * SPT); ++b) {
+            C.shift_list();
+            if constexpr (TWO) R2.shift();
+        }
     auto issue = [&](int kn) {   // called for kn = k0, k0 + 1, ... in order
-        if (HYB && kn > k0 && kn % (64 * SPT) == 0) C.shift_list();
+        if (HYB && kn > k0 && kn % (64 * SPT) == 0) {
+            C.shift_list();
+            if constexpr (TWO) R2.shift();
+        }
         const uint32_t stage = (kn % NSTAGE) * Lo::STAGE;
         if constexpr (TWO) {
             C.xso = (uint32_t)(ES * (kn / SPT) * BK + 128 * (kn % SPT));   // tile column in K order
-            issue_slice_two(C, kn, stage);
+            issue_slice_two(C, R2, kn, stage);
             return;
         }
         set_x(kn);

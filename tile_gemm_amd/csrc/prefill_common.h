@@ -113,9 +113,6 @@ struct Ctx {
     // and after each block of 64 entries the registers move down by one (shift_list), so entry p
     // is always lane p % 64 of the first register: one lane read, no register select.
     uint32_t lv[4], lm[4], lc[4];
-    // blocks of two 64-row tile rows (64-row tiles): lv / lm hold the first row's records in K order,
-    // lv2 / lm2 the second's, and lc the two rows' types (bit 0: first row 2:4, bit 1: second)
-    uint32_t lv2[4], lm2[4];
     int Tk;
     rsrc_t xr;                          // X rows m0 .. M-1
     rsrc_t wr;                          // values of the tile row from its first tile (or W rows n0 ..)
@@ -135,10 +132,23 @@ struct Ctx {
             lv[w] = lv[w + 1];
             lm[w] = lm[w + 1];
             lc[w] = lc[w + 1];
-            lv2[w] = lv2[w + 1];
-            lm2[w] = lm2[w + 1];
         }
-        lv[3] = lm[3] = lc[3] = lv2[3] = lm2[3] = 0u;
+        lv[3] = lm[3] = lc[3] = 0u;
+    }
+};
+
+// Blocks of two 64-row tile rows (64-row tiles): Ctx's lv / lm then hold the first row's records in
+// K order and lc both rows' types (bit 0: first row 2:4, bit 1: second); the second row's records
+// are kept here, one tile column per lane, and move along with Ctx's (shift with shift_list).
+struct SecondRow {
+    uint32_t lv[4], lm[4];
+    __device__ __forceinline__ void shift() {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            lv[w] = lv[w + 1];
+            lm[w] = lm[w + 1];
+        }
+        lv[3] = lm[3] = 0u;
     }
 };
 
@@ -162,8 +172,10 @@ __device__ __forceinline__ void issue_x(const Ctx<BK, HYB, BN, BM, NW>& C, uint3
     for (int v = 0; v < BM / (8 * NW); ++v) buf16(C.xr, stage + 1024 * (C.wave + NW * v), C.xvo[v], C.xso);
 }
 
-// Group gi of a slice from a packed tile: rows r .. r+63 of the tile whose values start at element
-// voff and whose codes start at word moff; s = slice of the tile.
+// Pieces of issue_slice (below) for blocks of two tile rows: the X copies of a slice, and group gi
+// of a slice from a packed tile -- rows r .. r+63 of the tile whose values start at element voff
+// and whose codes start at word moff; s = slice of the tile.  (issue_slice keeps its own copy of
+// this code: written inline there, the single-tile-row kernels compile as before.)
 template <int BK, bool HYB, int BN, int BM, int NSTAGE, bool DENSE, int NW, int ES>
 __device__ __forceinline__ void issue_packed_group(const Ctx<BK, HYB, BN, BM, NW>& C, int gi, uint32_t r,
                                                    uint32_t voff, uint32_t moff, int s, uint32_t stage) {
@@ -203,19 +215,35 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
         voff = list_entry(C.lv, p);
         moff = list_entry(C.lm, p);
     }
-    issue_x(C, stage);
+#pragma unroll
+    for (int v = 0; v < BM / (8 * NW); ++v) buf16(C.xr, stage + 1024 * (C.wave + NW * v), C.xvo[v], C.xso);
 #pragma unroll
     for (int gi = 0; gi < Lo::NG; ++gi) {
+        const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
         if (!HYB) {                             // rows past N read zeros (bound of the resource)
-            const uint32_t ws = stage + Lo::WOFF + gi * kGroupBytes;
 #pragma unroll
             for (int v = 0; v < JPG; ++v)
                 buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v],
                       (uint32_t)(ES * 64 * gi * C.ldw + 128 * (int64_t)ks));
             continue;
         }
-        // a block is one tile row: groups at rows 0, 64 of the tile
-        issue_packed_group<BK, HYB, BN, BM, NSTAGE, DENSE, NW, ES>(C, gi, 64 * gi, voff, moff, s, stage);
+        const uint32_t r = 64 * gi;             // a block is one tile row: groups at rows 0, 64
+        if (DENSE) {
+            // packed tile: slice s is chunk columns 8s .. 8s+7 of every row, 2048 bytes per 8 columns
+            const uint32_t so = ES * (voff - C.vbase + r * BK) + 2048 * s;
+#pragma unroll
+            for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
+        } else {
+            // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
+            // codes, then the same two again into the sink, or nothing with two stages).  With 4
+            // waves wave w does jobs w and 4 + w, with 8 waves job w.
+            if (NW == 4 || C.wave < 4)
+                buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
+            if ((NW == 4 || C.wave >= 4) && (NSTAGE > 2 || !C.meta_to_sink))
+                buf4(C.mr,
+                     C.meta_to_sink ? (uint32_t)Lo::SINK : ws + Lo::MHALF + 256 * C.mjob,
+                     C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
+        }
     }
 }
 
@@ -223,14 +251,15 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
 // tile column is the same in both rows, each row's tile has its own type and offsets, and a
 // second row past N is not copied.
 template <int BK, bool HYB, int BN, int BM, int NW>
-__device__ __forceinline__ void issue_slice_two(const Ctx<BK, HYB, BN, BM, NW>& C, int ks, uint32_t stage) {
+__device__ __forceinline__ void issue_slice_two(const Ctx<BK, HYB, BN, BM, NW>& C, const SecondRow& R2, int ks,
+                                                uint32_t stage) {
     static_assert(BN == 128, "two 64-row groups");
     constexpr int SPT = BK / 64;
     const int p = ks / SPT, s = ks % SPT;
     // every list read before the first copy
     const uint32_t ty = list_entry(C.lc, p);
     const uint32_t v0 = list_entry(C.lv, p), m0 = list_entry(C.lm, p);
-    const uint32_t v1 = list_entry(C.lv2, p), m1 = list_entry(C.lm2, p);
+    const uint32_t v1 = list_entry(R2.lv, p), m1 = list_entry(R2.lm, p);
     issue_x(C, stage);
     if (ty & 1u) issue_packed_group<BK, HYB, BN, BM, 2, false, NW, 2>(C, 0, 0u, v0, m0, s, stage);
     else issue_packed_group<BK, HYB, BN, BM, 2, true, NW, 2>(C, 0, 0u, v0, m0, s, stage);
@@ -293,11 +322,12 @@ __device__ __forceinline__ void load_tile_list(Ctx<BK, HYB, BN, BM, NW>& C, cons
 }
 
 // Reads the index records of the block's two 64-row tile rows (one tile column per thread) and
-// leaves them in C's registers in K order: lv / lm the first row's {val_off, meta_off}, lv2 / lm2
-// the second's (zeros when that row is past N), lc the two types.  Uses stage 0's memory and ends
+// leaves them in registers in K order: C.lv / C.lm the first row's {val_off, meta_off}, R2 the
+// second's (zeros when that row is past N), C.lc the two types.  Uses stage 0's memory and ends
 // with a barrier, as load_tile_list.
 template <typename Lo, int BK, bool HYB, int BN, int BM, int NW>
-__device__ __forceinline__ void load_two_lists(Ctx<BK, HYB, BN, BM, NW>& C, const GemmArgs& a, int tid, int lane) {
+__device__ __forceinline__ void load_two_lists(Ctx<BK, HYB, BN, BM, NW>& C, SecondRow& R2, const GemmArgs& a, int tid,
+                                               int lane) {
     uint2* l0 = reinterpret_cast<uint2*>(smem + Lo::LIST);
     uint2* l1 = reinterpret_cast<uint2*>(smem + Lo::LIST + kMaxTileCols * 8);
     uint8_t* ty = reinterpret_cast<uint8_t*>(smem + Lo::LIST + 2 * kMaxTileCols * 8);
@@ -320,8 +350,8 @@ __device__ __forceinline__ void load_two_lists(Ctx<BK, HYB, BN, BM, NW>& C, cons
         const bool in = q < C.Tk;
         C.lv[w] = in ? l0[q].x : 0u;
         C.lm[w] = in ? l0[q].y : 0u;
-        C.lv2[w] = in ? l1[q].x : 0u;
-        C.lm2[w] = in ? l1[q].y : 0u;
+        R2.lv[w] = in ? l1[q].x : 0u;
+        R2.lm[w] = in ? l1[q].y : 0u;
         C.lc[w] = in ? (uint32_t)ty[q] : 0u;
     }
     __syncthreads();   // stage 0: every wave has read the lists before the first copy

@@ -46,7 +46,7 @@ def _got(Y, out):
 CASES = [(1, "bf16", 128, 128, "bf16"), (16, "bf16", 128, 128, "bf16"), (24, "f16", 128, 128, "f16"),
          (100, "bf16", 128, 128, "bf16"), (300, "bf16", 128, 128, "f32"), (40, "f16", 64, 64, "f16"),
          (8, "bf16", 32, 32, "bf16"), (40, "bf16", 32, 32, "bf16"), (1, "fp8", 128, 128, "bf16"),
-         (300, "fp8", 128, 128, "f32")]
+         (300, "fp8", 128, 128, "f32"), (300, "bf16", 64, 64, "f32"), (130, "f16", 64, 128, "f16")]
 
 
 @pytest.mark.parametrize("M,dtype,bn,bk,out", CASES, ids=lambda v: str(v))

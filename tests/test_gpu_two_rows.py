@@ -131,3 +131,38 @@ def test_two_rows_and_one_row_forms(two, monkeypatch):
     for M in (100, 700):
         say(f"[two-rows-form] two={two} M={M}")
         _run_all(Xt, pw, M, Y_ref, "bf16", f"two={two}")
+
+
+@pytest.mark.parametrize("bk,dtype", [(64, "bf16"), (128, "f16")])
+def test_two_rows_at_the_column_limit(bk, dtype):
+    # 256 tile columns, the most a tile row of the tiled kernel holds: both rows' list registers
+    # shift through all four 64-entry blocks; three tile rows, so the second block has one
+    N, K, Mmax = 3 * 64, bk * 256, 300
+    W, X, m = _layer(dtype, 64, bk, N, K, "random", 6900 + bk, Mmax)
+    Y_ref = oracle.hybrid_ref(X, W, dtype, m, 64, bk)
+    pw = hts.pack(hts.tensor_from_bits(W, dtype, DEV), m, 64, bk)
+    Xt = hts.tensor_from_bits(X, dtype, DEV)
+    for M in (48, Mmax):
+        say(f"[two-rows-limit] Tk=256 bk={bk} {dtype} M={M}")
+        _run_all(Xt, pw, M, Y_ref, dtype, f"Tk=256 bk={bk}")
+
+
+@pytest.mark.parametrize("M", [64, 300])
+def test_two_rows_gated_unsplit_and_split(M):
+    # the gated output stage: applied in the kernel's epilogue (no workspace: unsplit) and in the
+    # sum of the parts (workspace given: split when it pays)
+    N, K = 5 * 64, 1024
+    W, X, m = _layer("bf16", 64, 64, N, K, "random", 7300 + M, M)
+    g = np.random.default_rng(7400 + M)
+    G_bits = wl.gaussian_bits((M, N), 2.0, "bf16", g)
+    ref = oracle.gated_ref(G_bits, oracle.hybrid_ref(X, W, "bf16", m, 64, 64), "bf16")
+    pw = hts.pack(hts.tensor_from_bits(W, "bf16", DEV), m, 64, 64)
+    Xt = hts.tensor_from_bits(X, "bf16", DEV)
+    G = hts.tensor_from_bits(G_bits, "bf16", DEV)
+    say(f"[two-rows-gated] M={M}")
+    Ys = hts.gemm_silu_mul(Xt, pw, G)                                # workspace allocated: split
+    Yu = torch.empty_like(G)
+    hts.hts_gemm_silu_mul(pw.desc, pw.index, pw.values, pw.meta, Xt, G, Yu)   # unsplit
+    torch.cuda.synchronize()
+    for what, Y in (("split", Ys), ("unsplit", Yu)):
+        _check(oracle.widen_f64(hts.bits_from_tensor(Y), "bf16"), ref, f"gated {what} M={M}")

@@ -439,8 +439,8 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 template <typename T, int BK, bool HYB, int SP>
 hipError_t launch4(const GemmArgs& a, hipStream_t s) {
-    // one tile row x 128 (or 64 or 192, prefill_block_m) X rows per workgroup, 4 waves, 2 stages
-    // (two workgroups per CU)
+    // 128 weight rows (one tile row, or two of 64-row tiles) x 128 (or 64 or 192, prefill_block_m)
+    // X rows per workgroup, 4 waves, 2 stages (two workgroups per CU)
     if constexpr (Elem<T>::bytes == 1) {
         if (prefill_block_m(a.M, a.N, a.dtype, 128) == 192) return launch_tile<T, BK, HYB, SP, 128, 192, 2>(a, s);
         return launch_tile<T, BK, HYB, SP, 128, 128, 2>(a, s);

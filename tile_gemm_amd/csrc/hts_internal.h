@@ -81,8 +81,9 @@ hipError_t launch_index_check(const hts_desc& d, const hts_tile* index, IndexChe
 // ksplit: waves per workgroup (4, 8 or 16); nt: 128-wide tile columns per batch of loads (2 or 4);
 // pp: 16-row panels per workgroup (1 or 2; 2 requires N % 32 == 0)
 hipError_t launch_gemm_decode(const GemmArgs& a, int ksplit, int nt, int pp, int sparse_path, hipStream_t s);
-// Tiled kernel (one tile row x 128 X rows per workgroup); with a.nsplit > 1 it also launches the
-// fixed-order sum of the partial products into Y.
+// Tiled kernel (128 weight rows -- one 128-row tile row or two 64-row ones -- x 64, 128 or 192 X
+// rows per workgroup); with a.nsplit > 1 it also launches the fixed-order sum of the partial
+// products into Y.
 hipError_t launch_gemm_prefill(const GemmArgs& a, int sparse_path, hipStream_t s);
 // X rows per block of the tiled kernel (64, 128 or 192) for M rows of X, N weight rows in blocks
 // of block_rows (128 or 64); the split planner counts blocks with it.
@@ -90,7 +91,7 @@ int prefill_block_m(int64_t M, int64_t N, int32_t dtype, int block_rows);
 // Weight rows per block of the tiled kernel on a packed weight with bn-row tiles (16-bit data).
 int prefill_weight_rows(int bn);
 // With a packed weight and M above the streaming range, K / bk must not exceed this: the
-// tiled kernel holds the index records of one tile row in LDS.
+// tiled kernel holds the index records of a block's tile rows in LDS.
 constexpr int kMaxTileColsPerRow = 256;
 hipError_t launch_silu_mul(int32_t dtype, int64_t M, int64_t N, const uint16_t* G, int64_t ldg, const uint16_t* U,
                            int64_t ldu, uint16_t* H, int64_t ldh, hipStream_t s);

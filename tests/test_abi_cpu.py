@@ -252,6 +252,13 @@ def test_split_product_workspace_sizes(monkeypatch):
     assert hts.hts_gemm_workspace(hts.make_desc(N, K, 128, 128, "fp8"), 17) == 0     # streams at M <= 32
     assert hts.hts_gemm_workspace(hts.make_desc(N, K, 128, 128, "fp8"), 33) == _r256(5 * 33 * N * 4)
     assert hts.hts_gemm_workspace(hts.make_desc(4096, 4096, 64, 64, "bf16"), 17) == _r256(8 * 17 * 4096 * 4)
+    # 64-row tiles go two tile rows to a 128-row block: at M = 200, 32 x 2 = 64 blocks -> 8 parts; with
+    # one tile row per block (HTS_PREFILL_TWO_ROWS=0) 64 x 2 = 128 blocks -> 4 parts
+    d64 = hts.make_desc(4096, 4096, 64, 64, "bf16")
+    assert hts.hts_gemm_workspace(d64, 200) == _r256(8 * 200 * 4096 * 4)
+    monkeypatch.setenv("HTS_PREFILL_TWO_ROWS", "0")
+    assert hts.hts_gemm_workspace(d64, 200) == _r256(4 * 200 * 4096 * 4)
+    monkeypatch.delenv("HTS_PREFILL_TWO_ROWS")
     # few slices: K = 256 has 4 (bf16), too few to split
     assert hts.hts_gemm_workspace(hts.make_desc(1024, 256, 128, 128, "bf16"), 64) == 0
     # 32-wide tiles: the unpacked weight, then the parts of the dense product

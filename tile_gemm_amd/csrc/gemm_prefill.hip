@@ -100,9 +100,13 @@ __device__ __forceinline__ void compute_dense(f32x4 (&acc)[NBI][NBJ], const uint
     }
 }
 
-template <typename T, int SP, int NBI, int NBJ>
+// ms: the group's codes, code row by code row (BK/32 words per row: every slice of the tile); s:
+// the slice of the tile.
+template <typename T, int BK, int SP, int NBI, int NBJ>
 __device__ __forceinline__ void compute_sparse(f32x4 (&acc)[NBI][NBJ], const uint8_t* xs, const uint8_t* ws,
-                                               const uint32_t* ms, int lane) {
+                                               const uint32_t* ms, int s, int lane) {
+    constexpr int CPR = BK / 32;            // code words per row in LDS
+    const int cs = (128 / (32 * Elem<T>::bytes)) * s;   // first word of slice s in a row (16-bit: 2 s)
     const int i = lane & 15, g = lane >> 4;
     const int s0 = 16 * (16 * g + i);    // stored order: chunk g of row i of the 16-row block
     u32x8 Bx[NBJ];
@@ -118,8 +122,8 @@ __device__ __forceinline__ void compute_sparse(f32x4 (&acc)[NBI][NBJ], const uin
             for (int b = 0; b < 4; ++b) {
                 A[b] = ld16(wg + b * 1024 + s0);
                 // 16-bit: a 16-bit half of the row's word g/2; 8-bit: the row's whole word g
-                idx[b] = Elem<T>::bytes == 1 ? mg[4 * (16 * b + i) + g]
-                                             : mg[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1));
+                idx[b] = Elem<T>::bytes == 1 ? mg[CPR * (16 * b + i) + cs + g]
+                                             : mg[CPR * (16 * b + i) + cs + (g >> 1)] >> (16 * (g & 1));
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b)
@@ -135,7 +139,7 @@ __device__ __forceinline__ void compute_sparse(f32x4 (&acc)[NBI][NBJ], const uin
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const uint2 v = *reinterpret_cast<const uint2*>(wg + b * 1024 + s0 + 8 * u);
-                    const uint32_t code = (mg[2 * (16 * b + i) + (g >> 1)] >> (16 * (g & 1) + 8 * u)) & 0xFFu;
+                    const uint32_t code = (mg[CPR * (16 * b + i) + cs + (g >> 1)] >> (16 * (g & 1) + 8 * u)) & 0xFFu;
                     A[b] = expand_two_groups(v, code);
                 }
 #pragma unroll
@@ -221,14 +225,8 @@ void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
     {
         // stored rows of BK/2 values: a slice of a 16-row panel is one contiguous kilobyte (job = panel)
         C.svo = (uint32_t)((wave & 3) * 16 * (BK / 2) * ES + 16 * lane);
-        // codes jobs of 256 bytes: 64 rows x (KSL / 32) words per slice; job j covers words
-        // 64 j .. 64 j + 63 of that row-major block
-        constexpr int WPR = KSL / 32, NCJ = MGB / 256;
-        const int cj = ((NW == 4) ? wave : wave - 4) & 3;  // this wave's codes job 0..3
-        C.mjob = cj % NCJ;
-        const int wi = 64 * C.mjob + lane;
-        C.mvo = (uint32_t)(4 * ((wi / WPR) * (BK / 32) + (wi % WPR)));
-        C.meta_to_sink = cj >= NCJ;
+        // a group's codes: one job, lane L the 16 bytes of code row L (issue_codes)
+        C.mvo = (uint32_t)(16 * lane);
     }
     // ordered tile list of the tile row, tile columns kept for the X copies
     SecondRow R2;                  // blocks of two tile rows only
@@ -319,7 +317,8 @@ void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
             if (!wvalid) continue;
             const uint8_t* ws = st + Lo::WOFF + wn * kGroupBytes;
             if (sparse)
-                compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, ws, reinterpret_cast<const uint32_t*>(ws + Lo::MHALF), lane);
+                compute_sparse<T, BK, SP, 4, NBJ>(acc, st + xoff, ws, reinterpret_cast<const uint32_t*>(ws + Lo::MHALF),
+                                                  ks % SPT, lane);
             else
                 compute_dense<T, SP, 4, NBJ, true>(acc, st + xoff, ws, lane);
         }
@@ -337,9 +336,9 @@ void gemm_prefill_kernel(const GemmArgs a, int NB, int MB, int ord, int lch) {
             for (; ks < ce; ++ks) {
                 const uint8_t* st = step(ks);
                 if (wvalid)
-                    compute_sparse<T, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
-                                               reinterpret_cast<const uint32_t*>(st + Lo::WOFF + wn * kGroupBytes + Lo::MHALF),
-                                               lane);
+                    compute_sparse<T, BK, SP, 4, NBJ>(acc, st + xoff, st + Lo::WOFF + wn * kGroupBytes,
+                                                      reinterpret_cast<const uint32_t*>(st + Lo::WOFF + wn * kGroupBytes + Lo::MHALF),
+                                                      ks % SPT, lane);
             }
         }
     }

@@ -50,8 +50,8 @@ __device__ __forceinline__ void block_of(int L, int NB, int MB, int ord, int& nb
 }
 
 // LDS image of one stage: X slice (BM rows x 128 B), then BN/64 weight-group slots of 8 KiB.  A
-// dense group fills its slot; a 2:4 group's stored values fill the lower half and its codes (MGB
-// bytes) sit in the upper half, so the codes need no space of their own.  The ordered tile list
+// dense group fills its slot; a 2:4 group's stored values fill the lower half and its codes (one
+// 1 KiB job: 64 code rows) sit in the upper half, so the codes need no space of their own.  The ordered tile list
 // is built once, before the first copy, in stage 0's memory.  With two stages nothing else is
 // needed: a 128 x 192 block then takes 80 KiB, and two such workgroups fit in a CU's 160 KiB.
 template <int BN, int BM, int NSTAGE, int MGB = kMetaGroupBytes>
@@ -65,7 +65,7 @@ struct Layout {
     static constexpr int LIST = 0;                           // ordered tile list: {val_off, meta_off}
     static constexpr int LCOL = LIST + kMaxTileCols * 8;     // ... and the tile column of each entry
     static constexpr int WCNT = LCOL + kMaxTileCols * 2;     // dense tiles of each chunk (bytes)
-    static_assert(MGB <= MHALF, "codes of a slice fit the upper half of a 2:4 group's slot");
+    static_assert(MGB <= 1024 && 1024 <= MHALF, "a group's codes job fits the upper half of a 2:4 group's slot");
     static_assert(WCNT + 64 <= STAGE, "the list fits in stage 0");
 };
 
@@ -123,8 +123,6 @@ struct Ctx {
     uint32_t dvo[JPG];                  // dense group jobs (row * BK + chunk, or row * ldw + chunk)
     uint32_t svo;                       // 2:4 values job
     uint32_t mvo;                       // 2:4 codes job
-    bool meta_to_sink;                  // a codes job past the codes of a slice repeats one into the sink
-    int mjob;                           // this wave's codes job (256 bytes each)
     __device__ __forceinline__ bool gvalid(int gi) const { return n0 + 64 * gi < N; }
     __device__ __forceinline__ void shift_list() {
 #pragma unroll
@@ -158,14 +156,31 @@ __device__ __forceinline__ uint32_t list_entry(const uint32_t (&r)[4], int p) {
     return (uint32_t)__builtin_amdgcn_readlane((int)r[0], p & 63);
 }
 
-// Copies of one slice into an LDS stage.  Per 64-row weight group there are 8 copy jobs:
-// dense = 8 x 1 KiB; 2:4 = 4 x 1 KiB of stored values and 2 x 256 B of codes (16-bit elements;
-// 4 x 256 B for 8-bit).  With three or more stages the two missing 16-bit jobs are padding
-// copies of the codes into a sink: each of the NW waves then issues BM/(8 NW) X copies and 8/NW
-// copies per group for every slice, whatever the tile types, so the wait for one slice is a
-// fixed count of outstanding copies.  Two stages wait for every copy in flight, so they skip
-// the padding (measured: all-2:4 4096^2 layer 62.0 -> 61.0 us, 13B 5120^2 at M = 4096 192.3 ->
-// 190.6 us).  KIND (dense / 2:4) is known at compile time: no branch per copy.
+// Copies of one slice into an LDS stage.  Per 64-row weight group: dense = 8 jobs of 1 KiB; 2:4 =
+// 4 x 1 KiB of stored values and one 1 KiB job of codes.  With three or more stages the waves
+// that copy no codes pad with a copy into a sink: each of the NW waves then issues BM/(8 NW) X
+// copies and 8/NW copies per group for every slice, whatever the tile types, so the wait for one
+// slice is a fixed count of outstanding copies.  Two stages wait for every copy in flight, so
+// they skip the padding.  KIND (dense / 2:4) is known at compile time: no branch per copy.
+// The codes of 2:4 group gi (rows r .. r+63 of the tile whose codes start at word moff) into the
+// upper half of its LDS slot ws.  One job of 16 bytes per lane: lane L copies code row L of the
+// group, all BK/32 words of it (the codes of every slice of the tile: a slice reads its own words
+// of each row; with 2 words per row the job's second half holds the next rows, unused).  One
+// wave per group issues it; with three or more stages the others pad with a copy into the sink,
+// so every wave issues the same number of copies per slice.  Against copying only the slice's
+// words in 4-byte-per-lane jobs (two per slice for 16-bit data, four for 8-bit), bit-identical
+// results and 1.00-1.02x the speed (most on layers with many 2:4 tiles).
+template <int BK, bool HYB, int BN, int BM, int NSTAGE, int NW, int ES>
+__device__ __forceinline__ void issue_codes(const Ctx<BK, HYB, BN, BM, NW>& C, int gi, uint32_t r, uint32_t moff,
+                                            int s, uint32_t ws) {
+    using Lo = Layout<BN, BM, NSTAGE, meta_group_bytes<ES>()>;
+    (void)s;
+    if (C.wave == NW - Lo::NG + gi)
+        buf16(C.mr, ws + Lo::MHALF, C.mvo, 4 * (moff - C.mbase + r * (BK / 32)));
+    else if (NSTAGE > 2 && (NW == 4 || C.wave >= 4))
+        buf4(C.mr, (uint32_t)Lo::SINK, 0u, 4 * (moff - C.mbase));
+}
+
 template <int BK, bool HYB, int BN, int BM, int NW>
 __device__ __forceinline__ void issue_x(const Ctx<BK, HYB, BN, BM, NW>& C, uint32_t stage) {
 #pragma unroll
@@ -189,15 +204,11 @@ __device__ __forceinline__ void issue_packed_group(const Ctx<BK, HYB, BN, BM, NW
 #pragma unroll
         for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
     } else {
-        // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
-        // codes, then the same two again into the sink, or nothing with two stages).  With 4
-        // waves wave w does jobs w and 4 + w, with 8 waves job w.
+        // jobs 0-3: stored values (wave w's, or waves 0-3's with 8 waves); then the group's codes,
+        // one job from one wave (issue_codes)
         if (NW == 4 || C.wave < 4)
             buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
-        if ((NW == 4 || C.wave >= 4) && (NSTAGE > 2 || !C.meta_to_sink))
-            buf4(C.mr,
-                 C.meta_to_sink ? (uint32_t)Lo::SINK : ws + Lo::MHALF + 256 * C.mjob,
-                 C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
+        issue_codes<BK, HYB, BN, BM, NSTAGE, NW, ES>(C, gi, r, moff, s, ws);
     }
 }
 
@@ -234,15 +245,11 @@ __device__ __forceinline__ void issue_slice(const Ctx<BK, HYB, BN, BM, NW>& C, i
 #pragma unroll
             for (int v = 0; v < JPG; ++v) buf16(C.wr, ws + 1024 * (C.wave + NW * v), C.dvo[v], so);
         } else {
-            // jobs 0-3: stored values; 4-7: codes, 256 bytes each (16-bit elements: two jobs of
-            // codes, then the same two again into the sink, or nothing with two stages).  With 4
-            // waves wave w does jobs w and 4 + w, with 8 waves job w.
+            // jobs 0-3: stored values (wave w's, or waves 0-3's with 8 waves); then the group's
+            // codes, one job from one wave (issue_codes)
             if (NW == 4 || C.wave < 4)
                 buf16(C.wr, ws + 1024 * (C.wave & 3), C.svo, ES * (voff - C.vbase + r * (BK / 2)) + 1024 * s);
-            if ((NW == 4 || C.wave >= 4) && (NSTAGE > 2 || !C.meta_to_sink))
-                buf4(C.mr,
-                     C.meta_to_sink ? (uint32_t)Lo::SINK : ws + Lo::MHALF + 256 * C.mjob,
-                     C.mvo, 4 * (moff - C.mbase + r * (BK / 32) + (KSL / 32) * s));
+            issue_codes<BK, HYB, BN, BM, NSTAGE, NW, ES>(C, gi, r, moff, s, ws);
         }
     }
 }
